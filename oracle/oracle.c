@@ -1,0 +1,333 @@
+/*
+ * CPU oracle for sliding-window / global causal attention with a per-head
+ * attention sink.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and
+ * the benchmark's CPU-baseline leg call it; the GPU library never does.  It
+ * shares no code, header, table or helper with the GPU path.
+ *
+ * Plain C99 + OpenMP.  Inputs arrive as fp32 (the exact upcast of bf16 or
+ * fp32 data); every step is computed in fp64 with libm's exp/log, two-pass
+ * (all scores, then their maximum, then the normaliser, then the output).
+ *
+ * What is computed (the plain definition the GPU kernels must reproduce):
+ *   For request b, query head h and a query at absolute position i:
+ *     g     = h / (Hq / Hkv)                    contiguous GQA groups
+ *     J(i)  = { j : max(0, i - W + 1) <= j <= i }   W keys including self;
+ *             { j : 0 <= j <= i } when W <= 0 (global attention)
+ *     s_j   = sm_scale * sum_d q[d] * K[j, g, d]
+ *     m     = max(sink_h, max_{j in J} s_j)
+ *     Z     = exp(sink_h - m) + sum_{j in J} exp(s_j - m)
+ *     O[d]  = sum_{j in J} exp(s_j - m) / Z * V[j, g, d]
+ *   The sink adds exp(sink_h) to the softmax denominator and carries no
+ *   value; no sink (NULL) removes that term.
+ *
+ * Sources (the web pages on MiMo-V2-Flash):
+ *   - sliding window of W = 128 tokens interleaved with global attention
+ *     5:1: MiMo-V2-Flash technical-report digest (fanfer.top), section
+ *     "MiMo-V2-Flash Model Architecture"; release blog (aihot.news), section
+ *     on pushing efficiency to the limit.
+ *   - learnable attention-sink bias in the gpt-oss style: technical-report
+ *     digest, paragraph "Hybrid Sliding Window Attention Architecture" (its
+ *     formula image is missing; the reading above is the gpt-oss one).
+ *   - verify of 1 committed + 3 draft tokens in one pass, and the
+ *     accept/accept/reject/discard example: release blog, section
+ *     "Multi-Token Prediction" (verify diagram).
+ *   - fixed-size SWA KV cache: release blog, section on pushing efficiency.
+ * Readings where the pages are silent (window edge, GQA grouping, causal
+ * offsets, cache layout) are listed with the design notes of the repository.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Error codes of the oracle entry points. */
+#define ORC_OK 0
+#define ORC_BAD_ARGS 1
+#define ORC_HISTORY_SHORT 2
+#define ORC_NO_MEMORY 3
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * One query vector against a key set made of up to two segments (segment A,
+ * then segment B), each a run of consecutive rows with a row stride in
+ * floats.  Writes O[D]; optionally the log of the full denominator
+ * (log(exp(sink) + sum exp(s_j))), the sink's probability mass and the
+ * per-key weights (in key order: segment A then segment B).
+ * `sbuf` must hold nA + nB doubles.
+ */
+static void attend(const float *qv, int D, double scale, const double *sink,
+                   const float *kA, const float *vA, long nA, long strideA,
+                   const float *kB, const float *vB, long nB, long strideB,
+                   double *out, double *lse_out, double *psink_out, double *w_out,
+                   double *sbuf)
+{
+    long n = nA + nB;
+    long j;
+    int d;
+
+    /* 1. scores s_j = scale * <q, k_j> */
+    for (j = 0; j < n; ++j) {
+        const float *kr = (j < nA) ? kA + j * strideA : kB + (j - nA) * strideB;
+        double acc = 0.0;
+        for (d = 0; d < D; ++d)
+            acc += (double)qv[d] * (double)kr[d];
+        sbuf[j] = scale * acc;
+    }
+
+    /* 2. maximum over the sink logit and the scores */
+    double m = sink ? *sink : -INFINITY;
+    for (j = 0; j < n; ++j)
+        if (sbuf[j] > m)
+            m = sbuf[j];
+
+    /* 3. normaliser: the sink's exp term plus every key's */
+    double z = sink ? exp(*sink - m) : 0.0;
+    for (j = 0; j < n; ++j)
+        z += exp(sbuf[j] - m);
+
+    /* 4. output: weighted sum of value rows (the sink contributes no value) */
+    for (d = 0; d < D; ++d)
+        out[d] = 0.0;
+    for (j = 0; j < n; ++j) {
+        const float *vr = (j < nA) ? vA + j * strideA : vB + (j - nA) * strideB;
+        double w = exp(sbuf[j] - m) / z;
+        if (w_out)
+            w_out[j] = w;
+        for (d = 0; d < D; ++d)
+            out[d] += w * (double)vr[d];
+    }
+    if (lse_out)
+        *lse_out = m + log(z);
+    if (psink_out)
+        *psink_out = sink ? exp(*sink - m) / z : 0.0;
+}
+
+/* Lowest key position of the window of a query at position i. */
+static long window_lo(long i, int window)
+{
+    if (window <= 0)
+        return 0;
+    long lo = i - (long)window + 1;
+    return lo < 0 ? 0 : lo;
+}
+
+/*
+ * Prefill over whole tensors.
+ *   q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D] (fp32), sinks [Hq] or NULL,
+ *   o [B, Sq, Hq, D] (fp64).  Query row r sits at position q_offset + r.
+ *   lse, psink: optional [B, Sq, Hq].  weights: optional [B, Sq, Hq, Sk],
+ *   zero outside the window.
+ */
+int oracle_prefill(const float *q, const float *k, const float *v, const double *sinks,
+                   double *o, double *lse, double *psink, double *weights,
+                   int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                   int window, int q_offset, double sm_scale)
+{
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 ||
+        q_offset < 0 || (long)q_offset + Sq > Sk)
+        return ORC_BAD_ARGS;
+    const int G = Hq / Hkv;
+    const long total = (long)B * Sq * Hq;
+    int err = ORC_OK;
+
+#pragma omp parallel
+    {
+        double *sbuf = (double *)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        double *wbuf = weights ? (double *)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1)) : NULL;
+        if (!sbuf || (weights && !wbuf)) {
+#pragma omp atomic write
+            err = ORC_NO_MEMORY;
+        } else {
+            long idx;
+#pragma omp for schedule(dynamic, 16)
+            for (idx = 0; idx < total; ++idx) {
+                long b = idx / ((long)Sq * Hq);
+                long r = (idx / Hq) % Sq;
+                int h = (int)(idx % Hq);
+                int g = h / G;
+                long i = (long)q_offset + r;
+                long lo = window_lo(i, window);
+                long n = i - lo + 1;
+                const float *qv = q + ((b * Sq + r) * Hq + h) * (long)D;
+                const float *kb = k + ((b * Sk + lo) * Hkv + g) * (long)D;
+                const float *vb = v + ((b * Sk + lo) * Hkv + g) * (long)D;
+                double *ov = o + ((b * Sq + r) * Hq + h) * (long)D;
+                long row = (b * Sq + r) * Hq + h;
+                attend(qv, D, sm_scale, sinks ? &sinks[h] : NULL,
+                       kb, vb, n, (long)Hkv * D, NULL, NULL, 0, 0,
+                       ov, lse ? &lse[row] : NULL, psink ? &psink[row] : NULL,
+                       wbuf, sbuf);
+                if (weights) {
+                    double *wr = weights + row * (long)Sk;
+                    memset(wr, 0, sizeof(double) * (size_t)Sk);
+                    memcpy(wr + lo, wbuf, sizeof(double) * (size_t)n);
+                }
+            }
+        }
+        free(sbuf);
+        free(wbuf);
+    }
+    return err;
+}
+
+/*
+ * Prefill for selected query rows of one request.
+ *   q_rows [n, Hq, D]: the query vectors of rows rows[0..n-1] (row r sits at
+ *   position q_offset + r).  k/v [nk, Hkv, D] hold key positions
+ *   k_base .. k_base + nk - 1.  o [n, Hq, D] (fp64).
+ * Returns ORC_HISTORY_SHORT if a needed key lies outside the given slice.
+ */
+int oracle_prefill_rows(const float *q_rows, const int64_t *rows, long n,
+                        const float *k, const float *v, long k_base, long nk,
+                        const double *sinks, double *o,
+                        int Hq, int Hkv, int D, int window, long q_offset, double sm_scale)
+{
+    if (n < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || nk < 0 || k_base < 0)
+        return ORC_BAD_ARGS;
+    const int G = Hq / Hkv;
+    long idx;
+    for (idx = 0; idx < n; ++idx) {
+        long i = q_offset + rows[idx];
+        if (window_lo(i, window) < k_base || i >= k_base + nk)
+            return ORC_HISTORY_SHORT;
+    }
+    const long total = n * Hq;
+    int err = ORC_OK;
+#pragma omp parallel
+    {
+        double *sbuf = (double *)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+        if (!sbuf) {
+#pragma omp atomic write
+            err = ORC_NO_MEMORY;
+        } else {
+            long t;
+#pragma omp for schedule(dynamic, 4)
+            for (t = 0; t < total; ++t) {
+                long a = t / Hq;
+                int h = (int)(t % Hq);
+                int g = h / G;
+                long i = q_offset + rows[a];
+                long lo = window_lo(i, window);
+                const float *kb = k + ((lo - k_base) * Hkv + g) * (long)D;
+                const float *vb = v + ((lo - k_base) * Hkv + g) * (long)D;
+                attend(q_rows + (a * Hq + h) * (long)D, D, sm_scale, sinks ? &sinks[h] : NULL,
+                       kb, vb, i - lo + 1, (long)Hkv * D, NULL, NULL, 0, 0,
+                       o + (a * Hq + h) * (long)D, NULL, NULL, NULL, sbuf);
+            }
+        }
+        free(sbuf);
+    }
+    return err;
+}
+
+/*
+ * Verify: q_len = T new tokens per request, scored in one pass.
+ *   Request b has L_b = cache_len[b] committed tokens.  Its logical history
+ *   k_hist/v_hist [B, Hlen, Hkv, D] holds position hist_base[b] + r in row r
+ *   (only rows for positions < L_b are read).  The T tokens under
+ *   verification sit at positions L_b .. L_b + T - 1 with keys/values
+ *   k_new/v_new [B, T, Hkv, D].  Query t (q [B, T, Hq, D]) sees history
+ *   positions and new tokens u <= t inside its window.  o [B, T, Hq, D].
+ * The oracle reads the logical history only, never a ring layout.
+ */
+int oracle_verify(const float *q, const float *k_new, const float *v_new,
+                  const float *k_hist, const float *v_hist, const int64_t *hist_base,
+                  const int64_t *cache_len, const double *sinks, double *o,
+                  int B, int T, int Hq, int Hkv, int D, long Hlen, int window, double sm_scale)
+{
+    if (B < 0 || T <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || Hlen < 0)
+        return ORC_BAD_ARGS;
+    const int G = Hq / Hkv;
+    int b;
+    for (b = 0; b < B; ++b) {
+        long L = cache_len[b];
+        if (L < 0 || hist_base[b] < 0 || hist_base[b] > L)
+            return ORC_BAD_ARGS;
+        /* the lowest window position over the T queries is that of t = 0 */
+        long lo = window_lo(L, window);
+        if (lo < L && (lo < hist_base[b] || L - hist_base[b] > Hlen))
+            return ORC_HISTORY_SHORT;
+    }
+    const long total = (long)B * T * Hq;
+    int err = ORC_OK;
+#pragma omp parallel
+    {
+        double *sbuf = (double *)malloc(sizeof(double) * (size_t)(Hlen + T + 1));
+        if (!sbuf) {
+#pragma omp atomic write
+            err = ORC_NO_MEMORY;
+        } else {
+            long idx;
+#pragma omp for schedule(dynamic, 4)
+            for (idx = 0; idx < total; ++idx) {
+                long bb = idx / ((long)T * Hq);
+                long t = (idx / Hq) % T;
+                int h = (int)(idx % Hq);
+                int g = h / G;
+                long L = cache_len[bb];
+                long i = L + t;
+                long lo = window_lo(i, window);
+                /* segment A: committed positions lo .. L-1 from the history */
+                long nA = lo < L ? L - lo : 0;
+                long rowA = lo - hist_base[bb];
+                const float *kA = k_hist + ((bb * Hlen + (nA ? rowA : 0)) * Hkv + g) * (long)D;
+                const float *vA = v_hist + ((bb * Hlen + (nA ? rowA : 0)) * Hkv + g) * (long)D;
+                /* segment B: new tokens u0 .. t (u0 > 0 only if the window is shorter than t+1) */
+                long u0 = lo > L ? lo - L : 0;
+                long nB = t - u0 + 1;
+                const float *kB = k_new + ((bb * T + u0) * Hkv + g) * (long)D;
+                const float *vB = v_new + ((bb * T + u0) * Hkv + g) * (long)D;
+                attend(q + ((bb * T + t) * Hq + h) * (long)D, D, sm_scale,
+                       sinks ? &sinks[h] : NULL,
+                       kA, vA, nA, (long)Hkv * D, kB, vB, nB, (long)Hkv * D,
+                       o + ((bb * T + t) * Hq + h) * (long)D, NULL, NULL, NULL, sbuf);
+            }
+        }
+        free(sbuf);
+    }
+    return err;
+}
+
+/*
+ * Commit accepted tokens to a KV cache (bytewise copy, any element size).
+ *   caches [B, slots, Hkv, D], new rows [B, T, Hkv, D].  For every request b
+ *   and every t < n_append[b], the row of position p = cache_len[b] + t goes
+ *   to slot p % slots (ring) or slot p (linear); nothing else changes.
+ *   Accepting a prefix of the drafts and discarding the rest follows the
+ *   verify diagram of the release blog, section "Multi-Token Prediction".
+ */
+int oracle_ring_append(unsigned char *k_cache, unsigned char *v_cache,
+                       const unsigned char *k_new, const unsigned char *v_new,
+                       const int64_t *cache_len, const int64_t *n_append,
+                       int B, int T, int Hkv, int D, long slots, int ring, int elem_bytes)
+{
+    if (B < 0 || T < 0 || Hkv <= 0 || D <= 0 || slots <= 0 || elem_bytes <= 0)
+        return ORC_BAD_ARGS;
+    const size_t rowb = (size_t)Hkv * D * elem_bytes;
+    int b;
+    for (b = 0; b < B; ++b) {
+        long t;
+        if (n_append[b] < 0 || n_append[b] > T || cache_len[b] < 0)
+            return ORC_BAD_ARGS;
+        for (t = 0; t < n_append[b]; ++t) {
+            long p = cache_len[b] + t;
+            long slot = ring ? p % slots : p;
+            if (slot >= slots)
+                return ORC_BAD_ARGS;
+            memcpy(k_cache + ((size_t)b * slots + slot) * rowb, k_new + ((size_t)b * T + t) * rowb, rowb);
+            memcpy(v_cache + ((size_t)b * slots + slot) * rowb, v_new + ((size_t)b * T + t) * rowb, rowb);
+        }
+    }
+    return ORC_OK;
+}
