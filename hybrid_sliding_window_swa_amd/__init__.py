@@ -1,0 +1,211 @@
+"""MI355X (gfx950) sliding-window / global attention with per-head sinks.
+
+Thin ctypes binding over ``libswa_attn.so`` (the HIP kernels behind the C ABI
+declared in ``include/swa_attn.h``).  The functions carry the C names:
+
+    swa_attn_prefill(q, k, v, sinks, window, q_offset=0, sm_scale=None, out=None)
+    swa_attn_verify_workspace_bytes(...)
+    swa_attn_verify(q, k_new, v_new, k_cache, v_cache, cache_len, sinks, window, ring, ...)
+    kv_ring_append(k_cache, v_cache, k_new, v_new, cache_len, n_append, ring)
+
+They only check and marshal arguments (device, dtype, contiguity, shapes)
+and pass raw device pointers plus torch's current HIP stream; every step of
+the computation runs in the library's kernels.  There is no fallback: if the
+library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "SwaError", "library_path", "load_library", "swa_attn_prefill",
+    "swa_attn_verify_workspace_bytes", "swa_attn_verify", "kv_ring_append",
+    "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libswa_attn.so"
+_lib = None
+
+SWA_F32, SWA_BF16 = 0, 1
+EXPORTED_SYMBOLS = ("swa_status_string", "swa_attn_prefill", "swa_attn_verify_workspace_bytes",
+                    "swa_attn_verify", "kv_ring_append")
+
+
+class SwaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def load_library():
+    """Load libswa_attn.so from the package directory (raises if absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m hybrid_sliding_window_swa_amd.build`")
+    lib = ctypes.CDLL(path)
+    i, p, f, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    lib.swa_status_string.argtypes = [i]
+    lib.swa_status_string.restype = ctypes.c_char_p
+    lib.swa_attn_prefill.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, p]
+    lib.swa_attn_prefill.restype = i
+    lib.swa_attn_verify_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
+    lib.swa_attn_verify_workspace_bytes.restype = sz
+    lib.swa_attn_verify.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, p, sz, p]
+    lib.swa_attn_verify.restype = i
+    lib.kv_ring_append.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, i, p]
+    lib.kv_ring_append.restype = i
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load_library().swa_status_string(status).decode()
+        raise SwaError(status, f"{what}: {msg}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SWA_BF16
+    if t.dtype == torch.float32:
+        return SWA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, ndim=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def swa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     sinks: Optional[torch.Tensor], window: int, q_offset: int = 0,
+                     sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Causal prefill: q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] (bf16 or fp32), sinks [Hq]
+    fp32 or None; window <= 0 means global.  Returns o [B,Sq,Hq,D]."""
+    lib = load_library()
+    _dev(q, "q", ndim=4)
+    _dev(k, "k", q.dtype, 4)
+    _dev(v, "v", q.dtype, 4)
+    _dev(sinks, "sinks", torch.float32, 1)
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError("k/v shape mismatch")
+    if sinks is not None and sinks.shape[0] != Hq:
+        raise ValueError("sinks must have Hq entries")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", q.dtype, 4)
+        if out.shape != q.shape:
+            raise ValueError("out shape mismatch")
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    st = lib.swa_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out),
+                              B, Sq, Sk, Hq, Hkv, D, int(window), int(q_offset), float(sm_scale),
+                              _dtype_code(q), _stream(stream))
+    _check(st, "swa_attn_prefill")
+    return out
+
+
+def swa_attn_verify_workspace_bytes(B: int, q_len: int, Hq: int, Hkv: int, D: int,
+                                    cache_slots: int, ring: bool, window: int,
+                                    dtype: torch.dtype = torch.bfloat16) -> int:
+    code = SWA_BF16 if dtype == torch.bfloat16 else SWA_F32
+    return int(load_library().swa_attn_verify_workspace_bytes(B, q_len, Hq, Hkv, D, cache_slots,
+                                                              int(bool(ring)), int(window), code))
+
+
+def swa_attn_verify(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    k_cache: torch.Tensor, v_cache: torch.Tensor, cache_len: torch.Tensor,
+                    sinks: Optional[torch.Tensor], window: int, ring: bool,
+                    sm_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Verify q [B,T,Hq,D] (tokens at positions cache_len[b] + t) against the
+    cache [B,slots,Hkv,D] (ring or linear) and the new rows k_new/v_new
+    [B,T,Hkv,D].  cache_len: int32 [B] on the GPU.  Returns o [B,T,Hq,D]."""
+    lib = load_library()
+    _dev(q, "q", ndim=4)
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, name, q.dtype, 4)
+    _dev(cache_len, "cache_len", torch.int32, 1)
+    _dev(sinks, "sinks", torch.float32, 1)
+    B, T, Hq, D = q.shape
+    _, slots, Hkv, _ = k_cache.shape
+    if k_new.shape != (B, T, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, q_len, Hkv, D]")
+    if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shape mismatch")
+    if cache_len.shape[0] != B:
+        raise ValueError("cache_len must have B entries")
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    need = swa_attn_verify_workspace_bytes(B, T, Hq, Hkv, D, slots, ring, window, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", q.dtype, 4)
+    st = lib.swa_attn_verify(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                             _ptr(cache_len), _ptr(sinks), _ptr(out), B, T, Hq, Hkv, D, slots,
+                             int(bool(ring)), int(window), float(sm_scale), _dtype_code(q),
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "swa_attn_verify")
+    return out
+
+
+def kv_ring_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+                   v_new: torch.Tensor, cache_len: torch.Tensor, n_append: torch.Tensor,
+                   ring: bool, stream=None) -> None:
+    """Copy rows t < n_append[b] of k_new/v_new into the cache slots of
+    positions cache_len[b] + t (ring: modulo the slot count).  In place."""
+    lib = load_library()
+    _dev(k_cache, "k_cache", ndim=4)
+    _dev(v_cache, "v_cache", k_cache.dtype, 4)
+    _dev(k_new, "k_new", k_cache.dtype, 4)
+    _dev(v_new, "v_new", k_cache.dtype, 4)
+    _dev(cache_len, "cache_len", torch.int32, 1)
+    _dev(n_append, "n_append", torch.int32, 1)
+    B, slots, Hkv, D = k_cache.shape
+    T = k_new.shape[1]
+    if k_new.shape != (B, T, Hkv, D) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    st = lib.kv_ring_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                            _ptr(cache_len), _ptr(n_append), B, T, Hkv, D, slots,
+                            int(bool(ring)), _dtype_code(k_cache), _stream(stream))
+    _check(st, "kv_ring_append")

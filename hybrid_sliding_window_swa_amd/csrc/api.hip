@@ -1,0 +1,130 @@
+// C-ABI entry points: validate on the host, then enqueue the kernels on the
+// caller's stream.  No allocation, no synchronisation, no state.
+#include <math.h>
+
+#include "launch.hpp"
+#include "swa_attn.h"
+#include "validate.h"
+
+using namespace swa;
+
+namespace {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+swa_status_t from_hip(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* swa_status_string(swa_status_t status) {
+  switch (status) {
+    case SWA_OK: return "ok";
+    case SWA_ERR_NULL: return "a required pointer is NULL";
+    case SWA_ERR_SHAPE: return "sizes violate a shape rule";
+    case SWA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or head grouping";
+    case SWA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SWA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+swa_status_t swa_attn_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                              void* o, int B, int Sq, int Sk, int Hq, int Hkv, int D, int window,
+                              int q_offset, float sm_scale, swa_dtype_t dtype, void* stream) {
+  swa_status_t st = swa_validate_prefill(q, k, v, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset, dtype);
+  if (st != SWA_OK || B == 0 || Sq == 0) return st;
+  PrefillArgs a = {};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.sinks = sinks;
+  a.o = (uint16_t*)o;
+  a.B = B;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.window = window > 0 ? window : 0;
+  a.q_offset = q_offset;
+  a.scale = sm_scale;
+  a.scale_log2 = sm_scale * kLog2eHost;
+  hipStream_t s = (hipStream_t)stream;
+  return from_hip(dtype == SWA_BF16 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s));
+}
+
+size_t swa_attn_verify_workspace_bytes(int B, int q_len, int Hq, int Hkv, int D, int cache_slots,
+                                       int ring, int window, swa_dtype_t dtype) {
+  if (swa_validate_verify_shape(B, q_len, Hq, Hkv, D, cache_slots, ring, window, dtype) != SWA_OK)
+    return 0;
+  if (dtype != SWA_BF16 || B == 0) return 0;
+  return plan_verify_bf16(B, q_len, Hq, Hkv, D, cache_slots, ring, window).ws_bytes;
+}
+
+swa_status_t swa_attn_verify(const void* q, const void* k_new, const void* v_new,
+                             const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                             const float* sinks, void* o, int B, int q_len, int Hq, int Hkv, int D,
+                             int cache_slots, int ring, int window, float sm_scale,
+                             swa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  swa_status_t st =
+      swa_validate_verify_shape(B, q_len, Hq, Hkv, D, cache_slots, ring, window, dtype);
+  if (st != SWA_OK || B == 0) return st;
+  st = swa_validate_verify_ptrs(q, k_new, v_new, k_cache, v_cache, cache_len, o);
+  if (st != SWA_OK) return st;
+  VerifyArgs a = {};
+  a.q = (const uint16_t*)q;
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.k_cache = (const uint16_t*)k_cache;
+  a.v_cache = (const uint16_t*)v_cache;
+  a.cache_len = cache_len;
+  a.sinks = sinks;
+  a.o = (uint16_t*)o;
+  a.B = B;
+  a.T = q_len;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.slots = cache_slots;
+  a.ring = ring;
+  a.window = window > 0 ? window : 0;
+  a.scale = sm_scale;
+  a.scale_log2 = sm_scale * kLog2eHost;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == SWA_F32) return from_hip(launch_verify_f32(a, s));
+  const VerifyPlan plan = plan_verify_bf16(B, q_len, Hq, Hkv, D, cache_slots, ring, window);
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes || ((uintptr_t)workspace & 255u) != 0)
+      return SWA_ERR_WORKSPACE;
+    a.ws_o = (float*)workspace;
+    a.ws_ml = a.ws_o + (size_t)B * Hkv * plan.nsplit * (32 * plan.nb) * D;
+  }
+  return from_hip(launch_verify_bf16(a, plan, s));
+}
+
+swa_status_t kv_ring_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                            const int32_t* cache_len, const int32_t* n_append, int B, int q_len,
+                            int Hkv, int D, int cache_slots, int ring, swa_dtype_t dtype,
+                            void* stream) {
+  swa_status_t st = swa_validate_append(k_cache, v_cache, k_new, v_new, cache_len, n_append, B,
+                                        q_len, Hkv, D, cache_slots, ring, dtype);
+  if (st != SWA_OK || B == 0) return st;
+  AppendArgs a = {};
+  a.k_cache = (uint8_t*)k_cache;
+  a.v_cache = (uint8_t*)v_cache;
+  a.k_new = (const uint8_t*)k_new;
+  a.v_new = (const uint8_t*)v_new;
+  a.cache_len = cache_len;
+  a.n_append = n_append;
+  a.B = B;
+  a.T = q_len;
+  a.row_bytes = Hkv * D * (dtype == SWA_BF16 ? 2 : 4);
+  a.slots = cache_slots;
+  a.ring = ring;
+  return from_hip(launch_append(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal kernel-launch interface between the C-ABI entry points and the
+// kernels.  All pointers are device pointers; arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swa {
+
+struct PrefillArgs {
+  const uint16_t* q;  // bf16 bits, or fp32 reinterpreted by the fp32 kernel
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* sinks;
+  uint16_t* o;
+  int B, Sq, Sk, Hq, Hkv, D;
+  int window, q_offset;
+  float scale;        // sm_scale
+  float scale_log2;   // sm_scale * log2(e)
+  // filled by the launcher
+  int n_tb, total, per_xcd;
+};
+
+struct VerifyArgs {
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* cache_len;
+  const float* sinks;
+  uint16_t* o;
+  float* ws_o;   // [B][Hkv][nsplit][R_pad][D] split partial outputs
+  float* ws_ml;  // [B][Hkv][nsplit][R_pad][2] split running max (log2) and sum
+  int B, T, Hq, Hkv, D;
+  int slots, ring, window;
+  float scale;
+  float scale_log2;
+  int split_len;   // cache rows per split (multiple of 32 * waves)
+  int nsplit;      // splits per (request, KV head) the workspace holds
+  int r_pad;       // query rows per (request, KV head), padded to 32 * NB
+};
+
+struct AppendArgs {
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  const int32_t* cache_len;
+  const int32_t* n_append;
+  int B, T, row_bytes, slots, ring;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+
+// Verify plan shared by the workspace query and the launch.
+struct VerifyPlan {
+  int nb;         // 32-row query blocks per (request, KV head)
+  int waves;      // waves per workgroup
+  int split_len;  // cache rows per split
+  int nsplit;     // splits per (request, KV head)
+  size_t ws_bytes;
+};
+VerifyPlan plan_verify_bf16(int B, int T, int Hq, int Hkv, int D, int slots, int ring, int window);
+hipError_t launch_verify_bf16(const VerifyArgs& a, const VerifyPlan& plan, hipStream_t s);
+hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s);
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
+}  // namespace swa

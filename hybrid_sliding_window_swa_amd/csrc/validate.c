@@ -1,0 +1,90 @@
+/* Host-side argument validation of the C ABI (no HIP dependency). */
+#include "validate.h"
+
+static int dtype_ok(swa_dtype_t dt) { return dt == SWA_F32 || dt == SWA_BF16; }
+static int head_dim_ok(int D) { return D == 64 || D == 128; }
+
+swa_status_t swa_validate_prefill(const void *q, const void *k, const void *v, const void *o,
+                                  int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                                  int window, int q_offset, swa_dtype_t dtype)
+{
+    (void)window;
+    if (!dtype_ok(dtype))
+        return SWA_ERR_UNSUPPORTED;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+        return SWA_ERR_SHAPE;
+    if (q_offset < 0 || (long long)q_offset + Sq > Sk)
+        return SWA_ERR_SHAPE;
+    if (!head_dim_ok(D))
+        return SWA_ERR_UNSUPPORTED;
+    {
+        const int G = Hq / Hkv;
+        if (dtype == SWA_BF16 && (G > 32 || 32 % G != 0))
+            return SWA_ERR_UNSUPPORTED;
+        if (dtype == SWA_F32 && G > 128)
+            return SWA_ERR_UNSUPPORTED;
+    }
+    /* element offsets must fit in 64-bit and per-tensor token counts in int */
+    if ((long long)B * Sq * Hq * D > (1LL << 46) || (long long)B * Sk * Hkv * D > (1LL << 46))
+        return SWA_ERR_SHAPE;
+    if (B == 0 || Sq == 0)
+        return SWA_OK;
+    if (!q || !k || !v || !o)
+        return SWA_ERR_NULL;
+    return SWA_OK;
+}
+
+swa_status_t swa_validate_verify_shape(int B, int q_len, int Hq, int Hkv, int D,
+                                       int cache_slots, int ring, int window, swa_dtype_t dtype)
+{
+    if (!dtype_ok(dtype))
+        return SWA_ERR_UNSUPPORTED;
+    if (B < 0 || q_len < 1 || q_len > 16 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+        cache_slots < 1 || (ring != 0 && ring != 1))
+        return SWA_ERR_SHAPE;
+    if (ring && (window < 1 || cache_slots < window))
+        return SWA_ERR_SHAPE;
+    if (!head_dim_ok(D))
+        return SWA_ERR_UNSUPPORTED;
+    {
+        const int rows = (Hq / Hkv) * q_len;
+        if (dtype == SWA_BF16 && rows > 64)
+            return SWA_ERR_UNSUPPORTED;
+        if (dtype == SWA_F32 && rows > 256)
+            return SWA_ERR_UNSUPPORTED;
+    }
+    if ((long long)B * cache_slots * Hkv * D > (1LL << 46))
+        return SWA_ERR_SHAPE;
+    return SWA_OK;
+}
+
+swa_status_t swa_validate_verify_ptrs(const void *q, const void *k_new, const void *v_new,
+                                      const void *k_cache, const void *v_cache,
+                                      const void *cache_len, const void *o)
+{
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_len || !o)
+        return SWA_ERR_NULL;
+    return SWA_OK;
+}
+
+swa_status_t swa_validate_append(const void *k_cache, const void *v_cache, const void *k_new,
+                                 const void *v_new, const void *cache_len, const void *n_append,
+                                 int B, int q_len, int Hkv, int D, int cache_slots, int ring,
+                                 swa_dtype_t dtype)
+{
+    if (!dtype_ok(dtype))
+        return SWA_ERR_UNSUPPORTED;
+    if (B < 0 || q_len < 1 || q_len > 16 || Hkv <= 0 || D <= 0 || cache_slots < 1 ||
+        (ring != 0 && ring != 1))
+        return SWA_ERR_SHAPE;
+    {
+        const long long row = (long long)Hkv * D * (dtype == SWA_BF16 ? 2 : 4);
+        if (row % 16 != 0)
+            return SWA_ERR_UNSUPPORTED;
+    }
+    if (B == 0)
+        return SWA_OK;
+    if (!k_cache || !v_cache || !k_new || !v_new || !cache_len || !n_append)
+        return SWA_ERR_NULL;
+    return SWA_OK;
+}

@@ -1,0 +1,438 @@
+// bf16 multi-token verify (q_len = 1 committed + drafts) over a ring-buffer
+// sliding-window cache or a linear global cache, on gfx950 MFMA.
+//
+// What it computes: each of the q_len tokens under verification is a query
+// at position L_b + t; it attends to the committed keys inside its window and
+// to the new tokens 0..t, with the per-head sink in the denominator.  The
+// release blog (section "Multi-Token Prediction") verifies 1 + 3 drafts in
+// one pass "without increasing KV-cache I/O": here every K/V row read from
+// HBM serves all G * q_len query rows of its KV head (8 heads x 4 tokens =
+// one 32-column MFMA block), so the cache is streamed exactly once.
+//
+// Work decomposition
+//   * Workgroup = (split of the cache rows, KV head g, request b).  Split 0
+//     also takes the tile of q_len new rows.  Within a workgroup, wave w takes
+//     tiles w, w + NW, ... (32 rows each) and keeps its own online-softmax
+//     state for the 32*NB query rows; the waves are merged through LDS at
+//     the end, in a fixed order (bitwise deterministic).
+//   * K rows go straight from HBM into MFMA A-operand registers (S^T = K Q^T);
+//     V rows are written transposed into a per-wave LDS tile to serve as the A
+//     operand of O^T += V^T P^T.  The next tile's loads are issued before the
+//     current tile is computed.
+//   * Rows past the end of the valid cache range are never loaded (zero-
+//     filled), so unused cache slots may hold anything, NaN included.
+//   * With one split per (request, KV head) the workgroup folds the sink and
+//     writes O directly; otherwise it writes (max, sum, unnormalised O) to the
+//     workspace and verify_combine merges the splits, folding the sink once.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace swa {
+
+namespace {
+
+// Cache-row range [c0, c1) (as cache slot indices) of split `s`, and the
+// number of splits, for request length L.
+struct SplitRange {
+  int clo, ncache, ns;
+};
+
+__device__ __forceinline__ SplitRange split_range(const VerifyArgs& p, int L) {
+  SplitRange r;
+  if (p.ring) {
+    r.clo = 0;
+    r.ncache = min(L, p.slots);
+  } else {
+    r.clo = p.window > 0 ? max(0, L - p.window + 1) : 0;
+    r.ncache = L - r.clo;
+  }
+  r.ns = max(1, (r.ncache + p.split_len - 1) / p.split_len);
+  return r;
+}
+
+}  // namespace
+
+template <int D, int NB, int NW, bool DIRECT>
+__global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
+  constexpr int NC = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int VROW = 32 + 4;                 // LDS pitch of a V^T row (bf16)
+  constexpr int VU = 16 * (D / 8);             // (key pair, 8 d) units per tile
+  constexpr int V_IT = VU / 64;
+  constexpr int ACC_N = NB * ND * 16;          // accumulator floats per lane
+  constexpr int MERGE_SLOTS = NW / 2 > 0 ? NW / 2 : 1;
+  static_assert(VU % 64 == 0, "V tile units must split evenly over a wave");
+
+  struct MergeLds {
+    float acc[MERGE_SLOTS][ACC_N][64];
+  };
+  struct TileLds {
+    uint16_t vt[NW][D * VROW];
+  };
+  constexpr size_t LDS_MAIN = sizeof(MergeLds) > sizeof(TileLds) ? sizeof(MergeLds) : sizeof(TileLds);
+  __shared__ __attribute__((aligned(16))) unsigned char lds_main[LDS_MAIN];
+  __shared__ float lds_m[NW][NB * 32];
+  __shared__ float lds_l[NW][NB * 32];
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int L = p.cache_len[b];
+  const SplitRange sr = split_range(p, L);
+  if (s >= sr.ns) return;
+  const int c0 = sr.clo + s * p.split_len;
+  const int c1 = sr.clo + min((s + 1) * p.split_len, sr.ncache);
+  const int ntc = (c1 - c0 + 31) / 32;          // cache tiles of this split
+  const int ntiles = ntc + (s == 0 ? 1 : 0);    // + the tile of new rows
+
+  const int G = p.Hq / p.Hkv;
+  const int R = G * p.T;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const long kv_tok = (long)p.Hkv * D;
+  // ring: slot of the oldest committed position held, to map slot -> position
+  const int ring_n = min(L, p.slots);
+  const int ring_base_slot = p.ring ? (L - ring_n) % p.slots : 0;
+
+  // ---- queries: row m = t * G + hh  ->  token t, head g*G + hh
+  bf16x8 qreg[NB][NC];
+  int qt[NB];
+  float m_run[NB], l_run[NB];
+  f32x16 acc[NB][ND];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int m = nb * 32 + col;
+    qt[nb] = -1;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qreg[nb][c] = bf16x8{};
+    if (m < R) {
+      const int t = m / G, h = g * G + m % G;
+      qt[nb] = t;
+      const uint16_t* qp = p.q + (((long)b * p.T + t) * p.Hq + h) * D + half * 8;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qreg[nb][c] = *(const bf16x8*)(qp + c * 16);
+    }
+    m_run[nb] = kNegInf;
+    l_run[nb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) acc[nb][db] = f32x16{};
+  }
+
+  uint16_t* vt = ((TileLds*)lds_main)->vt[wv];
+  const uint16_t* kcache = p.k_cache + ((long)b * p.slots * p.Hkv + g) * D;
+  const uint16_t* vcache = p.v_cache + ((long)b * p.slots * p.Hkv + g) * D;
+  const uint16_t* knew = p.k_new + ((long)b * p.T * p.Hkv + g) * D;
+  const uint16_t* vnew = p.v_new + ((long)b * p.T * p.Hkv + g) * D;
+
+  // row `r` (0..31) of tile j: pointer offset (in elements, from kcache/knew)
+  // and validity
+  auto row_src = [&](int j, int r, bool& is_new, bool& valid) -> long {
+    is_new = (s == 0 && j == ntc);
+    if (is_new) {
+      valid = r < p.T;
+      return (long)r * kv_tok;
+    }
+    const int ci = c0 + j * 32 + r;
+    valid = ci < c1;
+    return (long)ci * kv_tok;
+  };
+
+  bf16x8 kreg[NC], knext[NC];
+  u32x4 vnext[V_IT][2];
+  auto load_tile = [&](int j, bf16x8 (&kr)[NC], u32x4 (&vr)[V_IT][2]) {
+    bool is_new, valid;
+    const long off = row_src(j, col, is_new, valid);
+    const uint16_t* kp = (is_new ? knew : kcache) + off + half * 8;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[c] = valid ? *(const bf16x8*)(kp + c * 16) : bf16x8{};
+#pragma unroll
+    for (int i = 0; i < V_IT; ++i) {
+      const int u = lane + 64 * i;
+      const int pr = u % 16, c8 = u / 16;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        bool nw, ok;
+        const long o2 = row_src(j, 2 * pr + e, nw, ok);
+        const uint16_t* vp = (nw ? vnew : vcache) + o2 + c8 * 8;
+        vr[i][e] = ok ? *(const u32x4*)vp : u32x4{};
+      }
+    }
+  };
+  auto store_v = [&](const u32x4 (&vr)[V_IT][2]) {
+#pragma unroll
+    for (int i = 0; i < V_IT; ++i) {
+      const int u = lane + 64 * i;
+      const int pr = u % 16, c8 = u / 16;
+      uint32_t* dst = (uint32_t*)&vt[(c8 * 8) * VROW + 2 * pr];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w0 = vr[i][0][e >> 1], w1 = vr[i][1][e >> 1];
+        const uint32_t lo = (e & 1) ? (w0 >> 16) : (w0 & 0xffffu);
+        const uint32_t hi = (e & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
+        dst[e * (VROW / 2)] = lo | hi;
+      }
+    }
+  };
+
+  if (wv < ntiles) {
+    load_tile(wv, kreg, vnext);
+    store_v(vnext);
+  }
+  for (int j = wv; j < ntiles; j += NW) {
+    const bool more = j + NW < ntiles;
+    if (more) load_tile(j + NW, knext, vnext);
+    wave_lds_sync();
+
+    f32x16 sc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma32(kreg[c], qreg[nb][c], sc[nb]);
+    }
+    const bool is_new_tile = (s == 0 && j == ntc);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int t = qt[nb];
+      float mx = kNegInf;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = c_row(v, half);
+        bool ok;
+        if (is_new_tile) {
+          // new token u at position L + u, visible to query t iff u <= t and in window
+          ok = t >= 0 && r < p.T && r <= t && (p.window <= 0 || r > t - p.window);
+        } else {
+          const int ci = c0 + j * 32 + r;
+          int pos = ci;
+          if (p.ring) {
+            const int d = ci - ring_base_slot;
+            pos = L - ring_n + (d >= 0 ? d : d + p.slots);
+          }
+          ok = t >= 0 && ci < c1 && (p.window <= 0 || pos > L + t - p.window);
+        }
+        const float x = ok ? sc[nb][v] * p.scale_log2 : kNegInf;
+        sc[nb][v] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_new = fmaxf(m_run[nb], mx);
+      const bool need = m_new > m_run[nb] + kRescaleTau;
+      if (wave_any(need)) {
+        const float alpha = need ? exp2_fast(m_run[nb] - m_new) : 1.0f;
+        m_run[nb] = need ? m_new : m_run[nb];
+        l_run[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) acc[nb][db] *= alpha;
+      }
+      const float mu = m_run[nb] == kNegInf ? 0.0f : m_run[nb];
+      bf16x8 pb[2];
+      float ls = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float e = exp2_fast(sc[nb][v] - mu);
+        ls += e;
+        pb[v >> 3][v & 7] = (__bf16)e;
+      }
+      l_run[nb] += ls;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const uint16_t* vp = &vt[(db * 32 + col) * VROW + 16 * kc + 4 * half];
+          const u32x2 lo = *(const u32x2*)vp;
+          const u32x2 hi = *(const u32x2*)(vp + 8);
+          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+          acc[nb][db] = mfma32(__builtin_bit_cast(bf16x8, av), pb[kc], acc[nb][db]);
+        }
+      }
+    }
+    wave_lds_sync();
+    if (more) {
+      store_v(vnext);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kreg[c] = knext[c];
+    }
+  }
+
+  // ---- merge the waves: common max, then a fixed-order pairwise sum in LDS
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float lt = l_run[nb] + swap_halves(l_run[nb]);
+    if (half == 0) {
+      lds_m[wv][nb * 32 + col] = m_run[nb];
+      lds_l[wv][nb * 32 + col] = lt;
+    }
+  }
+  __syncthreads();
+  float m_all[NB], l_all[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float mm = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, lds_m[w][nb * 32 + col]);
+    float ll = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = lds_m[w][nb * 32 + col];
+      ll += mw == kNegInf ? 0.0f : lds_l[w][nb * 32 + col] * exp2_fast(mw - mm);
+    }
+    m_all[nb] = mm;
+    l_all[nb] = ll;
+    const float f = m_run[nb] == kNegInf ? 0.0f : exp2_fast(m_run[nb] - mm);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) acc[nb][db] *= f;
+  }
+  MergeLds* ml = (MergeLds*)lds_main;
+#pragma unroll
+  for (int r = NW / 2; r >= 1; r /= 2) {
+    if (wv >= r && wv < 2 * r) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) ml->acc[wv - r][(nb * ND + db) * 16 + v][lane] = acc[nb][db][v];
+    }
+    __syncthreads();
+    if (wv < r) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[nb][db][v] += ml->acc[wv][(nb * ND + db) * 16 + v][lane];
+    }
+    __syncthreads();
+  }
+  if (wv != 0) return;
+
+  // ---- wave 0 writes the result of this split
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int m = nb * 32 + col;
+    if (DIRECT) {
+      if (m >= R) continue;
+      const int t = m / G, h = g * G + m % G;
+      const float sink2 = p.sinks ? p.sinks[h] * kLog2e : kNegInf;
+      const float M = fmaxf(m_all[nb], sink2);
+      const float f = m_all[nb] == kNegInf ? 0.0f : exp2_fast(m_all[nb] - M);
+      const float denom = l_all[nb] * f + (sink2 == kNegInf ? 0.0f : exp2_fast(sink2 - M));
+      const float scale = f / denom;
+      uint16_t* op = p.o + (((long)b * p.T + t) * p.Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 y = {acc[nb][db][4 * a4] * scale, acc[nb][db][4 * a4 + 1] * scale,
+                           acc[nb][db][4 * a4 + 2] * scale, acc[nb][db][4 * a4 + 3] * scale};
+          *(bf16x4*)(op + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(y, bf16x4);
+        }
+      }
+    } else {
+      const long prow = (((long)b * p.Hkv + g) * p.nsplit + s) * p.r_pad + m;
+      float* op = p.ws_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 y = {acc[nb][db][4 * a4], acc[nb][db][4 * a4 + 1], acc[nb][db][4 * a4 + 2],
+                           acc[nb][db][4 * a4 + 3]};
+          *(f32x4*)(op + db * 32 + 8 * a4 + 4 * half) = y;
+        }
+      }
+      if (half == 0) {
+        p.ws_ml[prow * 2] = m_all[nb];
+        p.ws_ml[prow * 2 + 1] = l_all[nb];
+      }
+    }
+  }
+}
+
+// Merge the splits of one (request, KV head): M = max(max_s m_s, sink),
+// l = sum_s l_s 2^(m_s - M) + 2^(sink - M), O = sum_s O_s 2^(m_s - M) / l.
+template <int D>
+__global__ __launch_bounds__(256) void verify_combine_kernel(VerifyArgs p) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int L = p.cache_len[b];
+  const SplitRange sr = split_range(p, L);
+  const int G = p.Hq / p.Hkv;
+  const int R = G * p.T;
+  constexpr int TPR = D / 4;            // threads per row (4 floats each)
+  constexpr int RPP = 256 / TPR;        // rows per pass
+  const int tid = threadIdx.x;
+  const int d = (tid % TPR) * 4;
+  for (int m = tid / TPR; m < R; m += RPP) {
+    const int t = m / G, h = g * G + m % G;
+    const long base = ((long)b * p.Hkv + g) * p.nsplit * p.r_pad + m;
+    const float sink2 = p.sinks ? p.sinks[h] * kLog2e : kNegInf;
+    float M = sink2;
+    for (int s = 0; s < sr.ns; ++s) M = fmaxf(M, p.ws_ml[(base + (long)s * p.r_pad) * 2]);
+    float l = sink2 == kNegInf ? 0.0f : exp2_fast(sink2 - M);
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < sr.ns; ++s) {
+      const long row = base + (long)s * p.r_pad;
+      const float ms = p.ws_ml[row * 2];
+      if (ms == kNegInf) continue;
+      const float f = exp2_fast(ms - M);
+      l += p.ws_ml[row * 2 + 1] * f;
+      const f32x4 x = *(const f32x4*)(p.ws_o + row * D + d);
+      o += x * f;
+    }
+    o *= 1.0f / l;
+    uint16_t* op = p.o + (((long)b * p.T + t) * p.Hq + h) * D + d;
+    *(bf16x4*)op = __builtin_convertvector(o, bf16x4);
+  }
+}
+
+VerifyPlan plan_verify_bf16(int B, int T, int Hq, int Hkv, int D, int slots, int ring, int window) {
+  VerifyPlan pl;
+  const int G = Hq / Hkv;
+  const int R = G * T;
+  pl.nb = R <= 32 ? 1 : 2;
+  pl.waves = pl.nb == 1 ? 4 : 2;
+  const int unit = 32 * pl.waves;
+  // most cache rows one request can need
+  long max_rows = slots;
+  if (!ring && window > 0 && window - 1 < max_rows) max_rows = window - 1;
+  if (max_rows < 1) max_rows = 1;
+  // aim for >= ~1024 workgroups, splits of at most 4096 rows
+  long want = max_rows * (long)B * Hkv / 1024;
+  long sl = unit;
+  while (sl < want && sl < 4096) sl *= 2;
+  if (sl < unit) sl = unit;
+  sl = (sl + unit - 1) / unit * unit;
+  pl.split_len = (int)sl;
+  pl.nsplit = (int)((max_rows + sl - 1) / sl);
+  if (pl.nsplit < 1) pl.nsplit = 1;
+  const long r_pad = 32L * pl.nb;
+  pl.ws_bytes = pl.nsplit == 1 ? 0
+                               : (size_t)B * Hkv * pl.nsplit * r_pad * (size_t)(D + 2) * sizeof(float);
+  return pl;
+}
+
+template <int D, int NB, int NW>
+static hipError_t launch_verify_t(VerifyArgs a, const VerifyPlan& pl, hipStream_t s) {
+  dim3 grid(pl.nsplit, a.Hkv, a.B), block(NW * 64);
+  if (pl.nsplit == 1) {
+    hipLaunchKernelGGL((verify_bf16_kernel<D, NB, NW, true>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((verify_bf16_kernel<D, NB, NW, false>), grid, block, 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((verify_combine_kernel<D>), dim3(a.Hkv, a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_bf16(const VerifyArgs& a0, const VerifyPlan& pl, hipStream_t s) {
+  VerifyArgs a = a0;
+  a.split_len = pl.split_len;
+  a.nsplit = pl.nsplit;
+  a.r_pad = 32 * pl.nb;
+  if (a.D == 128) {
+    return pl.nb == 1 ? launch_verify_t<128, 1, 4>(a, pl, s) : launch_verify_t<128, 2, 2>(a, pl, s);
+  }
+  return pl.nb == 1 ? launch_verify_t<64, 1, 4>(a, pl, s) : launch_verify_t<64, 2, 2>(a, pl, s);
+}
+
+}  // namespace swa

@@ -1,0 +1,167 @@
+/*
+ * swa_attn.h -- C ABI of the MI355X (gfx950) sliding-window / global
+ * attention library with per-head attention sinks.
+ *
+ * The operation (from the pages on MiMo-V2-Flash):
+ *   - Sliding-window attention with a window of W = 128 tokens, interleaved
+ *     5:1 with global attention (W = infinity) in the same model; the MTP
+ *     draft layers use the sliding window too.  MiMo-V2-Flash technical-report
+ *     digest (fanfer.top), section "MiMo-V2-Flash Model Architecture"; release
+ *     blog (aihot.news), section on pushing efficiency to the limit.
+ *   - A learnable attention-sink bias per head in the gpt-oss style: the sink
+ *     logit adds exp(sink) to the softmax denominator and carries no value.
+ *     Technical-report digest, paragraph "Hybrid Sliding Window Attention
+ *     Architecture".
+ *   - MTP self-speculative decoding: the main model verifies 1 committed + 3
+ *     draft tokens in one pass without extra KV-cache I/O, accepts a prefix
+ *     and discards the rest.  Release blog, section "Multi-Token Prediction"
+ *     (verify diagram and the paragraph after it).
+ *   - The SWA layers keep a fixed-size KV cache.  Release blog, section on
+ *     pushing efficiency to the limit.
+ *
+ * Definition computed by every entry point, for request b, query head h,
+ * query at absolute position i (G = Hq / Hkv, KV head g = h / G):
+ *   J(i) = { j : max(0, i - W + 1) <= j <= i }   (W keys including self;
+ *          all j <= i when window <= 0)
+ *   s_j  = sm_scale * <q, K[j, g]>
+ *   O    = sum_{j in J(i)} exp(s_j) V[j, g] / (exp(sink_h) + sum_{j in J(i)} exp(s_j))
+ * With sinks == NULL (or a sink of -inf) the exp(sink_h) term is absent.
+ *
+ * Conventions common to all entry points
+ *   - Tensors are dense, row-major, token-major: [B, S, H, D] (the last index
+ *     is contiguous).  Every data pointer is a DEVICE pointer (hipMalloc'd or
+ *     from a framework allocator) owned by the caller.  The library allocates
+ *     no memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work on it and return without synchronising.
+ *   - Host-visible arguments are validated before anything is launched; on a
+ *     failure a nonzero status is returned and nothing is enqueued.
+ *     Values that live in device memory (cache_len, n_append) cannot be
+ *     checked without a synchronisation and are PRECONDITIONS (listed per
+ *     entry point); violating them is undefined behaviour.
+ *   - dtype SWA_BF16: q, k, v, o and caches are bfloat16; scores, softmax and
+ *     accumulation are fp32, the attention weights are rounded to bf16 before
+ *     the value product, and O is rounded to bf16 (round to nearest even).
+ *     dtype SWA_F32: everything is fp32 and nothing is rounded to bf16.
+ *   - sinks, when given, are fp32 [Hq] device values: finite or -inf.
+ *   - Supported: D in {64, 128}; Hq % Hkv == 0.  The bf16 paths also need
+ *     32 % (Hq / Hkv) == 0 (prefill) and (Hq / Hkv) * q_len <= 64 (verify).
+ */
+#ifndef SWA_ATTN_H
+#define SWA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Entry points are the only symbols the shared library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define SWA_API __attribute__((visibility("default")))
+#else
+#define SWA_API
+#endif
+
+typedef enum {
+    SWA_OK = 0,
+    SWA_ERR_NULL = 1,        /* a required pointer is NULL */
+    SWA_ERR_SHAPE = 2,       /* sizes violate a shape rule */
+    SWA_ERR_UNSUPPORTED = 3, /* valid but not implemented (dtype, D, grouping) */
+    SWA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+    SWA_ERR_LAUNCH = 5       /* the HIP runtime reported a launch error */
+} swa_status_t;
+
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype_t;
+
+/* Static, NUL-terminated description of a status code. */
+SWA_API const char *swa_status_string(swa_status_t status);
+
+/*
+ * Causal prefill (also chunked prefill and prefill after a cached prefix).
+ *   q      [B, Sq, Hq, D]   queries; query row r sits at absolute position
+ *                           q_offset + r
+ *   k, v   [B, Sk, Hkv, D]  keys / values of positions 0 .. Sk-1
+ *   sinks  [Hq] fp32 or NULL
+ *   o      [B, Sq, Hq, D]   output (same dtype as q); must not alias inputs
+ *   window >= 1: sliding window of `window` keys including the query's own
+ *          position; <= 0: global causal attention
+ *   q_offset  0 <= q_offset and q_offset + Sq <= Sk.  Fresh prefill uses 0; a
+ *          chunk [c0, c0 + C) of a long sequence passes its queries, the full
+ *          k / v and q_offset = c0 (only keys >= c0 - window + 1 are read).
+ *   sm_scale  multiplier of q.k (normally 1/sqrt(D)); the sink is not scaled.
+ * Rows of k / v inside a loaded 32-key tile but outside the window are read
+ * and weighted by exactly zero, so k and v must be finite for all Sk rows.
+ * B == 0 or Sq == 0 is a valid no-op.
+ */
+SWA_API swa_status_t swa_attn_prefill(const void *q, const void *k, const void *v,
+                              const float *sinks, void *o,
+                              int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                              int window, int q_offset, float sm_scale,
+                              swa_dtype_t dtype, void *stream);
+
+/*
+ * Bytes of device workspace swa_attn_verify needs for these sizes (split-KV
+ * partial results: running max, running sum and unnormalised output per
+ * query row and split).  0 when the arguments are invalid.
+ */
+SWA_API size_t swa_attn_verify_workspace_bytes(int B, int q_len, int Hq, int Hkv, int D,
+                                       int cache_slots, int ring, int window,
+                                       swa_dtype_t dtype);
+
+/*
+ * Multi-token verify step (q_len = 1 + number of drafts; q_len = 1 is plain
+ * decode) over a KV cache.
+ *   q             [B, q_len, Hq, D]   token t of request b sits at position
+ *                                     cache_len[b] + t
+ *   k_new, v_new  [B, q_len, Hkv, D]  keys / values of the tokens under
+ *                                     verification (not yet in the cache);
+ *                                     token t sees new tokens 0..t
+ *   k_cache, v_cache [B, cache_slots, Hkv, D]
+ *       ring == 1: ring buffer, position p lives in slot p % cache_slots;
+ *                  requires window >= 1 and cache_slots >= window.  Holds the
+ *                  last min(L_b, cache_slots) committed positions.
+ *       ring == 0: linear cache, position p lives in slot p.
+ *   cache_len     [B] int32 DEVICE array: L_b committed tokens per request.
+ *   sinks [Hq] fp32 or NULL;  o [B, q_len, Hq, D] output.
+ *   workspace     device buffer of at least
+ *                 swa_attn_verify_workspace_bytes(...) bytes (any alignment
+ *                 of 256 bytes or more); its contents are scratch.
+ * Device-side preconditions (not checked): 0 <= L_b; for ring == 0,
+ * L_b <= cache_slots.  Cache slots that hold no committed position are never
+ * read (they may hold NaN).  Calls that share a workspace must not overlap.
+ */
+SWA_API swa_status_t swa_attn_verify(const void *q, const void *k_new, const void *v_new,
+                             const void *k_cache, const void *v_cache,
+                             const int32_t *cache_len, const float *sinks, void *o,
+                             int B, int q_len, int Hq, int Hkv, int D,
+                             int cache_slots, int ring, int window, float sm_scale,
+                             swa_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * Commit accepted tokens after a verify step.  For every request b and every
+ * t < n_append[b], row t of k_new / v_new [B, q_len, Hkv, D] is copied to the
+ * slot of position cache_len[b] + t: slot (cache_len[b] + t) % cache_slots
+ * when ring == 1, slot cache_len[b] + t when ring == 0.  No other slot
+ * changes, cache_len is only read (the caller advances it by n_append), and
+ * rejected drafts never touch the cache (release blog, section
+ * "Multi-Token Prediction": accept a prefix, reject one token, discard the
+ * rest).
+ *   cache_len, n_append: [B] int32 DEVICE arrays.
+ * Device-side preconditions (not checked): 0 <= n_append[b] <= q_len,
+ * 0 <= cache_len[b], and for ring == 0 cache_len[b] + n_append[b] <= cache_slots.
+ * Works for either dtype (a copy of 2- or 4-byte elements).
+ */
+SWA_API swa_status_t kv_ring_append(void *k_cache, void *v_cache,
+                            const void *k_new, const void *v_new,
+                            const int32_t *cache_len, const int32_t *n_append,
+                            int B, int q_len, int Hkv, int D, int cache_slots, int ring,
+                            swa_dtype_t dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_ATTN_H */

@@ -1,0 +1,128 @@
+"""CPU checks of the C ABI: the library loads, exports exactly the declared
+entry points, and rejects bad host-visible arguments before launching
+anything (these calls return before any HIP call, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_sliding_window_swa_amd as swa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa_attn.h")
+OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
+BF16, F32 = 1, 0
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(swa.library_path()):
+        from hybrid_sliding_window_swa_amd import build
+        build.build()
+    return swa.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return set(re.findall(r"^SWA_API\s+(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, re.M))
+
+
+def test_header_declares_entry_points():
+    assert declared_symbols() == set(swa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    # and nothing else with external linkage in the text section
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", swa.library_path()],
+                         capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == declared_symbols()
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.swa_status_string(code)
+
+
+def _prefill(lib, q=1, k=1, v=1, o=1, B=1, Sq=8, Sk=8, Hq=8, Hkv=1, D=128, W=128, off=0, dt=BF16):
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.swa_attn_prefill(P(q), P(k), P(v), None, P(o), B, Sq, Sk, Hq, Hkv, D, W, off, 0.1, dt, None)
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, q=0) == NULL
+    assert _prefill(lib, o=0) == NULL
+    assert _prefill(lib, Hq=6, Hkv=4) == SHAPE
+    assert _prefill(lib, D=96) == UNSUP
+    assert _prefill(lib, D=256) == UNSUP
+    assert _prefill(lib, off=1) == SHAPE            # q_offset + Sq > Sk
+    assert _prefill(lib, off=-1) == SHAPE
+    assert _prefill(lib, Sq=-1) == SHAPE
+    assert _prefill(lib, dt=7) == UNSUP
+    assert _prefill(lib, Hq=64, Hkv=1) == UNSUP     # bf16 needs 32 % G == 0
+    assert _prefill(lib, Hq=12, Hkv=4) == UNSUP     # G = 3
+    assert _prefill(lib, Hq=256, Hkv=1, dt=F32) == UNSUP
+    # empty work is a no-op even with NULL pointers
+    assert _prefill(lib, q=0, k=0, v=0, o=0, B=0) == OK
+    assert _prefill(lib, q=0, k=0, v=0, o=0, Sq=0) == OK
+
+
+def _verify(lib, ptr=1, B=2, T=4, Hq=64, Hkv=8, D=128, slots=128, ring=1, W=128, dt=BF16,
+            ws=None, ws_bytes=0):
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.swa_attn_verify(P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), None, P(ptr),
+                               B, T, Hq, Hkv, D, slots, ring, W, 0.1, dt, P(ws), ws_bytes, None)
+
+
+def test_verify_validation(lib):
+    assert _verify(lib, ptr=0) == NULL
+    assert _verify(lib, T=0) == SHAPE
+    assert _verify(lib, T=17) == SHAPE
+    assert _verify(lib, slots=127) == SHAPE          # ring shorter than the window
+    assert _verify(lib, W=0) == SHAPE                # ring needs a finite window
+    assert _verify(lib, ring=2) == SHAPE
+    assert _verify(lib, Hq=63) == SHAPE
+    assert _verify(lib, D=32) == UNSUP
+    assert _verify(lib, T=9) == UNSUP                # bf16: G * q_len <= 64
+    assert _verify(lib, dt=3) == UNSUP
+    # linear global cache with many rows needs a workspace
+    assert _verify(lib, ring=0, W=0, slots=65536, ws=None) == WS
+    need = lib.swa_attn_verify_workspace_bytes(2, 4, 64, 8, 128, 65536, 0, 0, BF16)
+    assert need > 0
+    assert _verify(lib, ring=0, W=0, slots=65536, ws=256, ws_bytes=need - 1) == WS
+    assert _verify(lib, ring=0, W=0, slots=65536, ws=257, ws_bytes=need) == WS  # misaligned
+    assert _verify(lib, B=0, ptr=0) == OK
+
+
+def test_workspace_sizes(lib):
+    ws = lambda *a: lib.swa_attn_verify_workspace_bytes(*a)
+    # ring of 128 slots: one split, the kernel writes O directly
+    assert ws(64, 4, 64, 8, 128, 128, 1, 128, BF16) == 0
+    # fp32 path needs none
+    assert ws(64, 4, 64, 8, 128, 65536, 0, 0, F32) == 0
+    # invalid arguments -> 0
+    assert ws(64, 4, 64, 8, 100, 65536, 0, 0, BF16) == 0
+    # global cache of 65536 rows: splits of <= 4096 rows, (D + 2) floats per row and split
+    b = ws(64, 4, 64, 8, 128, 65536, 0, 0, BF16)
+    assert b == 64 * 8 * 16 * 32 * 130 * 4
+    # one request of 262148 rows: splits of 2048 rows
+    assert ws(1, 4, 64, 8, 128, 262148, 0, 0, BF16) == 1 * 8 * 129 * 32 * 130 * 4
+
+
+def _append(lib, ptr=1, B=2, T=4, Hkv=8, D=128, slots=128, ring=1, dt=BF16):
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.kv_ring_append(P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), B, T, Hkv, D,
+                              slots, ring, dt, None)
+
+
+def test_append_validation(lib):
+    assert _append(lib, ptr=0) == NULL
+    assert _append(lib, slots=0) == SHAPE
+    assert _append(lib, T=0) == SHAPE
+    assert _append(lib, ring=5) == SHAPE
+    assert _append(lib, Hkv=1, D=3) == UNSUP        # row not a multiple of 16 bytes
+    assert _append(lib, B=0, ptr=0) == OK
