@@ -1,0 +1,290 @@
+"""Benchmark of the sliding-window / global attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one bf16 SWA (W=128) + sink prefill of 32768 tokens (B=1, 64
+query heads, 8 KV heads, head_dim 128, causal).  `value` is that prefill's
+throughput in algorithmic TFLOP/s (4*D FLOP per (query head, key) pair inside
+the window; masked or skipped tile work is not counted), over K timed steps
+with inputs resident in HBM.  The same run also times the q_len=4 MTP verify
+on 64 requests (global-layer cache with contexts U[4096, 65536] and a
+128-slot SWA ring) and reports its HBM GB/s from algorithmic bytes (every
+K/V row the windows need read once, plus Q, the new rows and O).
+
+Prints ONE JSON line.  Inputs are seeded synthetic N(0,1) tensors rounded to
+bf16 (random numbers, no dataset).  --gpus above 1 is refused: this build
+runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+PREFILL_KERNEL_SRC = os.path.join(ROOT, "hybrid_sliding_window_swa_amd", "csrc", "prefill_bf16.hip")
+VERIFY_KERNEL_SRC = os.path.join(ROOT, "hybrid_sliding_window_swa_amd", "csrc", "verify_bf16.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true", help="time the prefill only")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (HBM counter calibration) and exit")
+    return ap.parse_args()
+
+
+def swa_pairs(S: int, W: int, q_offset: int = 0) -> int:
+    """(query, key) pairs inside the causal window, per head."""
+    if W <= 0:
+        return sum(q_offset + r + 1 for r in range(S))
+    tot = 0
+    for r in range(S):
+        i = q_offset + r
+        tot += min(i + 1, W)
+    return tot
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(name: str, src: str):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy-kernel calibration), kept under profiles/.
+    Returns None if absent or taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_hash(src):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_launches(fn, steps, stream, before=None):
+    """Average duration (ms) of fn() over `steps` launches, measured with HIP
+    events recorded on the stream the kernels run on."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        if before is not None:
+            before()
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design note, not part of this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hybrid_sliding_window_swa_amd as swa
+    from swa_inputs import PREFILL_CONFIGS, VERIFY_CONFIGS, prefill_inputs, verify_inputs
+
+    swa.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
+
+    # ------------------------------------------------------------ prefill
+    cfg = PREFILL_CONFIGS["swa_32k"]
+    q, k, v, sinks = prefill_inputs(cfg, device=dev)
+    o = torch.empty_like(q)
+    pairs = swa_pairs(cfg.S, cfg.window) * cfg.Hq * cfg.B
+    flop = 4.0 * cfg.D * pairs
+    elt = 2
+    p_bytes = elt * cfg.B * (2 * cfg.S * cfg.Hq * cfg.D + 2 * cfg.keys * cfg.Hkv * cfg.D)
+
+    def prefill():
+        swa.swa_attn_prefill(q, k, v, sinks, cfg.window, cfg.q_offset, cfg.scale, out=o)
+
+    for _ in range(args.warmup):
+        prefill()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        prefill()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    value = flop / (wall / args.steps) / 1e12
+    ms_kernel = time_launches(prefill, max(args.steps, 5), stream)
+    ach_gbs = p_bytes / (ms_kernel * 1e-3) / 1e9
+    traffic = read_traffic("prefill_bf16_swa32k_hbm_counters.txt", PREFILL_KERNEL_SRC)
+
+    result = {
+        "metric": "SWA(W=128)+sink attn: prefill TFLOP/s; q_len=4 verify-decode HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "swa_32k_prefill",
+            "batch": cfg.B, "seq_len": cfg.S, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
+            "head_dim": cfg.D, "window": cfg.window, "causal": True, "sinks": "per-head N(0,1)",
+            "inputs": "seeded N(0,1) rounded to bf16", "algorithmic_flop_per_step": flop,
+            "algorithmic_bytes_per_step": p_bytes,
+        },
+        "roofline": {
+            "kernel": "prefill_bf16_kernel",
+            "bound": "hbm",
+            "achieved": round(ach_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(ach_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_ms": round(ms_kernel, 5),
+            "mfma_tflops": round(flop / (ms_kernel * 1e-3) / 1e12, 2),
+            "mfma_frac_of_bf16_peak": round(flop / (ms_kernel * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline_tflops": round(min(MFMA_BF16_PEAK_TFLOPS, flop / p_bytes * HBM_PEAK_GBS / 1e3), 1),
+        },
+    }
+    del o
+
+    # ------------------------------------------------------------ verify
+    if not args.no_verify:
+        vres = {}
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for name in ("verify_ga_b64", "verify_swa_b64"):
+            vc = VERIFY_CONFIGS[name]
+            inp = verify_inputs(vc, device=dev)
+            cl = inp["cache_len"].to(torch.int32).to(dev)
+            L = inp["cache_len"].to(torch.int64)
+            need = swa.swa_attn_verify_workspace_bytes(vc.B, vc.T, vc.Hq, vc.Hkv, vc.D, vc.slots,
+                                                       vc.ring, vc.window)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            ov = torch.empty_like(inp["q"])
+            # rows the windows need: history positions max(0, L-W+1) .. L-1 (global: 0 .. L-1)
+            if vc.window > 0:
+                hist_rows = int(torch.clamp(L, max=vc.window - 1).sum())
+            else:
+                hist_rows = int(L.sum())
+            row_b = vc.Hkv * vc.D * 2
+            vbytes = (2 * hist_rows * row_b                      # K and V history
+                      + 2 * vc.B * vc.T * row_b                  # new K and V rows
+                      + 2 * vc.B * vc.T * vc.Hq * vc.D * 2)      # Q in, O out
+
+            def verify():
+                swa.swa_attn_verify(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"],
+                                    inp["v_cache"], cl, inp["sinks"], vc.window, vc.ring, vc.scale,
+                                    workspace=ws, out=ov)
+
+            for _ in range(args.warmup):
+                verify()
+            # small working sets would sit in the 256 MB Infinity Cache: flush it first
+            before = (lambda: flush.zero_()) if vbytes < (1 << 30) else None
+            ms = time_launches(verify, max(args.steps, 5), stream, before)
+            vres[name] = {
+                "workload": name, "batch": vc.B, "q_len": vc.T, "cache": "ring" if vc.ring else "linear",
+                "slots": vc.slots, "window": vc.window, "context_lengths": [vc.len_lo, vc.len_hi],
+                "algorithmic_bytes": vbytes, "ms": round(ms, 5),
+                "GB/s": round(vbytes / (ms * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(vbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            }
+            del inp, ws, ov
+            torch.cuda.empty_cache()
+        ga = vres["verify_ga_b64"]
+        result["verify"] = {
+            "metric": "q_len=4 verify-decode HBM GB/s",
+            "value": ga["GB/s"], "unit": "GB/s", "workloads": vres,
+            "roofline": {
+                "kernel": "verify_bf16_kernel + verify_combine_kernel", "bound": "hbm",
+                "achieved": ga["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ga["frac_of_hbm_peak"],
+                "traffic": read_traffic("verify_bf16_ga_b64_hbm_counters.txt", VERIFY_KERNEL_SRC),
+            },
+        }
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, sinks, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, q, k, v, sinks, target_s):
+    """Time the CPU oracle on a bounded sample of rows of the same workload
+    and convert to algorithmic TFLOP/s."""
+    import torch
+    import oracle
+    from swa_inputs import sample_rows
+
+    threads = oracle.num_threads()
+    kk = k[0].float().cpu()
+    vv = v[0].float().cpu()
+    s = sinks.cpu()
+
+    def run(n):
+        rows = sample_rows(cfg.S, n, 777 + n, ())
+        qr = q[0].index_select(0, rows.to(q.device)).cpu()
+        t0 = time.perf_counter()
+        oracle.prefill_rows(qr, rows, kk, vv, s, cfg.window, cfg.q_offset, cfg.scale)
+        dt = time.perf_counter() - t0
+        pairs = sum(min(int(r) + cfg.q_offset + 1, cfg.window) for r in rows) * cfg.Hq
+        return dt, pairs, len(rows)
+
+    dt, pairs, n = run(256)
+    scale = max(1.0, target_s / max(dt, 1e-3))
+    n2 = min(cfg.S, int(256 * scale))
+    dt, pairs, n = run(n2)
+    flop = 4.0 * cfg.D * pairs
+    return {
+        "value": round(flop / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n} of {cfg.S} query rows x {cfg.Hq} heads of the swa_32k prefill "
+                  f"(fp64 C oracle, OpenMP), {dt:.1f} s",
+        "seconds": round(dt, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()
