@@ -40,7 +40,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-verify", action="store_true", help="time the prefill only")
+    ap.add_argument("--no-verify", action="store_true", help="time the SWA prefill only")
+    ap.add_argument("--only", choices=["prefill", "ga", "verify"], default=None,
+                    help="run one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -99,6 +101,134 @@ def time_launches(fn, steps, stream, before=None):
     return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
 
 
+def run_prefill(args, swa, torch, dev, stream, cfg):
+    """Time the SWA 32K prefill: wall clock over K steps + per-launch events."""
+    from swa_inputs import prefill_inputs
+    q, k, v, sinks = prefill_inputs(cfg, device=dev)
+    o = torch.empty_like(q)
+    flop = 4.0 * cfg.D * swa_pairs(cfg.S, cfg.window) * cfg.Hq * cfg.B
+    p_bytes = 2 * cfg.B * (2 * cfg.S * cfg.Hq * cfg.D + 2 * cfg.keys * cfg.Hkv * cfg.D)
+
+    def prefill():
+        swa.swa_attn_prefill(q, k, v, sinks, cfg.window, cfg.q_offset, cfg.scale, out=o)
+
+    for _ in range(args.warmup):
+        prefill()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        prefill()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_kernel = time_launches(prefill, max(args.steps, 5), stream)
+    ach_gbs = p_bytes / (ms_kernel * 1e-3) / 1e9
+    res = {
+        "ms_per_step": wall * 1e3 / args.steps,
+        "value": flop / (wall / args.steps) / 1e12,
+        "config": {
+            "workload": "swa_32k_prefill",
+            "batch": cfg.B, "seq_len": cfg.S, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
+            "head_dim": cfg.D, "window": cfg.window, "causal": True, "sinks": "per-head N(0,1)",
+            "inputs": "seeded N(0,1) rounded to bf16", "algorithmic_flop_per_step": flop,
+            "algorithmic_bytes_per_step": p_bytes,
+        },
+        "roofline": {
+            "kernel": "prefill_swa_strip_kernel",
+            "bound": "hbm",
+            "achieved": round(ach_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(ach_gbs / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic("prefill_bf16_swa32k_hbm_counters.txt", PREFILL_KERNEL_SRC),
+            "kernel_ms": round(ms_kernel, 5),
+            "mfma_tflops": round(flop / (ms_kernel * 1e-3) / 1e12, 2),
+            "mfma_frac_of_bf16_peak": round(flop / (ms_kernel * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline_tflops": round(min(MFMA_BF16_PEAK_TFLOPS, flop / p_bytes * HBM_PEAK_GBS / 1e3), 1),
+        },
+    }
+    return res, (q, k, v, sinks)
+
+
+def run_ga(args, swa, torch, dev, stream):
+    """Time the global-attention 32K prefill (per-launch events)."""
+    from swa_inputs import PREFILL_CONFIGS, prefill_inputs
+    gcfg = PREFILL_CONFIGS["ga_32k"]
+    gq, gk, gv, gs = prefill_inputs(gcfg, device=dev)
+    go = torch.empty_like(gq)
+    gflop = 4.0 * gcfg.D * swa_pairs(gcfg.S, gcfg.window) * gcfg.Hq * gcfg.B
+
+    def ga_prefill():
+        swa.swa_attn_prefill(gq, gk, gv, gs, gcfg.window, gcfg.q_offset, gcfg.scale, out=go)
+
+    for _ in range(max(1, args.warmup)):
+        ga_prefill()
+    gms = time_launches(ga_prefill, max(3, min(args.steps, 10)), stream)
+    del gq, gk, gv, go
+    torch.cuda.empty_cache()
+    return {
+        "workload": "ga_32k_prefill", "window": "global", "seq_len": gcfg.S,
+        "algorithmic_flop": gflop, "ms": round(gms, 4),
+        "TFLOP/s": round(gflop / (gms * 1e-3) / 1e12, 2),
+        "frac_of_bf16_mfma_peak": round(gflop / (gms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+    }
+
+
+def run_verify(args, swa, torch, dev, stream):
+    """Time the q_len=4 verify on the global-layer cache and the SWA ring."""
+    from swa_inputs import VERIFY_CONFIGS, verify_inputs
+    vres = {}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for name in ("verify_ga_b64", "verify_swa_b64"):
+        vc = VERIFY_CONFIGS[name]
+        inp = verify_inputs(vc, device=dev)
+        cl = inp["cache_len"].to(torch.int32).to(dev)
+        L = inp["cache_len"].to(torch.int64)
+        need = swa.swa_attn_verify_workspace_bytes(vc.B, vc.T, vc.Hq, vc.Hkv, vc.D, vc.slots,
+                                                   vc.ring, vc.window)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ov = torch.empty_like(inp["q"])
+        # rows the windows need: history positions max(0, L-W+1) .. L-1 (global: 0 .. L-1)
+        if vc.window > 0:
+            hist_rows = int(torch.clamp(L, max=vc.window - 1).sum())
+        else:
+            hist_rows = int(L.sum())
+        row_b = vc.Hkv * vc.D * 2
+        vbytes = (2 * hist_rows * row_b                      # K and V history
+                  + 2 * vc.B * vc.T * row_b                  # new K and V rows
+                  + 2 * vc.B * vc.T * vc.Hq * vc.D * 2)      # Q in, O out
+
+        def verify():
+            swa.swa_attn_verify(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"],
+                                inp["v_cache"], cl, inp["sinks"], vc.window, vc.ring, vc.scale,
+                                workspace=ws, out=ov)
+
+        for _ in range(args.warmup):
+            verify()
+        # small working sets would sit in the 256 MB Infinity Cache: flush it first
+        before = (lambda: flush.zero_()) if vbytes < (1 << 30) else None
+        ms = time_launches(verify, max(args.steps, 5), stream, before)
+        vres[name] = {
+            "workload": name, "batch": vc.B, "q_len": vc.T, "cache": "ring" if vc.ring else "linear",
+            "slots": vc.slots, "window": vc.window, "context_lengths": [vc.len_lo, vc.len_hi],
+            "algorithmic_bytes": vbytes, "ms": round(ms, 5),
+            "GB/s": round(vbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(vbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+        del inp, ws, ov
+        torch.cuda.empty_cache()
+    ga = vres["verify_ga_b64"]
+    return {
+        "metric": "q_len=4 verify-decode HBM GB/s",
+        "value": ga["GB/s"], "unit": "GB/s", "workloads": vres,
+        "roofline": {
+            "kernel": "verify_bf16_kernel + verify_combine_kernel", "bound": "hbm",
+            "achieved": ga["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": ga["frac_of_hbm_peak"],
+            "traffic": read_traffic("verify_bf16_ga_b64_hbm_counters.txt", VERIFY_KERNEL_SRC),
+        },
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -108,7 +238,7 @@ def main():
 
     import torch
     import hybrid_sliding_window_swa_amd as swa
-    from swa_inputs import PREFILL_CONFIGS, VERIFY_CONFIGS, prefill_inputs, verify_inputs
+    from swa_inputs import PREFILL_CONFIGS
 
     swa.load_library()
     dev = torch.device("cuda:0")
@@ -126,126 +256,36 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
         return
 
-    # ------------------------------------------------------------ prefill
+    if args.only == "ga":
+        print(json.dumps({"ga_prefill": run_ga(args, swa, torch, dev, stream)}), flush=True)
+        return
+    if args.only == "verify":
+        print(json.dumps({"verify": run_verify(args, swa, torch, dev, stream)}), flush=True)
+        return
+
     cfg = PREFILL_CONFIGS["swa_32k"]
-    q, k, v, sinks = prefill_inputs(cfg, device=dev)
-    o = torch.empty_like(q)
-    pairs = swa_pairs(cfg.S, cfg.window) * cfg.Hq * cfg.B
-    flop = 4.0 * cfg.D * pairs
-    elt = 2
-    p_bytes = elt * cfg.B * (2 * cfg.S * cfg.Hq * cfg.D + 2 * cfg.keys * cfg.Hkv * cfg.D)
-
-    def prefill():
-        swa.swa_attn_prefill(q, k, v, sinks, cfg.window, cfg.q_offset, cfg.scale, out=o)
-
-    for _ in range(args.warmup):
-        prefill()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        prefill()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    value = flop / (wall / args.steps) / 1e12
-    ms_kernel = time_launches(prefill, max(args.steps, 5), stream)
-    ach_gbs = p_bytes / (ms_kernel * 1e-3) / 1e9
-    traffic = read_traffic("prefill_bf16_swa32k_hbm_counters.txt", PREFILL_KERNEL_SRC)
-
+    pres, tensors = run_prefill(args, swa, torch, dev, stream, cfg)
     result = {
         "metric": "SWA(W=128)+sink attn: prefill TFLOP/s; q_len=4 verify-decode HBM GB/s",
-        "value": round(value, 2),
+        "value": round(pres["value"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(pres["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {
-            "workload": "swa_32k_prefill",
-            "batch": cfg.B, "seq_len": cfg.S, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
-            "head_dim": cfg.D, "window": cfg.window, "causal": True, "sinks": "per-head N(0,1)",
-            "inputs": "seeded N(0,1) rounded to bf16", "algorithmic_flop_per_step": flop,
-            "algorithmic_bytes_per_step": p_bytes,
-        },
-        "roofline": {
-            "kernel": "prefill_bf16_kernel",
-            "bound": "hbm",
-            "achieved": round(ach_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(ach_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel_ms": round(ms_kernel, 5),
-            "mfma_tflops": round(flop / (ms_kernel * 1e-3) / 1e12, 2),
-            "mfma_frac_of_bf16_peak": round(flop / (ms_kernel * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "roofline_tflops": round(min(MFMA_BF16_PEAK_TFLOPS, flop / p_bytes * HBM_PEAK_GBS / 1e3), 1),
-        },
+        "config": pres["config"],
+        "roofline": pres["roofline"],
     }
-    del o
-
-    # ------------------------------------------------------------ verify
-    if not args.no_verify:
-        vres = {}
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        for name in ("verify_ga_b64", "verify_swa_b64"):
-            vc = VERIFY_CONFIGS[name]
-            inp = verify_inputs(vc, device=dev)
-            cl = inp["cache_len"].to(torch.int32).to(dev)
-            L = inp["cache_len"].to(torch.int64)
-            need = swa.swa_attn_verify_workspace_bytes(vc.B, vc.T, vc.Hq, vc.Hkv, vc.D, vc.slots,
-                                                       vc.ring, vc.window)
-            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-            ov = torch.empty_like(inp["q"])
-            # rows the windows need: history positions max(0, L-W+1) .. L-1 (global: 0 .. L-1)
-            if vc.window > 0:
-                hist_rows = int(torch.clamp(L, max=vc.window - 1).sum())
-            else:
-                hist_rows = int(L.sum())
-            row_b = vc.Hkv * vc.D * 2
-            vbytes = (2 * hist_rows * row_b                      # K and V history
-                      + 2 * vc.B * vc.T * row_b                  # new K and V rows
-                      + 2 * vc.B * vc.T * vc.Hq * vc.D * 2)      # Q in, O out
-
-            def verify():
-                swa.swa_attn_verify(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"],
-                                    inp["v_cache"], cl, inp["sinks"], vc.window, vc.ring, vc.scale,
-                                    workspace=ws, out=ov)
-
-            for _ in range(args.warmup):
-                verify()
-            # small working sets would sit in the 256 MB Infinity Cache: flush it first
-            before = (lambda: flush.zero_()) if vbytes < (1 << 30) else None
-            ms = time_launches(verify, max(args.steps, 5), stream, before)
-            vres[name] = {
-                "workload": name, "batch": vc.B, "q_len": vc.T, "cache": "ring" if vc.ring else "linear",
-                "slots": vc.slots, "window": vc.window, "context_lengths": [vc.len_lo, vc.len_hi],
-                "algorithmic_bytes": vbytes, "ms": round(ms, 5),
-                "GB/s": round(vbytes / (ms * 1e-3) / 1e9, 1),
-                "frac_of_hbm_peak": round(vbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            }
-            del inp, ws, ov
-            torch.cuda.empty_cache()
-        ga = vres["verify_ga_b64"]
-        result["verify"] = {
-            "metric": "q_len=4 verify-decode HBM GB/s",
-            "value": ga["GB/s"], "unit": "GB/s", "workloads": vres,
-            "roofline": {
-                "kernel": "verify_bf16_kernel + verify_combine_kernel", "bound": "hbm",
-                "achieved": ga["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": ga["frac_of_hbm_peak"],
-                "traffic": read_traffic("verify_bf16_ga_b64_hbm_counters.txt", VERIFY_KERNEL_SRC),
-            },
-        }
-
-    # ------------------------------------------------------------ CPU oracle baseline
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, q, k, v, sinks, args.cpu_seconds)
-
+    if args.only is None and not args.no_verify:
+        result["ga_prefill"] = run_ga(args, swa, torch, dev, stream)
+        result["verify"] = run_verify(args, swa, torch, dev, stream)
+    if args.only is None and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, *tensors, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -23,7 +23,7 @@ const char* swa_status_string(swa_status_t status) {
     case SWA_OK: return "ok";
     case SWA_ERR_NULL: return "a required pointer is NULL";
     case SWA_ERR_SHAPE: return "sizes violate a shape rule";
-    case SWA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or head grouping";
+    case SWA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or head grouping, or sm_scale not finite > 0";
     case SWA_ERR_WORKSPACE: return "workspace missing or too small";
     case SWA_ERR_LAUNCH: return "kernel launch failed";
   }
@@ -33,7 +33,8 @@ const char* swa_status_string(swa_status_t status) {
 swa_status_t swa_attn_prefill(const void* q, const void* k, const void* v, const float* sinks,
                               void* o, int B, int Sq, int Sk, int Hq, int Hkv, int D, int window,
                               int q_offset, float sm_scale, swa_dtype_t dtype, void* stream) {
-  swa_status_t st = swa_validate_prefill(q, k, v, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset, dtype);
+  swa_status_t st = swa_validate_prefill(q, k, v, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset,
+                                         sm_scale, dtype);
   if (st != SWA_OK || B == 0 || Sq == 0) return st;
   PrefillArgs a = {};
   a.q = (const uint16_t*)q;
@@ -71,6 +72,7 @@ swa_status_t swa_attn_verify(const void* q, const void* k_new, const void* v_new
                              void* stream) {
   swa_status_t st =
       swa_validate_verify_shape(B, q_len, Hq, Hkv, D, cache_slots, ring, window, dtype);
+  if (st == SWA_OK) st = swa_validate_scale(sm_scale);
   if (st != SWA_OK || B == 0) return st;
   st = swa_validate_verify_ptrs(q, k_new, v_new, k_cache, v_cache, cache_len, o);
   if (st != SWA_OK) return st;

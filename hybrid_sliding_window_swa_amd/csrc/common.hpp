@@ -43,9 +43,52 @@ __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32,
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
+// Index of this wave in its workgroup, as a wave-uniform (scalar) value so
+// that everything derived from it stays in SGPRs and branches stay uniform.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi) {
   return (uint32_t)lo | ((uint32_t)hi << 16);
 }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// A tile of 32 rows x D bf16 in LDS, row-major, with the 16-byte chunks of
+// row r XOR-swizzled by (r mod D/8) so that the MFMA operand reads below hit
+// distinct banks.  Filled with one ds_write_b128 per 16-byte chunk.
+template <int D>
+struct SwzTile {
+  static constexpr int CPR = D / 8;      // 16-byte chunks per row
+  static constexpr int ELEMS = 32 * D;   // bf16 elements per tile
+  // element offset of logical (row, d); d % 4 == 0
+  static __device__ __forceinline__ int off(int row, int d) {
+    return row * D + (((d >> 3) ^ (row & (CPR - 1))) << 3) + (d & 7);
+  }
+  // A operand of S^T = K Q^T for contraction chunk c: row `col`, d in
+  // [16c + 8*half, +8)
+  static __device__ __forceinline__ bf16x8 k_operand(const uint16_t* t, int col, int half, int c) {
+    return *(const bf16x8*)(t + off(col, 16 * c + 8 * half));
+  }
+  // A operand of O^T += V^T P^T for output rows d in [32db, 32db + 32) and
+  // keys [16kc, 16kc + 16): lane l receives V[n][32db + l%32] for
+  // n = 16kc + 4(l/32) + {0..3} and then n + 8 + {0..3}.  gfx950's
+  // ds_read_b64_tr_b16 gives lane j of each 16-lane group element j%4 of the
+  // 8-byte chunks addressed by lanes 4e + j/4 (e = 0..3), so source lane s
+  // addresses row n0 + s/4, columns d0 + 4(s%4).
+  static __device__ __forceinline__ bf16x8 vt_operand(const uint16_t* t, int lane, int db, int kc) {
+    const int s = lane & 15;
+    const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const int r0 = 16 * kc + 4 * (lane >> 5) + (s >> 2);
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + off(r0, d)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + off(r0 + 8, d)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, both);
+  }
+};
 
 // Wave-local LDS ordering: make this wave's LDS writes visible to its other
 // lanes before the reads that follow (and keep reads before later writes).

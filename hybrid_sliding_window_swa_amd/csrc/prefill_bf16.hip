@@ -8,11 +8,11 @@
 // when W <= 0), softmax over the scaled scores with exp(sink_h) added to the
 // denominator, times the values.
 //
-// Work decomposition
-//   * A workgroup owns TB consecutive tokens of one request and ALL G query
-//     heads of one KV head g, so every K/V tile it stages in LDS serves G
-//     heads (the GQA group) and TB tokens.  Each wave owns 32*NB query rows:
-//     row m of a 32-row block is (token m / G, head m % G).
+// Shared structure of both kernels in this file
+//   * A workgroup owns consecutive tokens of one request and ALL G query heads
+//     of one KV head g, so every K/V tile it stages in LDS serves the whole
+//     GQA group.  Each wave owns 32*NB query rows: row m of a 32-row block is
+//     (token m / G, head m % G).
 //   * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16
 //     MFMA: lane l then holds 16 scores of ONE query (column l%32) and the
 //     other 16 live in lane l^32, so the softmax row max needs one half swap
@@ -21,41 +21,230 @@
 //     through LDS.
 //   * V^T is the A operand of that product; the staging step writes each V
 //     tile into LDS transposed ([d][key]) once per workgroup.
-//   * Key tiles are 32 keys.  Only tiles that intersect the workgroup's
-//     window are loaded; each wave skips tiles outside its own window and
+//   * Key tiles are 32 keys.  Each wave skips tiles outside its own window and
 //     applies the causal / window mask only on boundary tiles.
 //   * Online softmax in the log2 domain, fp32, started from the sink
 //     (m = sink*log2e, l = 1), with a lazy rescale: the running max is only
 //     raised when a score exceeds it by more than kRescaleTau.
-//   * Workgroup -> work mapping is XCD-aware: workgroups dispatched to the
-//     same XCD (blockIdx % 8) take consecutive token blocks of one (b, g), so
-//     the K/V rows that neighbouring blocks share stay in that XCD's L2, and
-//     the latest (longest, for global attention) blocks go first.
+//
+// prefill_swa_strip_kernel (sliding window, G in {4, 8}): persistent over a
+//   strip of consecutive 32-token blocks of one (request, KV head).  The K/V
+//   window lives in an LDS ring of 32-key tiles; each block adds one tile.
+//   While a block is computed, the next block's queries and its new K/V tile
+//   are already in flight, and the block's output is stored asynchronously,
+//   so HBM streams continuously.
+// prefill_bf16_kernel (global attention and any other shape): one workgroup
+//   per token block, double-buffered K/V tiles, XCD-aware block order with
+//   the longest (latest) blocks first.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace swa {
 
+namespace {
+
+constexpr int KT = 32;  // keys per tile
+
+template <int D>
+struct TileGeom {
+  static constexpr int NC = D / 16;             // 16-wide chunks of the QK^T contraction
+  static constexpr int ND = D / 32;             // 32-wide blocks of d in the output
+  static constexpr int K_ELEMS = SwzTile<D>::ELEMS;  // one K tile in LDS
+  static constexpr int V_ELEMS = SwzTile<D>::ELEMS;  // one V tile in LDS (row-major)
+  static constexpr int KCH = KT * D / 8;        // 16-byte chunks of a K (or V) tile
+};
+
+// Global -> register half of staging one 32-key tile of K and of V; rows at
+// or past Sk are clamped to row Sk - 1 (finite data, always masked out).
+template <int D, int NT>
+struct Stager {
+  using Gm = TileGeom<D>;
+  static constexpr int IT = (Gm::KCH + NT - 1) / NT;
+  u32x4 kpre[IT];
+  u32x4 vpre[IT];
+
+  __device__ __forceinline__ void load(const uint16_t* kg, const uint16_t* vg, long kv_tok, int kb,
+                                       int Sk, int tid) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int c = tid + i * NT;
+      if (c < Gm::KCH) {
+        const int row = c / (D / 8), c8 = c % (D / 8);
+        const long off = (long)min(kb + row, Sk - 1) * kv_tok + c8 * 8;
+        kpre[i] = *(const u32x4*)(kg + off);
+        vpre[i] = *(const u32x4*)(vg + off);
+      }
+    }
+  }
+
+  // Register -> LDS half: both tiles row-major, 16-byte chunks swizzled.
+  __device__ __forceinline__ void store(uint16_t* k_dst, uint16_t* v_dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int c = tid + i * NT;
+      if (c < Gm::KCH) {
+        const int row = c / (D / 8), c8 = c % (D / 8);
+        const int o = SwzTile<D>::off(row, c8 * 8);
+        *(u32x4*)&k_dst[o] = kpre[i];
+        *(u32x4*)&v_dst[o] = vpre[i];
+      }
+    }
+  }
+};
+
+// Per-lane state of NB 32-query blocks.
+template <int D, int NB>
+struct QState {
+  using Gm = TileGeom<D>;
+  bf16x8 q[NB][Gm::NC];
+  int qpos[NB];
+  float m_run[NB], l_run[NB];
+  f32x16 acc[NB][Gm::ND];
+
+  // token of block nb for this lane, with G heads per token
+  __device__ __forceinline__ void load_q(const uint16_t* qbase, long q_tok, int tw0, int G, int g,
+                                         int Sq, int q_offset, int col, int half) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int tok = tw0 + nb * (32 / G) + col / G;
+      const int h = g * G + col % G;
+      qpos[nb] = q_offset + tok;
+      if (tok < Sq) {
+        const uint16_t* qp = qbase + (long)tok * q_tok + (long)h * D + half * 8;
+#pragma unroll
+        for (int c = 0; c < Gm::NC; ++c) q[nb][c] = *(const bf16x8*)(qp + c * 16);
+      } else {
+#pragma unroll
+        for (int c = 0; c < Gm::NC; ++c) q[nb][c] = bf16x8{};
+      }
+    }
+  }
+
+  // Start every row from its head's sink: m = sink*log2e, l = 1 (counted once,
+  // in the lower half of the wave).  sink2 = sink * log2(e), or -inf for none.
+  // Every lane's rows share one head set (col % G), so one value serves all
+  // blocks.
+  __device__ __forceinline__ void reset(float sink2, int half) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      m_run[nb] = sink2;
+      l_run[nb] = (sink2 != kNegInf && half == 0) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db) acc[nb][db] = f32x16{};
+    }
+  }
+
+  // Fold one 32-key tile (K and V rows in LDS, first key position kb).
+  __device__ __forceinline__ void attend(const uint16_t* k_t, const uint16_t* v_t, int kb,
+                                         bool need_mask, int window, float c2, int lane) {
+    const int col = lane & 31, half = lane >> 5;
+    f32x16 s[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < Gm::NC; ++c) {
+      const bf16x8 a = SwzTile<D>::k_operand(k_t, col, half, c);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[nb] = mfma32(a, q[nb][c], s[nb]);
+    }
+    if (need_mask) {
+      // causal / window mask of a boundary tile: masked scores -> -inf
+      const int klo = window > 0 ? 1 - window : -(1 << 30);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rel = kb + c_row(v, half) - qpos[nb];  // key position - query position
+          s[nb][v] = (rel <= 0 && rel >= klo) ? s[nb][v] : kNegInf;
+        }
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      // raw-score max (scale > 0 commutes with max)
+      float mx = kNegInf;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[nb][v]);
+      mx = fmaxf(mx, swap_halves(mx)) * c2;
+      const float m_new = fmaxf(m_run[nb], mx);
+      const bool need = m_new > m_run[nb] + kRescaleTau;
+      if (wave_any(need)) {
+        const float alpha = need ? exp2_fast(m_run[nb] - m_new) : 1.0f;
+        m_run[nb] = need ? m_new : m_run[nb];
+        l_run[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < Gm::ND; ++db) acc[nb][db] *= alpha;
+      }
+      const float mu = m_run[nb] == kNegInf ? 0.0f : m_run[nb];
+      bf16x8 pb[2];
+      float ls = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float e = exp2_fast(fmaf(s[nb][v], c2, -mu));
+        ls += e;
+        pb[v >> 3][v & 7] = (__bf16)e;
+      }
+      l_run[nb] += ls;
+      // O^T += V^T P^T: keys 16kc .. 16kc+15 per MFMA
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+        for (int db = 0; db < Gm::ND; ++db)
+          acc[nb][db] = mfma32(SwzTile<D>::vt_operand(v_t, lane, db, kc), pb[kc], acc[nb][db]);
+      }
+    }
+  }
+
+  // O = acc / l in bf16, one 8-byte store per 4 consecutive d.
+  __device__ __forceinline__ void store_o(uint16_t* obase, long q_tok, int tw0, int G, int g, int Sq,
+                                          int col, int half) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int tok = tw0 + nb * (32 / G) + col / G;
+      const int h = g * G + col % G;
+      const float lt = l_run[nb] + swap_halves(l_run[nb]);
+      if (tok >= Sq) continue;
+      const float inv = 1.0f / lt;
+      uint16_t* op = obase + (long)tok * q_tok + (long)h * D;
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 y = {acc[nb][db][4 * a4] * inv, acc[nb][db][4 * a4 + 1] * inv,
+                           acc[nb][db][4 * a4 + 2] * inv, acc[nb][db][4 * a4 + 3] * inv};
+          *(bf16x4*)(op + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(y, bf16x4);
+        }
+      }
+    }
+  }
+};
+
+// Does the wave whose queries sit at positions [wpos_lo, wpos_hi] need tile
+// [kb, kb + 31], and does it need the mask there?
+__device__ __forceinline__ bool tile_needed(int kb, int wpos_lo, int wpos_hi, int window,
+                                            bool& need_mask) {
+  const int wkey_lo = window > 0 ? max(0, wpos_lo - window + 1) : 0;
+  need_mask = (kb + KT - 1 > wpos_lo) || (window > 0 && kb < wpos_hi - window + 1);
+  return kb + KT - 1 >= wkey_lo && kb <= wpos_hi;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------
+// One workgroup per block of TB tokens (global attention and general shapes).
 template <int D, int G, int NB, int NW>
 __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
+  using Gm = TileGeom<D>;
   constexpr int NT = NW * 64;
   constexpr int TW = 32 * NB / G;   // tokens per wave
   constexpr int TB = TW * NW;       // tokens per workgroup
-  constexpr int NC = D / 16;        // 16-wide chunks of the QK^T contraction
-  constexpr int ND = D / 32;        // 32-wide blocks of d in the output
-  constexpr int KT = 32;            // keys per tile
-  constexpr int KROW = D + 8;       // LDS pitch of a K row (bf16 elements)
-  constexpr int VROW = KT + 4;      // LDS pitch of a V^T row (bf16 elements)
-  constexpr int KCH = KT * D / 8;   // 16-byte chunks of a K tile
-  constexpr int VU = (KT / 2) * (D / 8);  // (key pair, 8 d) units of a V tile
-  constexpr int K_IT = (KCH + NT - 1) / NT;
-  constexpr int V_IT = (VU + NT - 1) / NT;
   static_assert(32 * NB % G == 0, "a 32-row block must hold whole tokens");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][Gm::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][Gm::V_ELEMS];
 
-  // ---- work item
+  // XCD-aware work item: workgroups on one XCD (blockIdx % 8) take consecutive
+  // token blocks of one (b, g), latest (longest) first.
   const int bid = blockIdx.x;
   const int w = (bid & 7) * p.per_xcd + (bid >> 3);
   if (w >= p.total) return;
@@ -64,48 +253,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   const int g = bg % p.Hkv;
   const int b = bg / p.Hkv;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int half = lane >> 5;
-  const int col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_index();
+  const int half = lane >> 5, col = lane & 31;
   const int t0 = tb * TB;
   const int tw0 = t0 + wv * TW;
   const long q_tok = (long)p.Hq * D;
   const long kv_tok = (long)p.Hkv * D;
-  const uint16_t* __restrict__ kg = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
-  const uint16_t* __restrict__ vg = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
+  const uint16_t* kg = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
+  const uint16_t* vg = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
+  const long qoff = (long)b * p.Sq * q_tok;
 
-  // ---- this lane's queries (one per 32-row block)
-  bf16x8 qreg[NB][NC];
-  int qpos[NB];
-  float m_run[NB], l_run[NB];
-  f32x16 acc[NB][ND];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int tok = tw0 + nb * (32 / G) + col / G;
-    const int h = g * G + col % G;
-    qpos[nb] = p.q_offset + tok;
-    if (tok < p.Sq) {
-      const uint16_t* qp = p.q + ((long)b * p.Sq + tok) * q_tok + (long)h * D + half * 8;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) qreg[nb][c] = *(const bf16x8*)(qp + c * 16);
-    } else {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) qreg[nb][c] = bf16x8{};
-    }
-    if (p.sinks) {
-      m_run[nb] = p.sinks[h] * kLog2e;   // start from the sink: exp2(sink - m) = 1
-      l_run[nb] = half == 0 ? 1.0f : 0.0f;
-    } else {
-      m_run[nb] = kNegInf;
-      l_run[nb] = 0.0f;
-    }
-#pragma unroll
-    for (int db = 0; db < ND; ++db) acc[nb][db] = f32x16{};
-  }
+  QState<D, NB> st;
+  st.load_q(p.q + qoff, q_tok, tw0, G, g, p.Sq, p.q_offset, col, half);
+  st.reset(p.sinks ? p.sinks[g * G + col % G] * kLog2e : kNegInf, half);
 
-  // ---- key range of the workgroup and of this wave
   const int tlast = min(t0 + TB, p.Sq) - 1;
   const int pos_lo = p.q_offset + t0, pos_hi = p.q_offset + tlast;
   const int key_lo = p.window > 0 ? max(0, pos_lo - p.window + 1) : 0;
@@ -113,161 +274,136 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   const bool wave_active = tw0 < p.Sq;
   const int wpos_lo = p.q_offset + tw0;
   const int wpos_hi = p.q_offset + min(tw0 + TW, p.Sq) - 1;
-  const int wkey_lo = p.window > 0 ? max(0, wpos_lo - p.window + 1) : 0;
 
-  // ---- tile staging: global -> registers -> LDS (V transposed)
-  u32x4 kpre[K_IT];
-  u32x4 vpre[V_IT][2];
-  auto load_tile = [&](int kt) {
-    const int kb = kt * KT;
-#pragma unroll
-    for (int i = 0; i < K_IT; ++i) {
-      const int c = tid + i * NT;
-      kpre[i] = u32x4{};
-      if (c < KCH) {
-        const int row = c / (D / 8), c8 = c % (D / 8);
-        const int key = kb + row;
-        if (key < p.Sk) kpre[i] = *(const u32x4*)(kg + (long)key * kv_tok + c8 * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_IT; ++i) {
-      const int u = tid + i * NT;
-      vpre[i][0] = u32x4{};
-      vpre[i][1] = u32x4{};
-      if (u < VU) {
-        const int pr = u % (KT / 2), c8 = u / (KT / 2);
-        const int key = kb + 2 * pr;
-        if (key < p.Sk) vpre[i][0] = *(const u32x4*)(vg + (long)key * kv_tok + c8 * 8);
-        if (key + 1 < p.Sk) vpre[i][1] = *(const u32x4*)(vg + (long)(key + 1) * kv_tok + c8 * 8);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < K_IT; ++i) {
-      const int c = tid + i * NT;
-      if (c < KCH) {
-        const int row = c / (D / 8), c8 = c % (D / 8);
-        *(u32x4*)&k_lds[buf][row * KROW + c8 * 8] = kpre[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_IT; ++i) {
-      const int u = tid + i * NT;
-      if (u < VU) {
-        const int pr = u % (KT / 2), c8 = u / (KT / 2);
-        uint32_t* dst = (uint32_t*)&vt_lds[buf][(c8 * 8) * VROW + 2 * pr];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t w0 = vpre[i][0][e >> 1], w1 = vpre[i][1][e >> 1];
-          const uint32_t lo = (e & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-          const uint32_t hi = (e & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
-          dst[e * (VROW / 2)] = lo | hi;
-        }
-      }
-    }
-  };
-
-  load_tile(kt_begin);
-  store_tile(0);
+  Stager<D, NT> sg;
+  sg.load(kg, vg, kv_tok, kt_begin * KT, p.Sk, tid);
+  sg.store(k_lds[0], v_lds[0], tid);
+  // Drain the prologue loads (queries, first tile): inside the loop the only
+  // loads in flight are then the next tile's, and no wait for the queries
+  // can stall on them.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
     const int buf = (kt - kt_begin) & 1;
     const bool more = kt < kt_end;
-    if (more) load_tile(kt + 1);
-    const int kb = kt * KT;
-    if (wave_active && kb + KT - 1 >= wkey_lo && kb <= wpos_hi) {
-      const bool need_mask = (kb + KT - 1 > wpos_lo) ||
-                             (p.window > 0 && kb < wpos_hi - p.window + 1);
-      // S^T = K Q^T for each 32-query block
-      f32x16 s[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 a = *(const bf16x8*)&k_lds[buf][col * KROW + c * 16 + half * 8];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[nb] = mfma32(a, qreg[nb][c], s[nb]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = s[nb][v] * p.scale_log2;
-          if (need_mask) {
-            const int kpos = kb + c_row(v, half);
-            const bool ok = kpos <= qpos[nb] && (p.window <= 0 || kpos > qpos[nb] - p.window);
-            x = ok ? x : kNegInf;
-          }
-          s[nb][v] = x;
-          mx = fmaxf(mx, x);
-        }
-        mx = fmaxf(mx, swap_halves(mx));
-        const float m_new = fmaxf(m_run[nb], mx);
-        const bool need = m_new > m_run[nb] + kRescaleTau;
-        if (wave_any(need)) {
-          const float alpha = need ? exp2_fast(m_run[nb] - m_new) : 1.0f;
-          m_run[nb] = need ? m_new : m_run[nb];
-          l_run[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < ND; ++db) acc[nb][db] *= alpha;
-        }
-        const float mu = m_run[nb] == kNegInf ? 0.0f : m_run[nb];
-        bf16x8 pb[2];
-        float ls = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float e = exp2_fast(s[nb][v] - mu);
-          ls += e;
-          pb[v >> 3][v & 7] = (__bf16)e;
-        }
-        l_run[nb] += ls;
-        // O^T += V^T P^T: keys 16kc .. 16kc+15 per MFMA
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-          for (int db = 0; db < ND; ++db) {
-            const uint16_t* vp = &vt_lds[buf][(db * 32 + col) * VROW + 16 * kc + 4 * half];
-            const u32x2 lo = *(const u32x2*)vp;
-            const u32x2 hi = *(const u32x2*)(vp + 8);
-            const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-            acc[nb][db] = mfma32(__builtin_bit_cast(bf16x8, av), pb[kc], acc[nb][db]);
-          }
-        }
-      }
-    }
-    if (more) store_tile(buf ^ 1);
+    if (more) sg.load(kg, vg, kv_tok, (kt + 1) * KT, p.Sk, tid);
+    bool need_mask;
+    if (wave_active && tile_needed(kt * KT, wpos_lo, wpos_hi, p.window, need_mask))
+      st.attend(k_lds[buf], v_lds[buf], kt * KT, need_mask, p.window, p.scale_log2, lane);
+    if (more) sg.store(k_lds[buf ^ 1], v_lds[buf ^ 1], tid);
     __syncthreads();
   }
+  if (wave_active) st.store_o(p.o + qoff, q_tok, tw0, G, g, p.Sq, col, half);
+}
 
-  // ---- epilogue: O = acc / l, bf16, one 8-byte store per 4 consecutive d
-  if (!wave_active) return;
+// ----------------------------------------------------------------------------
+// Sliding window: persistent over a strip of 32-token blocks with an LDS ring.
+// G waves per workgroup, each wave 32/G tokens x G heads (one 32-row block).
+constexpr int kRingTiles = 8;
+
+template <int D, int G>
+__global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p) {
+  using Gm = TileGeom<D>;
+  constexpr int NW = G;
+  constexpr int NT = NW * 64;
+  constexpr int TW = 32 / G;   // tokens per wave
+  constexpr int TB = 32;       // tokens per block (= one key tile)
+  constexpr int NR = kRingTiles;
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_ring[NR][Gm::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_ring[NR][Gm::V_ELEMS];
+
+  // strip -> (b, g, block range)
+  const int strip = blockIdx.x;
+  const int bg = strip / p.per_xcd;          // per_xcd holds strips per (b, g) here
+  const int sidx = strip - bg * p.per_xcd;
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+  const int blk0 = (int)((long)sidx * p.n_tb / p.per_xcd);
+  const int blk1 = (int)((long)(sidx + 1) * p.n_tb / p.per_xcd);
+  if (blk0 >= blk1) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_index();
+  const int half = lane >> 5, col = lane & 31;
+  const long q_tok = (long)p.Hq * D;
+  const long kv_tok = (long)p.Hkv * D;
+  const uint16_t* kg = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
+  const uint16_t* vg = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
+  const long qoff = (long)b * p.Sq * q_tok;
+  const int W = p.window;
+
+  auto kt_lo = [&](int blk) { return max(0, p.q_offset + blk * TB - W + 1) / KT; };
+  auto kt_hi = [&](int blk) { return (p.q_offset + min(blk * TB + TB, p.Sq) - 1) / KT; };
+
+  QState<D, 1> st;
+  bf16x8 qnext[Gm::NC];
+  Stager<D, NT> sg;
+  const float sink2 = p.sinks ? p.sinks[g * G + col % G] * kLog2e : kNegInf;
+
+  // prologue: the first block's queries and its whole window
+  st.load_q(p.q + qoff, q_tok, blk0 * TB + wv * TW, G, g, p.Sq, p.q_offset, col, half);
+  int loaded_hi = kt_hi(blk0);
+  for (int kt = kt_lo(blk0); kt <= loaded_hi; ++kt) {
+    sg.load(kg, vg, kv_tok, kt * KT, p.Sk, tid);
+    sg.store(k_ring[kt % NR], v_ring[kt % NR], tid);
+  }
+  // Drain every prologue load here, so that inside the loop the only loads in
+  // flight are the prefetches and no wait inserted for the current queries
+  // can stall on them.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const int tw0 = blk * TB + wv * TW;
+    const bool nxt = blk + 1 < blk1;
+    // prefetch: next block's queries and (at most one) new K/V tile
+    const int new_kt = nxt ? kt_hi(blk + 1) : -1;
+    const bool have_new = new_kt > loaded_hi;
+    if (nxt) {
+      const int ntok = tw0 + TB + col / G;
+      const int h = g * G + col % G;
+      if (ntok < p.Sq) {
+        const uint16_t* qp = p.q + qoff + (long)ntok * q_tok + (long)h * D + half * 8;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int tok = tw0 + nb * (32 / G) + col / G;
-    const int h = g * G + col % G;
-    const float lt = l_run[nb] + swap_halves(l_run[nb]);
-    if (tok >= p.Sq) continue;
-    const float inv = 1.0f / lt;
-    uint16_t* op = p.o + ((long)b * p.Sq + tok) * q_tok + (long)h * D;
+        for (int c = 0; c < Gm::NC; ++c) qnext[c] = *(const bf16x8*)(qp + c * 16);
+      } else {
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const f32x4 y = {acc[nb][db][4 * a4] * inv, acc[nb][db][4 * a4 + 1] * inv,
-                         acc[nb][db][4 * a4 + 2] * inv, acc[nb][db][4 * a4 + 3] * inv};
-        const bf16x4 yb = __builtin_convertvector(y, bf16x4);
-        *(bf16x4*)(op + db * 32 + 8 * a4 + 4 * half) = yb;
+        for (int c = 0; c < Gm::NC; ++c) qnext[c] = bf16x8{};
       }
+    }
+    if (have_new) sg.load(kg, vg, kv_tok, new_kt * KT, p.Sk, tid);
+
+    // compute this block from the ring
+    st.reset(sink2, half);
+    const bool wave_active = tw0 < p.Sq;
+    if (wave_active) {
+      const int wpos_lo = p.q_offset + tw0;
+      const int wpos_hi = p.q_offset + min(tw0 + TW, p.Sq) - 1;
+      const int k1 = kt_hi(blk);
+      for (int kt = kt_lo(blk); kt <= k1; ++kt) {
+        bool need_mask;
+        if (tile_needed(kt * KT, wpos_lo, wpos_hi, W, need_mask))
+          st.attend(k_ring[kt % NR], v_ring[kt % NR], kt * KT, need_mask, W, p.scale_log2, lane);
+      }
+      st.store_o(p.o + qoff, q_tok, tw0, G, g, p.Sq, col, half);
+    }
+    // the new tile's slot held tile new_kt - NR, older than this block's window
+    if (have_new) {
+      sg.store(k_ring[new_kt % NR], v_ring[new_kt % NR], tid);
+      loaded_hi = new_kt;
+    }
+    __syncthreads();
+    if (nxt) {
+#pragma unroll
+      for (int c = 0; c < Gm::NC; ++c) st.q[0][c] = qnext[c];
+      st.qpos[0] += TB;
     }
   }
 }
 
+// ----------------------------------------------------------------------------
 template <int D, int G, int NB, int NW>
-static hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream) {
+static hipError_t launch_generic(const PrefillArgs& a0, hipStream_t stream) {
   PrefillArgs a = a0;
   constexpr int TB = (32 * NB / G) * NW;
   a.n_tb = (a.Sq + TB - 1) / TB;
@@ -278,22 +414,46 @@ static hipError_t launch_prefill_t(const PrefillArgs& a0, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, int G>
+static hipError_t launch_strip(const PrefillArgs& a0, int num_cu, hipStream_t stream) {
+  PrefillArgs a = a0;
+  a.n_tb = (a.Sq + 31) / 32;
+  const int bgs = a.B * a.Hkv;
+  int spb = num_cu / bgs;                 // strips per (b, g): about one workgroup per CU
+  if (spb < 1) spb = 1;
+  if (spb > a.n_tb) spb = a.n_tb;
+  a.per_xcd = spb;
+  a.total = bgs * spb;
+  hipLaunchKernelGGL((prefill_swa_strip_kernel<D, G>), dim3(a.total), dim3(G * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D>
-static hipError_t launch_prefill_d(const PrefillArgs& a, int G, hipStream_t s) {
+static hipError_t launch_d(const PrefillArgs& a, int G, hipStream_t s) {
+  // the strip kernel's ring must hold a block's window plus the next tile
+  const bool ring_fits = a.window > 0 && (31 + a.window + KT - 1) / KT + 1 + 1 <= kRingTiles;
+  if (ring_fits && (G == 8 || G == 4)) {
+    int dev = 0, num_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        num_cu <= 0)
+      num_cu = 256;
+    return G == 8 ? launch_strip<D, 8>(a, num_cu, s) : launch_strip<D, 4>(a, num_cu, s);
+  }
   switch (G) {
-    case 1: return launch_prefill_t<D, 1, 1, 8>(a, s);
-    case 2: return launch_prefill_t<D, 2, 1, 8>(a, s);
-    case 4: return launch_prefill_t<D, 4, 1, 8>(a, s);
-    case 8: return launch_prefill_t<D, 8, 1, 8>(a, s);
-    case 16: return launch_prefill_t<D, 16, 1, 8>(a, s);
-    case 32: return launch_prefill_t<D, 32, 1, 8>(a, s);
+    case 1: return launch_generic<D, 1, 1, 8>(a, s);
+    case 2: return launch_generic<D, 2, 1, 8>(a, s);
+    case 4: return launch_generic<D, 4, 1, 8>(a, s);
+    case 8: return launch_generic<D, 8, 1, 8>(a, s);
+    case 16: return launch_generic<D, 16, 1, 8>(a, s);
+    case 32: return launch_generic<D, 32, 1, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  return a.D == 128 ? launch_prefill_d<128>(a, G, s) : launch_prefill_d<64>(a, G, s);
+  return a.D == 128 ? launch_d<128>(a, G, s) : launch_d<64>(a, G, s);
 }
 
 }  // namespace swa

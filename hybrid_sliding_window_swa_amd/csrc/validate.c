@@ -4,12 +4,22 @@
 static int dtype_ok(swa_dtype_t dt) { return dt == SWA_F32 || dt == SWA_BF16; }
 static int head_dim_ok(int D) { return D == 64 || D == 128; }
 
+swa_status_t swa_validate_scale(float sm_scale)
+{
+    /* finite and > 0 (NaN fails the comparison) */
+    if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f)
+        return SWA_ERR_UNSUPPORTED;
+    return SWA_OK;
+}
+
 swa_status_t swa_validate_prefill(const void *q, const void *k, const void *v, const void *o,
                                   int B, int Sq, int Sk, int Hq, int Hkv, int D,
-                                  int window, int q_offset, swa_dtype_t dtype)
+                                  int window, int q_offset, float sm_scale, swa_dtype_t dtype)
 {
     (void)window;
     if (!dtype_ok(dtype))
+        return SWA_ERR_UNSUPPORTED;
+    if (swa_validate_scale(sm_scale) != SWA_OK)
         return SWA_ERR_UNSUPPORTED;
     if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
         return SWA_ERR_SHAPE;

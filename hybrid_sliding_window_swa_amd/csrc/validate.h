@@ -11,10 +11,13 @@ extern "C" {
 
 swa_status_t swa_validate_prefill(const void *q, const void *k, const void *v, const void *o,
                                   int B, int Sq, int Sk, int Hq, int Hkv, int D,
-                                  int window, int q_offset, swa_dtype_t dtype);
+                                  int window, int q_offset, float sm_scale, swa_dtype_t dtype);
 
 swa_status_t swa_validate_verify_shape(int B, int q_len, int Hq, int Hkv, int D,
                                        int cache_slots, int ring, int window, swa_dtype_t dtype);
+
+/* sm_scale must be finite and positive. */
+swa_status_t swa_validate_scale(float sm_scale);
 
 swa_status_t swa_validate_verify_ptrs(const void *q, const void *k_new, const void *v_new,
                                       const void *k_cache, const void *v_cache,

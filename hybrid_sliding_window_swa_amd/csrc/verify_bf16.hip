@@ -85,7 +85,7 @@ __global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
 
   const int G = p.Hq / p.Hkv;
   const int R = G * p.T;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_index();
   const int half = lane >> 5, col = lane & 31;
   const long kv_tok = (long)p.Hkv * D;
   // ring: slot of the oldest committed position held, to map slot -> position
@@ -122,38 +122,27 @@ __global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
   const uint16_t* knew = p.k_new + ((long)b * p.T * p.Hkv + g) * D;
   const uint16_t* vnew = p.v_new + ((long)b * p.T * p.Hkv + g) * D;
 
-  // row `r` (0..31) of tile j: pointer offset (in elements, from kcache/knew)
-  // and validity
-  auto row_src = [&](int j, int r, bool& is_new, bool& valid) -> long {
-    is_new = (s == 0 && j == ntc);
-    if (is_new) {
-      valid = r < p.T;
-      return (long)r * kv_tok;
-    }
-    const int ci = c0 + j * 32 + r;
-    valid = ci < c1;
-    return (long)ci * kv_tok;
+  // Source row of row r (0..31) of tile j.  Rows past the valid range are
+  // clamped to the last valid row: they are masked out of the softmax and
+  // their (finite, committed) values get weight exactly 0, so unused cache
+  // slots are never read and no zero-fill branch is needed.
+  auto row_ptr = [&](int j, int r, const uint16_t* kbase_new, const uint16_t* kbase_cache) {
+    if (s == 0 && j == ntc) return kbase_new + (long)min(r, p.T - 1) * kv_tok;
+    return kbase_cache + (long)min(c0 + j * 32 + r, c1 - 1) * kv_tok;
   };
 
   bf16x8 kreg[NC], knext[NC];
   u32x4 vnext[V_IT][2];
   auto load_tile = [&](int j, bf16x8 (&kr)[NC], u32x4 (&vr)[V_IT][2]) {
-    bool is_new, valid;
-    const long off = row_src(j, col, is_new, valid);
-    const uint16_t* kp = (is_new ? knew : kcache) + off + half * 8;
+    const uint16_t* kp = row_ptr(j, col, knew, kcache) + half * 8;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kr[c] = valid ? *(const bf16x8*)(kp + c * 16) : bf16x8{};
+    for (int c = 0; c < NC; ++c) kr[c] = *(const bf16x8*)(kp + c * 16);
 #pragma unroll
     for (int i = 0; i < V_IT; ++i) {
       const int u = lane + 64 * i;
       const int pr = u % 16, c8 = u / 16;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        bool nw, ok;
-        const long o2 = row_src(j, 2 * pr + e, nw, ok);
-        const uint16_t* vp = (nw ? vnew : vcache) + o2 + c8 * 8;
-        vr[i][e] = ok ? *(const u32x4*)vp : u32x4{};
-      }
+      for (int e = 0; e < 2; ++e) vr[i][e] = *(const u32x4*)(row_ptr(j, 2 * pr + e, vnew, vcache) + c8 * 8);
     }
   };
   auto store_v = [&](const u32x4 (&vr)[V_IT][2]) {
@@ -176,6 +165,10 @@ __global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
     load_tile(wv, kreg, vnext);
     store_v(vnext);
   }
+  // Drain the prologue loads (queries, first tile) so that inside the loop
+  // the only loads in flight are the prefetch of the next tile and nothing
+  // waits on it before the current tile is computed.
+  __builtin_amdgcn_s_waitcnt(0);
   for (int j = wv; j < ntiles; j += NW) {
     const bool more = j + NW < ntiles;
     if (more) load_tile(j + NW, knext, vnext);

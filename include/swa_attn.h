@@ -68,7 +68,7 @@ typedef enum {
     SWA_OK = 0,
     SWA_ERR_NULL = 1,        /* a required pointer is NULL */
     SWA_ERR_SHAPE = 2,       /* sizes violate a shape rule */
-    SWA_ERR_UNSUPPORTED = 3, /* valid but not implemented (dtype, D, grouping) */
+    SWA_ERR_UNSUPPORTED = 3, /* not implemented (dtype, D, grouping) or sm_scale not finite > 0 */
     SWA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
     SWA_ERR_LAUNCH = 5       /* the HIP runtime reported a launch error */
 } swa_status_t;
@@ -90,7 +90,8 @@ SWA_API const char *swa_status_string(swa_status_t status);
  *   q_offset  0 <= q_offset and q_offset + Sq <= Sk.  Fresh prefill uses 0; a
  *          chunk [c0, c0 + C) of a long sequence passes its queries, the full
  *          k / v and q_offset = c0 (only keys >= c0 - window + 1 are read).
- *   sm_scale  multiplier of q.k (normally 1/sqrt(D)); the sink is not scaled.
+ *   sm_scale  multiplier of q.k (normally 1/sqrt(D)), finite and > 0; the
+ *          sink is not scaled.
  * Rows of k / v inside a loaded 32-key tile but outside the window are read
  * and weighted by exactly zero, so k and v must be finite for all Sk rows.
  * B == 0 or Sq == 0 is a valid no-op.
@@ -124,7 +125,8 @@ SWA_API size_t swa_attn_verify_workspace_bytes(int B, int q_len, int Hq, int Hkv
  *                  last min(L_b, cache_slots) committed positions.
  *       ring == 0: linear cache, position p lives in slot p.
  *   cache_len     [B] int32 DEVICE array: L_b committed tokens per request.
- *   sinks [Hq] fp32 or NULL;  o [B, q_len, Hq, D] output.
+ *   sinks [Hq] fp32 or NULL;  o [B, q_len, Hq, D] output;
+ *   sm_scale finite and > 0 (the sink is not scaled).
  *   workspace     device buffer of at least
  *                 swa_attn_verify_workspace_bytes(...) bytes (any alignment
  *                 of 256 bytes or more); its contents are scratch.

@@ -48,9 +48,10 @@ def test_status_strings(lib):
         assert lib.swa_status_string(code)
 
 
-def _prefill(lib, q=1, k=1, v=1, o=1, B=1, Sq=8, Sk=8, Hq=8, Hkv=1, D=128, W=128, off=0, dt=BF16):
+def _prefill(lib, q=1, k=1, v=1, o=1, B=1, Sq=8, Sk=8, Hq=8, Hkv=1, D=128, W=128, off=0, dt=BF16,
+             scale=0.1):
     P = lambda x: ctypes.c_void_p(x) if x else None
-    return lib.swa_attn_prefill(P(q), P(k), P(v), None, P(o), B, Sq, Sk, Hq, Hkv, D, W, off, 0.1, dt, None)
+    return lib.swa_attn_prefill(P(q), P(k), P(v), None, P(o), B, Sq, Sk, Hq, Hkv, D, W, off, scale, dt, None)
 
 
 def test_prefill_validation(lib):
@@ -66,16 +67,20 @@ def test_prefill_validation(lib):
     assert _prefill(lib, Hq=64, Hkv=1) == UNSUP     # bf16 needs 32 % G == 0
     assert _prefill(lib, Hq=12, Hkv=4) == UNSUP     # G = 3
     assert _prefill(lib, Hq=256, Hkv=1, dt=F32) == UNSUP
+    assert _prefill(lib, scale=0.0) == UNSUP
+    assert _prefill(lib, scale=-0.1) == UNSUP
+    assert _prefill(lib, scale=float("nan")) == UNSUP
+    assert _prefill(lib, scale=float("inf")) == UNSUP
     # empty work is a no-op even with NULL pointers
     assert _prefill(lib, q=0, k=0, v=0, o=0, B=0) == OK
     assert _prefill(lib, q=0, k=0, v=0, o=0, Sq=0) == OK
 
 
 def _verify(lib, ptr=1, B=2, T=4, Hq=64, Hkv=8, D=128, slots=128, ring=1, W=128, dt=BF16,
-            ws=None, ws_bytes=0):
+            ws=None, ws_bytes=0, scale=0.1):
     P = lambda x: ctypes.c_void_p(x) if x else None
     return lib.swa_attn_verify(P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), None, P(ptr),
-                               B, T, Hq, Hkv, D, slots, ring, W, 0.1, dt, P(ws), ws_bytes, None)
+                               B, T, Hq, Hkv, D, slots, ring, W, scale, dt, P(ws), ws_bytes, None)
 
 
 def test_verify_validation(lib):
@@ -89,6 +94,8 @@ def test_verify_validation(lib):
     assert _verify(lib, D=32) == UNSUP
     assert _verify(lib, T=9) == UNSUP                # bf16: G * q_len <= 64
     assert _verify(lib, dt=3) == UNSUP
+    assert _verify(lib, scale=0.0) == UNSUP
+    assert _verify(lib, scale=float("nan")) == UNSUP
     # linear global cache with many rows needs a workspace
     assert _verify(lib, ring=0, W=0, slots=65536, ws=None) == WS
     need = lib.swa_attn_verify_workspace_bytes(2, 4, 64, 8, 128, 65536, 0, 0, BF16)
