@@ -55,40 +55,81 @@ __device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi) {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// A tile of 32 rows x D bf16 in LDS, row-major, with the 16-byte chunks of
-// row r XOR-swizzled by (r mod D/8) so that the MFMA operand reads below hit
-// distinct banks.  Filled with one ds_write_b128 per 16-byte chunk.
-template <int D>
-struct SwzTile {
-  static constexpr int CPR = D / 8;      // 16-byte chunks per row
-  static constexpr int ELEMS = 32 * D;   // bf16 elements per tile
-  // element offset of logical (row, d); d % 4 == 0
-  static __device__ __forceinline__ int off(int row, int d) {
-    return row * D + (((d >> 3) ^ (row & (CPR - 1))) << 3) + (d & 7);
+// A tile of 32 rows x D bf16 in LDS, row-major with a padded row pitch of
+// PITCH elements (a multiple of 8).  Every MFMA operand address is a per-lane
+// base plus a compile-time offset, so no address arithmetic sits in the tile
+// loop.  Pitches used (32 banks of 4 bytes): K tiles D + 8 (16-byte chunk
+// position advances by 1 per row: the 8 rows of a K-operand read hit 8
+// distinct chunk positions); V tiles D + 16 (advance by 2 per row: the 4 rows
+// x 2 chunks of a transposed read hit 8 distinct positions); staging tiles of
+// D/2 columns + 8.
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 32-bit LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// tile base + per-lane offset, opaque to the optimizer (an empty asm with a
+// register operand; it touches no memory) so that every operand read of the
+// tile becomes this one register plus an immediate offset.
+__device__ __forceinline__ const lds_u16* lane_base(uint32_t tile_addr, uint32_t lane_off_bytes) {
+  uint32_t a = tile_addr + lane_off_bytes;
+  __asm__ volatile("" : "+v"(a));
+  return (const lds_u16*)(uintptr_t)a;
+}
+
+template <int D, int PITCH>
+struct PadTile {
+  static_assert(PITCH % 8 == 0, "rows must stay 16-byte aligned");
+  static constexpr int ELEMS = 32 * PITCH;   // bf16 elements per tile
+  static __device__ __forceinline__ int off(int row, int d) { return row * PITCH + d; }
+
+  // K-operand reads: lane (col, half) reads row `col`, d in [16c + 8*half, +8)
+  static __device__ __forceinline__ uint32_t k_lane_off(int lane) {
+    return 2u * ((lane & 31) * PITCH + 8 * (lane >> 5));
   }
-  // A operand of S^T = K Q^T for contraction chunk c: row `col`, d in
-  // [16c + 8*half, +8)
-  static __device__ __forceinline__ bf16x8 k_operand(const uint16_t* t, int col, int half, int c) {
-    return *(const bf16x8*)(t + off(col, 16 * c + 8 * half));
+  static __device__ __forceinline__ bf16x8 k_operand(const lds_u16* b, int c) {
+    return *(const lds_bf16x8*)(b + 16 * c);
   }
-  // A operand of O^T += V^T P^T for output rows d in [32db, 32db + 32) and
-  // keys [16kc, 16kc + 16): lane l receives V[n][32db + l%32] for
+
+  // V^T-operand reads of O^T += V^T P^T for output rows d in [32db, 32db+32)
+  // and keys [16kc, 16kc + 16): lane l receives V[n][32db + l%32] for
   // n = 16kc + 4(l/32) + {0..3} and then n + 8 + {0..3}.  gfx950's
   // ds_read_b64_tr_b16 gives lane j of each 16-lane group element j%4 of the
   // 8-byte chunks addressed by lanes 4e + j/4 (e = 0..3), so source lane s
   // addresses row n0 + s/4, columns d0 + 4(s%4).
-  static __device__ __forceinline__ bf16x8 vt_operand(const uint16_t* t, int lane, int db, int kc) {
+  static __device__ __forceinline__ uint32_t vt_lane_off(int lane) {
     const int s = lane & 15;
-    const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-    const int r0 = 16 * kc + 4 * (lane >> 5) + (s >> 2);
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + off(r0, d)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + off(r0 + 8, d)));
+    return 2u * ((4 * (lane >> 5) + (s >> 2)) * PITCH + 16 * ((lane >> 4) & 1) + 4 * (s & 3));
+  }
+  static __device__ __forceinline__ bf16x8 vt_operand(const lds_u16* b, int db, int kc) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + 16 * kc * PITCH + 32 * db));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + (16 * kc + 8) * PITCH + 32 * db));
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, both);
   }
 };
+template <int D>
+using KTile = PadTile<D, D + 8>;
+template <int D>
+using VTile = PadTile<D, D + 16>;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of the 16 bf16 weights of two bf16x8 vectors into acc (fp32), two per
+// v_dot2_f32_bf16: the row sum uses exactly the rounded weights that enter P V.
+__device__ __forceinline__ float sum_bf16x16(const bf16x8& a, const bf16x8& b, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#define SWA_DOT2(v, i) acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, i, i + 1), one, acc, false)
+  SWA_DOT2(a, 0); SWA_DOT2(a, 2); SWA_DOT2(a, 4); SWA_DOT2(a, 6);
+  SWA_DOT2(b, 0); SWA_DOT2(b, 2); SWA_DOT2(b, 4); SWA_DOT2(b, 6);
+#undef SWA_DOT2
+  return acc;
+}
 
 // Wave-local LDS ordering: make this wave's LDS writes visible to its other
 // lanes before the reads that follow (and keep reads before later writes).

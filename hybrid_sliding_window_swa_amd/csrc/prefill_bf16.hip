@@ -44,13 +44,14 @@ namespace swa {
 namespace {
 
 constexpr int KT = 32;  // keys per tile
+constexpr int kMaskHi = 1, kMaskLo = 2;
 
 template <int D>
 struct TileGeom {
   static constexpr int NC = D / 16;             // 16-wide chunks of the QK^T contraction
   static constexpr int ND = D / 32;             // 32-wide blocks of d in the output
-  static constexpr int K_ELEMS = SwzTile<D>::ELEMS;  // one K tile in LDS
-  static constexpr int V_ELEMS = SwzTile<D>::ELEMS;  // one V tile in LDS (row-major)
+  static constexpr int K_ELEMS = KTile<D>::ELEMS;  // one K tile in LDS
+  static constexpr int V_ELEMS = VTile<D>::ELEMS;  // one V tile in LDS (row-major)
   static constexpr int KCH = KT * D / 8;        // 16-byte chunks of a K (or V) tile
 };
 
@@ -77,16 +78,15 @@ struct Stager {
     }
   }
 
-  // Register -> LDS half: both tiles row-major, 16-byte chunks swizzled.
+  // Register -> LDS half: both tiles row-major with padded pitches.
   __device__ __forceinline__ void store(uint16_t* k_dst, uint16_t* v_dst, int tid) const {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int c = tid + i * NT;
       if (c < Gm::KCH) {
         const int row = c / (D / 8), c8 = c % (D / 8);
-        const int o = SwzTile<D>::off(row, c8 * 8);
-        *(u32x4*)&k_dst[o] = kpre[i];
-        *(u32x4*)&v_dst[o] = vpre[i];
+        *(u32x4*)&k_dst[KTile<D>::off(row, c8 * 8)] = kpre[i];
+        *(u32x4*)&v_dst[VTile<D>::off(row, c8 * 8)] = vpre[i];
       }
     }
   }
@@ -135,27 +135,40 @@ struct QState {
   }
 
   // Fold one 32-key tile (K and V rows in LDS, first key position kb).
+  // mask: kMaskHi if some key of the tile lies after some query of the wave,
+  // kMaskLo if some key lies below some query's window.
   __device__ __forceinline__ void attend(const uint16_t* k_t, const uint16_t* v_t, int kb,
-                                         bool need_mask, int window, float c2, int lane) {
+                                         int mask, int window, float c2, int lane) {
     const int col = lane & 31, half = lane >> 5;
     f32x16 s[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
+    const lds_u16* kbase = lane_base(lds_addr(k_t), KTile<D>::k_lane_off(lane));
 #pragma unroll
     for (int c = 0; c < Gm::NC; ++c) {
-      const bf16x8 a = SwzTile<D>::k_operand(k_t, col, half, c);
+      const bf16x8 a = KTile<D>::k_operand(kbase, c);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s[nb] = mfma32(a, q[nb][c], s[nb]);
     }
-    if (need_mask) {
-      // causal / window mask of a boundary tile: masked scores -> -inf
-      const int klo = window > 0 ? 1 - window : -(1 << 30);
+    if (mask) {
+      // Causal / window mask of a boundary tile (masked scores -> -inf).  The
+      // key of register v sits at kb + 4*half + cv with cv = 8*(v/4) + v%4, so
+      // with a = qpos - kb - 4*half it is valid iff a - W + 1 <= cv <= a: one
+      // compare per score when only one bound can bite.
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
+        const int a = qpos[nb] - kb - 4 * half;
+        const int alo = a - window + 1;
+        if (mask == kMaskHi) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int rel = kb + c_row(v, half) - qpos[nb];  // key position - query position
-          s[nb][v] = (rel <= 0 && rel >= klo) ? s[nb][v] : kNegInf;
+          for (int v = 0; v < 16; ++v) s[nb][v] = (c_row(v, 0) <= a) ? s[nb][v] : kNegInf;
+        } else if (mask == kMaskLo) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[nb][v] = (c_row(v, 0) >= alo) ? s[nb][v] : kNegInf;
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            s[nb][v] = (c_row(v, 0) <= a && c_row(v, 0) >= alo) ? s[nb][v] : kNegInf;
         }
       }
     }
@@ -177,20 +190,16 @@ struct QState {
       }
       const float mu = m_run[nb] == kNegInf ? 0.0f : m_run[nb];
       bf16x8 pb[2];
-      float ls = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = exp2_fast(fmaf(s[nb][v], c2, -mu));
-        ls += e;
-        pb[v >> 3][v & 7] = (__bf16)e;
-      }
-      l_run[nb] += ls;
+      for (int v = 0; v < 16; ++v) pb[v >> 3][v & 7] = (__bf16)exp2_fast(fmaf(s[nb][v], c2, -mu));
+      l_run[nb] = sum_bf16x16(pb[0], pb[1], l_run[nb]);
       // O^T += V^T P^T: keys 16kc .. 16kc+15 per MFMA
+      const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
         for (int db = 0; db < Gm::ND; ++db)
-          acc[nb][db] = mfma32(SwzTile<D>::vt_operand(v_t, lane, db, kc), pb[kc], acc[nb][db]);
+          acc[nb][db] = mfma32(VTile<D>::vt_operand(vbase, db, kc), pb[kc], acc[nb][db]);
       }
     }
   }
@@ -220,11 +229,12 @@ struct QState {
 };
 
 // Does the wave whose queries sit at positions [wpos_lo, wpos_hi] need tile
-// [kb, kb + 31], and does it need the mask there?
+// [kb, kb + 31], and which mask bounds can bite there?
 __device__ __forceinline__ bool tile_needed(int kb, int wpos_lo, int wpos_hi, int window,
-                                            bool& need_mask) {
+                                            int& mask) {
   const int wkey_lo = window > 0 ? max(0, wpos_lo - window + 1) : 0;
-  need_mask = (kb + KT - 1 > wpos_lo) || (window > 0 && kb < wpos_hi - window + 1);
+  mask = ((kb + KT - 1 > wpos_lo) ? kMaskHi : 0) |
+         ((window > 0 && kb < wpos_hi - window + 1) ? kMaskLo : 0);
   return kb + KT - 1 >= wkey_lo && kb <= wpos_hi;
 }
 
@@ -288,9 +298,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
     const int buf = (kt - kt_begin) & 1;
     const bool more = kt < kt_end;
     if (more) sg.load(kg, vg, kv_tok, (kt + 1) * KT, p.Sk, tid);
-    bool need_mask;
-    if (wave_active && tile_needed(kt * KT, wpos_lo, wpos_hi, p.window, need_mask))
-      st.attend(k_lds[buf], v_lds[buf], kt * KT, need_mask, p.window, p.scale_log2, lane);
+    int mask;
+    if (wave_active && tile_needed(kt * KT, wpos_lo, wpos_hi, p.window, mask))
+      st.attend(k_lds[buf], v_lds[buf], kt * KT, mask, p.window, p.scale_log2, lane);
     if (more) sg.store(k_lds[buf ^ 1], v_lds[buf ^ 1], tid);
     __syncthreads();
   }
@@ -300,7 +310,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
 // ----------------------------------------------------------------------------
 // Sliding window: persistent over a strip of 32-token blocks with an LDS ring.
 // G waves per workgroup, each wave 32/G tokens x G heads (one 32-row block).
-constexpr int kRingTiles = 8;
+// A wave's 32 query rows are TW runs of G*D contiguous elements in q and o
+// (the G heads of one token), so Q is loaded and O stored in whole rows,
+// half a head_dim at a time, through a private 32 x D/2 LDS staging tile that
+// converts between that layout and the MFMA register layout.
+constexpr int kRingTiles = 7;
 
 template <int D, int G>
 __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p) {
@@ -310,9 +324,14 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
   constexpr int TW = 32 / G;   // tokens per wave
   constexpr int TB = 32;       // tokens per block (= one key tile)
   constexpr int NR = kRingTiles;
+  constexpr int HD = D / 2;    // staging width: half a head
+  constexpr int HC = HD / 8;   // 16-byte chunks per staged row
+  constexpr int SIT = 32 * HC / 64;  // 16-byte chunks per lane per staged half
+  using Stg = PadTile<HD, HD + 8>;
 
   __shared__ __attribute__((aligned(16))) uint16_t k_ring[NR][Gm::K_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t v_ring[NR][Gm::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t stage_lds[NW][Stg::ELEMS];
 
   // strip -> (b, g, block range)
   const int strip = blockIdx.x;
@@ -329,24 +348,87 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
   const long kv_tok = (long)p.Hkv * D;
   const uint16_t* kg = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
   const uint16_t* vg = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
-  const long qoff = (long)b * p.Sq * q_tok;
+  // element offset of query row m (token tw0 + m / G, head g*G + m % G) of this request
+  const long qoff = (long)b * p.Sq * q_tok + (long)g * G * D;
   const int W = p.window;
+  uint16_t* stg = stage_lds[wv];
 
   auto kt_lo = [&](int blk) { return max(0, p.q_offset + blk * TB - W + 1) / KT; };
   auto kt_hi = [&](int blk) { return (p.q_offset + min(blk * TB + TB, p.Sq) - 1) / KT; };
+  auto row_off = [&](int tw0, int m) {  // rows past Sq read row Sq-1's token (never stored)
+    return qoff + (long)min(tw0 + m / G, p.Sq - 1) * q_tok + (long)(m % G) * D;
+  };
 
+  // Q of a block in whole-row layout: chunk u = it*64 + lane of half hh is
+  // row u / HC, 16-byte chunk u % HC of that half.
+  u32x4 qpre[2][SIT];
+  auto load_q_rows = [&](int tw0) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int it = 0; it < SIT; ++it) {
+        const int u = it * 64 + lane;
+        qpre[hh][it] = *(const u32x4*)(p.q + row_off(tw0, u / HC) + hh * HD + (u % HC) * 8);
+      }
+  };
   QState<D, 1> st;
-  bf16x8 qnext[Gm::NC];
+  // whole rows -> LDS -> MFMA B-operand layout (row col, d = 16c + 8*half)
+  auto stage_q = [&]() {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int it = 0; it < SIT; ++it) {
+        const int u = it * 64 + lane;
+        *(u32x4*)&stg[Stg::off(u / HC, (u % HC) * 8)] = qpre[hh][it];
+      }
+      wave_lds_sync();
+      const lds_u16* sbase = lane_base(lds_addr(stg), Stg::k_lane_off(lane));
+#pragma unroll
+      for (int c = 0; c < Gm::NC / 2; ++c)
+        st.q[0][hh * (Gm::NC / 2) + c] = Stg::k_operand(sbase, c);
+      wave_lds_sync();
+    }
+  };
+  // O = acc / l: MFMA layout -> LDS -> whole rows, half a head at a time
+  auto store_o_rows = [&](int tw0) {
+    const float lt = st.l_run[0] + swap_halves(st.l_run[0]);
+    const float inv = 1.0f / lt;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int db2 = 0; db2 < Gm::ND / 2; ++db2) {
+        const int db = hh * (Gm::ND / 2) + db2;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 y = {st.acc[0][db][4 * a4] * inv, st.acc[0][db][4 * a4 + 1] * inv,
+                           st.acc[0][db][4 * a4 + 2] * inv, st.acc[0][db][4 * a4 + 3] * inv};
+          *(bf16x4*)&stg[Stg::off(col, 32 * db2 + 8 * a4 + 4 * half)] = __builtin_convertvector(y, bf16x4);
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int it = 0; it < SIT; ++it) {
+        const int u = it * 64 + lane;
+        const int m = u / HC;
+        if (tw0 + m / G < p.Sq)
+          *(u32x4*)(p.o + qoff + (long)(tw0 + m / G) * q_tok + (long)(m % G) * D + hh * HD + (u % HC) * 8) =
+              *(const u32x4*)&stg[Stg::off(m, (u % HC) * 8)];
+      }
+      wave_lds_sync();
+    }
+  };
+
   Stager<D, NT> sg;
   const float sink2 = p.sinks ? p.sinks[g * G + col % G] * kLog2e : kNegInf;
 
   // prologue: the first block's queries and its whole window
-  st.load_q(p.q + qoff, q_tok, blk0 * TB + wv * TW, G, g, p.Sq, p.q_offset, col, half);
+  load_q_rows(blk0 * TB + wv * TW);
   int loaded_hi = kt_hi(blk0);
   for (int kt = kt_lo(blk0); kt <= loaded_hi; ++kt) {
     sg.load(kg, vg, kv_tok, kt * KT, p.Sk, tid);
     sg.store(k_ring[kt % NR], v_ring[kt % NR], tid);
   }
+  stage_q();
   // Drain every prologue load here, so that inside the loop the only loads in
   // flight are the prefetches and no wait inserted for the current queries
   // can stall on them.
@@ -359,21 +441,11 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
     // prefetch: next block's queries and (at most one) new K/V tile
     const int new_kt = nxt ? kt_hi(blk + 1) : -1;
     const bool have_new = new_kt > loaded_hi;
-    if (nxt) {
-      const int ntok = tw0 + TB + col / G;
-      const int h = g * G + col % G;
-      if (ntok < p.Sq) {
-        const uint16_t* qp = p.q + qoff + (long)ntok * q_tok + (long)h * D + half * 8;
-#pragma unroll
-        for (int c = 0; c < Gm::NC; ++c) qnext[c] = *(const bf16x8*)(qp + c * 16);
-      } else {
-#pragma unroll
-        for (int c = 0; c < Gm::NC; ++c) qnext[c] = bf16x8{};
-      }
-    }
+    if (nxt) load_q_rows(tw0 + TB);
     if (have_new) sg.load(kg, vg, kv_tok, new_kt * KT, p.Sk, tid);
 
     // compute this block from the ring
+    st.qpos[0] = p.q_offset + tw0 + col / G;
     st.reset(sink2, half);
     const bool wave_active = tw0 < p.Sq;
     if (wave_active) {
@@ -381,23 +453,19 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
       const int wpos_hi = p.q_offset + min(tw0 + TW, p.Sq) - 1;
       const int k1 = kt_hi(blk);
       for (int kt = kt_lo(blk); kt <= k1; ++kt) {
-        bool need_mask;
-        if (tile_needed(kt * KT, wpos_lo, wpos_hi, W, need_mask))
-          st.attend(k_ring[kt % NR], v_ring[kt % NR], kt * KT, need_mask, W, p.scale_log2, lane);
+        int mask;
+        if (tile_needed(kt * KT, wpos_lo, wpos_hi, W, mask))
+          st.attend(k_ring[kt % NR], v_ring[kt % NR], kt * KT, mask, W, p.scale_log2, lane);
       }
-      st.store_o(p.o + qoff, q_tok, tw0, G, g, p.Sq, col, half);
+      store_o_rows(tw0);
     }
     // the new tile's slot held tile new_kt - NR, older than this block's window
     if (have_new) {
       sg.store(k_ring[new_kt % NR], v_ring[new_kt % NR], tid);
       loaded_hi = new_kt;
     }
+    if (nxt) stage_q();
     __syncthreads();
-    if (nxt) {
-#pragma unroll
-      for (int c = 0; c < Gm::NC; ++c) st.q[0][c] = qnext[c];
-      st.qpos[0] += TB;
-    }
   }
 }
 
@@ -430,8 +498,9 @@ static hipError_t launch_strip(const PrefillArgs& a0, int num_cu, hipStream_t st
 
 template <int D>
 static hipError_t launch_d(const PrefillArgs& a, int G, hipStream_t s) {
-  // the strip kernel's ring must hold a block's window plus the next tile
-  const bool ring_fits = a.window > 0 && (31 + a.window + KT - 1) / KT + 1 + 1 <= kRingTiles;
+  // the strip kernel's ring must hold a block's window (at most
+  // floor((W + 30) / 32) + 2 tiles) plus the next block's new tile
+  const bool ring_fits = a.window > 0 && (a.window + 30) / KT + 2 + 1 <= kRingTiles;
   if (ring_fits && (G == 8 || G == 4)) {
     int dev = 0, num_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||

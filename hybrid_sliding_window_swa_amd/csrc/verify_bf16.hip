@@ -56,18 +56,17 @@ template <int D, int NB, int NW, bool DIRECT>
 __global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
-  constexpr int VROW = 32 + 4;                 // LDS pitch of a V^T row (bf16)
-  constexpr int VU = 16 * (D / 8);             // (key pair, 8 d) units per tile
-  constexpr int V_IT = VU / 64;
+  constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  constexpr int LD_IT = 32 * CPR / 64;         // 16-byte loads per lane per tile (K or V)
   constexpr int ACC_N = NB * ND * 16;          // accumulator floats per lane
   constexpr int MERGE_SLOTS = NW / 2 > 0 ? NW / 2 : 1;
-  static_assert(VU % 64 == 0, "V tile units must split evenly over a wave");
 
   struct MergeLds {
     float acc[MERGE_SLOTS][ACC_N][64];
   };
   struct TileLds {
-    uint16_t vt[NW][D * VROW];
+    uint16_t k[NW][KTile<D>::ELEMS];
+    uint16_t v[NW][VTile<D>::ELEMS];
   };
   constexpr size_t LDS_MAIN = sizeof(MergeLds) > sizeof(TileLds) ? sizeof(MergeLds) : sizeof(TileLds);
   __shared__ __attribute__((aligned(16))) unsigned char lds_main[LDS_MAIN];
@@ -116,54 +115,47 @@ __global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
     for (int db = 0; db < ND; ++db) acc[nb][db] = f32x16{};
   }
 
-  uint16_t* vt = ((TileLds*)lds_main)->vt[wv];
-  const uint16_t* kcache = p.k_cache + ((long)b * p.slots * p.Hkv + g) * D;
-  const uint16_t* vcache = p.v_cache + ((long)b * p.slots * p.Hkv + g) * D;
-  const uint16_t* knew = p.k_new + ((long)b * p.T * p.Hkv + g) * D;
-  const uint16_t* vnew = p.v_new + ((long)b * p.T * p.Hkv + g) * D;
+  uint16_t* k_t = ((TileLds*)lds_main)->k[wv];
+  uint16_t* v_t = ((TileLds*)lds_main)->v[wv];
+  const long bg_off = ((long)b * p.slots * p.Hkv + g) * D;
+  const long bg_new = ((long)b * p.T * p.Hkv + g) * D;
 
-  // Source row of row r (0..31) of tile j.  Rows past the valid range are
-  // clamped to the last valid row: they are masked out of the softmax and
-  // their (finite, committed) values get weight exactly 0, so unused cache
-  // slots are never read and no zero-fill branch is needed.
-  auto row_ptr = [&](int j, int r, const uint16_t* kbase_new, const uint16_t* kbase_cache) {
-    if (s == 0 && j == ntc) return kbase_new + (long)min(r, p.T - 1) * kv_tok;
-    return kbase_cache + (long)min(c0 + j * 32 + r, c1 - 1) * kv_tok;
+  // Element offset (from the cache or new-row base) of row r (0..31) of tile
+  // j.  Rows past the valid range are clamped to the last valid row: they are
+  // masked out of the softmax and their (finite, committed) values get weight
+  // exactly 0, so unused cache slots are never read and no zero-fill is needed.
+  auto row_off = [&](int j, int r) -> long {
+    if (s == 0 && j == ntc) return bg_new + (long)min(r, p.T - 1) * kv_tok;
+    return bg_off + (long)min(c0 + j * 32 + r, c1 - 1) * kv_tok;
   };
 
-  bf16x8 kreg[NC], knext[NC];
-  u32x4 vnext[V_IT][2];
-  auto load_tile = [&](int j, bf16x8 (&kr)[NC], u32x4 (&vr)[V_IT][2]) {
-    const uint16_t* kp = row_ptr(j, col, knew, kcache) + half * 8;
+  // Tile staging: load i of a lane covers row 4i + lane/16 (D = 128), chunk
+  // lane%16: every load instruction reads whole 256-byte rows.
+  u32x4 kpre[LD_IT], vpre[LD_IT];
+  auto load_tile = [&](int j) {
+    const bool nw = (s == 0 && j == ntc);
+    const uint16_t* kb = nw ? p.k_new : p.k_cache;
+    const uint16_t* vb = nw ? p.v_new : p.v_cache;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kr[c] = *(const bf16x8*)(kp + c * 16);
-#pragma unroll
-    for (int i = 0; i < V_IT; ++i) {
-      const int u = lane + 64 * i;
-      const int pr = u % 16, c8 = u / 16;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) vr[i][e] = *(const u32x4*)(row_ptr(j, 2 * pr + e, vnew, vcache) + c8 * 8);
+    for (int i = 0; i < LD_IT; ++i) {
+      const int c = lane + 64 * i;
+      const long o = row_off(j, c / CPR) + (c % CPR) * 8;
+      kpre[i] = *(const u32x4*)(kb + o);
+      vpre[i] = *(const u32x4*)(vb + o);
     }
   };
-  auto store_v = [&](const u32x4 (&vr)[V_IT][2]) {
+  auto store_tile = [&]() {
 #pragma unroll
-    for (int i = 0; i < V_IT; ++i) {
-      const int u = lane + 64 * i;
-      const int pr = u % 16, c8 = u / 16;
-      uint32_t* dst = (uint32_t*)&vt[(c8 * 8) * VROW + 2 * pr];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w0 = vr[i][0][e >> 1], w1 = vr[i][1][e >> 1];
-        const uint32_t lo = (e & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-        const uint32_t hi = (e & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
-        dst[e * (VROW / 2)] = lo | hi;
-      }
+    for (int i = 0; i < LD_IT; ++i) {
+      const int c = lane + 64 * i;
+      *(u32x4*)&k_t[KTile<D>::off(c / CPR, (c % CPR) * 8)] = kpre[i];
+      *(u32x4*)&v_t[VTile<D>::off(c / CPR, (c % CPR) * 8)] = vpre[i];
     }
   };
 
   if (wv < ntiles) {
-    load_tile(wv, kreg, vnext);
-    store_v(vnext);
+    load_tile(wv);
+    store_tile();
   }
   // Drain the prologue loads (queries, first tile) so that inside the loop
   // the only loads in flight are the prefetch of the next tile and nothing
@@ -171,16 +163,18 @@ __global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
   __builtin_amdgcn_s_waitcnt(0);
   for (int j = wv; j < ntiles; j += NW) {
     const bool more = j + NW < ntiles;
-    if (more) load_tile(j + NW, knext, vnext);
+    if (more) load_tile(j + NW);
     wave_lds_sync();
 
     f32x16 sc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x16{};
+    const lds_u16* kbase = lane_base(lds_addr(k_t), KTile<D>::k_lane_off(lane));
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+      const bf16x8 a = KTile<D>::k_operand(kbase, c);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma32(kreg[c], qreg[nb][c], sc[nb]);
+      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma32(a, qreg[nb][c], sc[nb]);
     }
     const bool is_new_tile = (s == 0 && j == ntc);
 #pragma unroll
@@ -219,32 +213,19 @@ __global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
       }
       const float mu = m_run[nb] == kNegInf ? 0.0f : m_run[nb];
       bf16x8 pb[2];
-      float ls = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = exp2_fast(sc[nb][v] - mu);
-        ls += e;
-        pb[v >> 3][v & 7] = (__bf16)e;
-      }
-      l_run[nb] += ls;
+      for (int v = 0; v < 16; ++v) pb[v >> 3][v & 7] = (__bf16)exp2_fast(sc[nb][v] - mu);
+      l_run[nb] = sum_bf16x16(pb[0], pb[1], l_run[nb]);
+      const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const uint16_t* vp = &vt[(db * 32 + col) * VROW + 16 * kc + 4 * half];
-          const u32x2 lo = *(const u32x2*)vp;
-          const u32x2 hi = *(const u32x2*)(vp + 8);
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          acc[nb][db] = mfma32(__builtin_bit_cast(bf16x8, av), pb[kc], acc[nb][db]);
-        }
+        for (int db = 0; db < ND; ++db)
+          acc[nb][db] = mfma32(VTile<D>::vt_operand(vbase, db, kc), pb[kc], acc[nb][db]);
       }
     }
     wave_lds_sync();
-    if (more) {
-      store_v(vnext);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kreg[c] = knext[c];
-    }
+    if (more) store_tile();
   }
 
   // ---- merge the waves: common max, then a fixed-order pairwise sum in LDS
