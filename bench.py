@@ -30,8 +30,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-PREFILL_KERNEL_SRC = os.path.join(ROOT, "hybrid_sliding_window_swa_amd", "csrc", "prefill_bf16.hip")
-VERIFY_KERNEL_SRC = os.path.join(ROOT, "hybrid_sliding_window_swa_amd", "csrc", "verify_bf16.hip")
+_CSRC = os.path.join(ROOT, "hybrid_sliding_window_swa_amd", "csrc")
+# sources a kernel's HBM traffic depends on (counters are void once these change)
+PREFILL_KERNEL_SRC = [os.path.join(_CSRC, f) for f in ("prefill_bf16.hip", "common.hpp", "launch.hpp")]
+VERIFY_KERNEL_SRC = [os.path.join(_CSRC, f) for f in ("verify_bf16.hip", "common.hpp", "launch.hpp")]
 
 
 def parse():
@@ -61,8 +63,11 @@ def swa_pairs(S: int, W: int, q_offset: int = 0) -> int:
     return tot
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(name: str, src: str):

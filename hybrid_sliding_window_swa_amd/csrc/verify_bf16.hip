@@ -53,7 +53,7 @@ __device__ __forceinline__ SplitRange split_range(const VerifyArgs& p, int L) {
 }  // namespace
 
 template <int D, int NB, int NW, bool DIRECT>
-__global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_bf16_kernel(VerifyArgs p) {
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
@@ -73,7 +73,11 @@ __global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
   __shared__ float lds_m[NW][NB * 32];
   __shared__ float lds_l[NW][NB * 32];
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // grid (B * Hkv, nsplit): workgroups are dealt to the 8 XCDs round-robin by
+  // linear id, so with (request, KV head) as the fastest dimension every XCD
+  // gets the same mix of long and short requests (with 8 KV heads, XCD = KV
+  // head); splits past a request's length exit at once.
+  const int g = blockIdx.x % p.Hkv, b = blockIdx.x / p.Hkv, s = blockIdx.y;
   const int L = p.cache_len[b];
   const SplitRange sr = split_range(p, L);
   if (s >= sr.ns) return;
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(NW * 64) void verify_bf16_kernel(VerifyArgs p) {
 // l = sum_s l_s 2^(m_s - M) + 2^(sink - M), O = sum_s O_s 2^(m_s - M) / l.
 template <int D>
 __global__ __launch_bounds__(256) void verify_combine_kernel(VerifyArgs p) {
-  const int g = blockIdx.x, b = blockIdx.y;
+  const int g = blockIdx.x % p.Hkv, b = blockIdx.x / p.Hkv;
   const int L = p.cache_len[b];
   const SplitRange sr = split_range(p, L);
   const int G = p.Hq / p.Hkv;
@@ -369,10 +373,11 @@ VerifyPlan plan_verify_bf16(int B, int T, int Hq, int Hkv, int D, int slots, int
   long max_rows = slots;
   if (!ring && window > 0 && window - 1 < max_rows) max_rows = window - 1;
   if (max_rows < 1) max_rows = 1;
-  // aim for >= ~1024 workgroups, splits of at most 4096 rows
+  // aim for >= ~1024 workgroups, splits of at most 8192 rows (measured best on
+  // the 64-request global-cache verify: fewer partials, short enough tail)
   long want = max_rows * (long)B * Hkv / 1024;
   long sl = unit;
-  while (sl < want && sl < 4096) sl *= 2;
+  while (sl < want && sl < 8192) sl *= 2;
   if (sl < unit) sl = unit;
   sl = (sl + unit - 1) / unit * unit;
   pl.split_len = (int)sl;
@@ -386,7 +391,7 @@ VerifyPlan plan_verify_bf16(int B, int T, int Hq, int Hkv, int D, int slots, int
 
 template <int D, int NB, int NW>
 static hipError_t launch_verify_t(VerifyArgs a, const VerifyPlan& pl, hipStream_t s) {
-  dim3 grid(pl.nsplit, a.Hkv, a.B), block(NW * 64);
+  dim3 grid(a.B * a.Hkv, pl.nsplit), block(NW * 64);
   if (pl.nsplit == 1) {
     hipLaunchKernelGGL((verify_bf16_kernel<D, NB, NW, true>), grid, block, 0, s, a);
     return hipGetLastError();
@@ -394,7 +399,7 @@ static hipError_t launch_verify_t(VerifyArgs a, const VerifyPlan& pl, hipStream_
   hipLaunchKernelGGL((verify_bf16_kernel<D, NB, NW, false>), grid, block, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_combine_kernel<D>), dim3(a.Hkv, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((verify_combine_kernel<D>), dim3(a.B * a.Hkv), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
