@@ -38,8 +38,35 @@ __device__ __forceinline__ constexpr int c_row(int v, int half) {
   return 8 * (v >> 2) + 4 * half + (v & 3);
 }
 
-// Value of x in lane (l ^ 32).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// Both halves of the wave combined, lane l with lane l ^ 32, in registers:
+// v_permlane32_swap leaves (x_lo, x_lo) in one result and (x_hi, x_hi) in the
+// other, so every lane sees both values of its pair without an LDS round trip.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Raw buffer resource over [base, base + bytes): a load past the end reads
+// zeros and a store past the end is dropped (the buffer range check), so
+// ragged tails need no per-lane clamps or branches, and the tile / row
+// offset can live in a scalar register.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
@@ -58,11 +85,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // A tile of 32 rows x D bf16 in LDS, row-major with a padded row pitch of
 // PITCH elements (a multiple of 8).  Every MFMA operand address is a per-lane
 // base plus a compile-time offset, so no address arithmetic sits in the tile
-// loop.  Pitches used (32 banks of 4 bytes): K tiles D + 8 (16-byte chunk
-// position advances by 1 per row: the 8 rows of a K-operand read hit 8
-// distinct chunk positions); V tiles D + 16 (advance by 2 per row: the 4 rows
-// x 2 chunks of a transposed read hit 8 distinct positions); staging tiles of
-// D/2 columns + 8.
+// loop.  gfx950's LDS has 64 banks of 4 bytes (256 bytes per clock; measured
+// with the SQ_LDS_BANK_CONFLICT counter per access pattern):
+//   * K tiles, pitch D + 8: a 16-byte K-operand read serves 16 lanes per
+//     clock, rows 0..15 of one chunk, whose 16-byte positions advance by one
+//     per row, so all 64 banks are distinct.
+//   * V tiles, pitch D + 32: ds_read_b64_tr_b16 serves 32 lanes per clock,
+//     rows n0..n0+3 x 64 bytes; the pitch is 16 (D = 128) or 48 (D = 64)
+//     dwords modulo 64, so the four rows land on disjoint 16-bank groups.
+//     (D + 16 costs two extra clocks per read.)
+//   * staging tiles of D/2 columns + 8, as K tiles.
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -116,7 +148,7 @@ struct PadTile {
 template <int D>
 using KTile = PadTile<D, D + 8>;
 template <int D>
-using VTile = PadTile<D, D + 16>;
+using VTile = PadTile<D, D + 32>;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 

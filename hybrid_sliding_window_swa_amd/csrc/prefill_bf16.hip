@@ -11,21 +11,23 @@
 // Shared structure of both kernels in this file
 //   * A workgroup owns consecutive tokens of one request and ALL G query heads
 //     of one KV head g, so every K/V tile it stages in LDS serves the whole
-//     GQA group.  Each wave owns 32*NB query rows: row m of a 32-row block is
-//     (token m / G, head m % G).
+//     GQA group.  Each wave owns 32 query rows: row m is (token m / G, head
+//     m % G).
 //   * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16
 //     MFMA: lane l then holds 16 scores of ONE query (column l%32) and the
 //     other 16 live in lane l^32, so the softmax row max needs one half swap
-//     and the row sum none until the end.  The exponentiated scores P^T are
-//     already laid out as the B operand of O^T += V^T P^T, so P never goes
-//     through LDS.
-//   * V^T is the A operand of that product; the staging step writes each V
-//     tile into LDS transposed ([d][key]) once per workgroup.
-//   * Key tiles are 32 keys.  Each wave skips tiles outside its own window and
-//     applies the causal / window mask only on boundary tiles.
+//     (v_permlane32_swap) and the row sum none until the end.  The
+//     exponentiated scores P^T are already laid out as the B operand of
+//     O^T += V^T P^T, so P never goes through LDS.
+//   * V^T is the A operand of that product.  V tiles stay row-major in LDS;
+//     ds_read_b64_tr_b16 transposes while reading.
+//   * Key tiles are 32 keys.  Each wave visits only the tiles of its own
+//     window and applies the causal / window mask on boundary tiles only.
 //   * Online softmax in the log2 domain, fp32, started from the sink
 //     (m = sink*log2e, l = 1), with a lazy rescale: the running max is only
 //     raised when a score exceeds it by more than kRescaleTau.
+//   * Software pipelining inside each wave: the score MFMAs of tile kt + 1
+//     are issued between the exponentials of tile kt.
 //
 // prefill_swa_strip_kernel (sliding window, G in {4, 8}): persistent over a
 //   strip of consecutive 32-token blocks of one (request, KV head).  The K/V
@@ -34,7 +36,7 @@
 //   are already in flight, and the block's output is stored asynchronously,
 //   so HBM streams continuously.
 // prefill_bf16_kernel (global attention and any other shape): one workgroup
-//   per token block, double-buffered K/V tiles, XCD-aware block order with
+//   per token block, K tiles staged one ahead of V tiles, XCD-aware order with
 //   the longest (latest) blocks first.
 #include "common.hpp"
 #include "launch.hpp"
@@ -44,7 +46,7 @@ namespace swa {
 namespace {
 
 constexpr int KT = 32;  // keys per tile
-constexpr int kMaskHi = 1, kMaskLo = 2;
+constexpr int kMaskHi = 1, kMaskLo = 2, kMaskAll = 4;
 
 template <int D>
 struct TileGeom {
@@ -55,174 +57,220 @@ struct TileGeom {
   static constexpr int KCH = KT * D / 8;        // 16-byte chunks of a K (or V) tile
 };
 
-// Global -> register half of staging one 32-key tile of K and of V; rows at
-// or past Sk are clamped to row Sk - 1 (finite data, always masked out).
+// Global -> register half of staging 32-key tiles of K and of V (possibly of
+// different tiles), through raw buffer loads: the tile's first row is a
+// scalar base, each thread's offset inside the tile is fixed, and rows at or
+// past Sk read as zeros (always masked out).
 template <int D, int NT>
 struct Stager {
   using Gm = TileGeom<D>;
   static constexpr int IT = (Gm::KCH + NT - 1) / NT;
   u32x4 kpre[IT];
   u32x4 vpre[IT];
+  uint32_t voff[IT];  // byte offset of this thread's 16-byte chunks in a tile
 
-  __device__ __forceinline__ void load(const uint16_t* kg, const uint16_t* vg, long kv_tok, int kb,
-                                       int Sk, int tid) {
+  __device__ __forceinline__ void init(long kv_tok, int tid) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int c = tid + i * NT;
-      if (c < Gm::KCH) {
-        const int row = c / (D / 8), c8 = c % (D / 8);
-        const long off = (long)min(kb + row, Sk - 1) * kv_tok + c8 * 8;
-        kpre[i] = *(const u32x4*)(kg + off);
-        vpre[i] = *(const u32x4*)(vg + off);
-      }
+      voff[i] = (uint32_t)(((c / (D / 8)) * kv_tok + (c % (D / 8)) * 8) * 2);
     }
   }
+  static __device__ __forceinline__ rsrc_t tile(const uint16_t* g, long kv_tok, int kb, int Sk) {
+    const int rows = min(KT, Sk - kb);
+    return make_rsrc(g + (long)kb * kv_tok, (uint32_t)(((rows - 1) * kv_tok + D) * 2));
+  }
+  __device__ __forceinline__ void load_k(const uint16_t* kg, long kv_tok, int kb, int Sk, int tid) {
+    const rsrc_t r = tile(kg, kv_tok, kb, Sk);
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+      if (tid + i * NT < Gm::KCH) kpre[i] = buf_load16(r, voff[i], 0);
+  }
+  __device__ __forceinline__ void load_v(const uint16_t* vg, long kv_tok, int kb, int Sk, int tid) {
+    const rsrc_t r = tile(vg, kv_tok, kb, Sk);
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+      if (tid + i * NT < Gm::KCH) vpre[i] = buf_load16(r, voff[i], 0);
+  }
+  __device__ __forceinline__ void load(const uint16_t* kg, const uint16_t* vg, long kv_tok, int kb,
+                                       int Sk, int tid) {
+    load_k(kg, kv_tok, kb, Sk, tid);
+    load_v(vg, kv_tok, kb, Sk, tid);
+  }
 
-  // Register -> LDS half: both tiles row-major with padded pitches.
-  __device__ __forceinline__ void store(uint16_t* k_dst, uint16_t* v_dst, int tid) const {
+  // Register -> LDS half: row-major tiles with padded pitches.
+  __device__ __forceinline__ void store_k(uint16_t* k_dst, int tid) const {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int c = tid + i * NT;
-      if (c < Gm::KCH) {
-        const int row = c / (D / 8), c8 = c % (D / 8);
-        *(u32x4*)&k_dst[KTile<D>::off(row, c8 * 8)] = kpre[i];
-        *(u32x4*)&v_dst[VTile<D>::off(row, c8 * 8)] = vpre[i];
-      }
+      if (c < Gm::KCH) *(u32x4*)&k_dst[KTile<D>::off(c / (D / 8), (c % (D / 8)) * 8)] = kpre[i];
     }
+  }
+  __device__ __forceinline__ void store_v(uint16_t* v_dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int c = tid + i * NT;
+      if (c < Gm::KCH) *(u32x4*)&v_dst[VTile<D>::off(c / (D / 8), (c % (D / 8)) * 8)] = vpre[i];
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* k_dst, uint16_t* v_dst, int tid) const {
+    store_k(k_dst, tid);
+    store_v(v_dst, tid);
   }
 };
 
-// Per-lane state of NB 32-query blocks.
-template <int D, int NB>
+// Per-lane state of one 32-query block; row m of the block is (token m / G,
+// head m % G), and lane l holds query column l % 32.
+template <int D>
 struct QState {
   using Gm = TileGeom<D>;
-  bf16x8 q[NB][Gm::NC];
-  int qpos[NB];
-  float m_run[NB], l_run[NB];
-  f32x16 acc[NB][Gm::ND];
+  bf16x8 q[Gm::NC];
+  int qpos;
+  float m_run, l_run;
+  f32x16 acc[Gm::ND];
 
-  // token of block nb for this lane, with G heads per token
   __device__ __forceinline__ void load_q(const uint16_t* qbase, long q_tok, int tw0, int G, int g,
                                          int Sq, int q_offset, int col, int half) {
+    const int tok = tw0 + col / G;
+    const int h = g * G + col % G;
+    qpos = q_offset + tok;
+    if (tok < Sq) {
+      const uint16_t* qp = qbase + (long)tok * q_tok + (long)h * D + half * 8;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int tok = tw0 + nb * (32 / G) + col / G;
-      const int h = g * G + col % G;
-      qpos[nb] = q_offset + tok;
-      if (tok < Sq) {
-        const uint16_t* qp = qbase + (long)tok * q_tok + (long)h * D + half * 8;
+      for (int c = 0; c < Gm::NC; ++c) q[c] = *(const bf16x8*)(qp + c * 16);
+    } else {
 #pragma unroll
-        for (int c = 0; c < Gm::NC; ++c) q[nb][c] = *(const bf16x8*)(qp + c * 16);
-      } else {
-#pragma unroll
-        for (int c = 0; c < Gm::NC; ++c) q[nb][c] = bf16x8{};
-      }
+      for (int c = 0; c < Gm::NC; ++c) q[c] = bf16x8{};
     }
   }
 
   // Start every row from its head's sink: m = sink*log2e, l = 1 (counted once,
   // in the lower half of the wave).  sink2 = sink * log2(e), or -inf for none.
-  // Every lane's rows share one head set (col % G), so one value serves all
-  // blocks.
   __device__ __forceinline__ void reset(float sink2, int half) {
+    m_run = sink2;
+    l_run = (sink2 != kNegInf && half == 0) ? 1.0f : 0.0f;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      m_run[nb] = sink2;
-      l_run[nb] = (sink2 != kNegInf && half == 0) ? 1.0f : 0.0f;
-#pragma unroll
-      for (int db = 0; db < Gm::ND; ++db) acc[nb][db] = f32x16{};
-    }
+    for (int db = 0; db < Gm::ND; ++db) acc[db] = f32x16{};
   }
 
-  // Fold one 32-key tile (K and V rows in LDS, first key position kb).
-  // mask: kMaskHi if some key of the tile lies after some query of the wave,
-  // kMaskLo if some key lies below some query's window.
-  __device__ __forceinline__ void attend(const uint16_t* k_t, const uint16_t* v_t, int kb,
-                                         int mask, int window, float c2, int lane) {
-    const int col = lane & 31, half = lane >> 5;
-    f32x16 s[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
+  // Raw scores S^T = K Q^T of one 32-key tile in LDS.
+  __device__ __forceinline__ f32x16 scores(const uint16_t* k_t, int lane) const {
     const lds_u16* kbase = lane_base(lds_addr(k_t), KTile<D>::k_lane_off(lane));
+    bf16x8 ka[Gm::NC];
 #pragma unroll
-    for (int c = 0; c < Gm::NC; ++c) {
-      const bf16x8 a = KTile<D>::k_operand(kbase, c);
+    for (int c = 0; c < Gm::NC; ++c) ka[c] = KTile<D>::k_operand(kbase, c);
+    f32x16 s = {};
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) s[nb] = mfma32(a, q[nb][c], s[nb]);
+    for (int c = 0; c < Gm::NC; ++c) s = mfma32(ka[c], q[c], s);
+    return s;
+  }
+
+  // Causal / window mask of the tile starting at key kb, the row max and the
+  // lazy rescale; returns the shift of the exponents.  mask: kMaskHi if some
+  // key of the tile lies after some query of the wave, kMaskLo if some key
+  // lies below some query's window, kMaskAll to drop the whole tile.
+  __device__ __forceinline__ float prep(f32x16& s, int kb, int mask, int window, float c2, int half) {
+    if (mask == kMaskAll) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = kNegInf;
+    } else if (mask) {
+      // The key of register v sits at kb + 4*half + cv with cv = 8*(v/4) +
+      // v%4, so with a = qpos - kb - 4*half it is valid iff a - W + 1 <= cv
+      // <= a: one compare per score when only one bound can bite.
+      const int a = qpos - kb - 4 * half;
+      const int alo = a - window + 1;
+      if (mask == kMaskHi) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = (c_row(v, 0) <= a) ? s[v] : kNegInf;
+      } else if (mask == kMaskLo) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = (c_row(v, 0) >= alo) ? s[v] : kNegInf;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = (c_row(v, 0) <= a && c_row(v, 0) >= alo) ? s[v] : kNegInf;
+      }
     }
-    if (mask) {
-      // Causal / window mask of a boundary tile (masked scores -> -inf).  The
-      // key of register v sits at kb + 4*half + cv with cv = 8*(v/4) + v%4, so
-      // with a = qpos - kb - 4*half it is valid iff a - W + 1 <= cv <= a: one
-      // compare per score when only one bound can bite.
+    // raw-score max (scale > 0 commutes with max)
+    float mx = kNegInf;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int a = qpos[nb] - kb - 4 * half;
-        const int alo = a - window + 1;
-        if (mask == kMaskHi) {
+    for (int v = 0; v < 16; ++v) mx = __builtin_fmaxf(mx, s[v]);
+    mx = halves_max(mx) * c2;
+    const float m_new = __builtin_fmaxf(m_run, mx);
+    const bool need = m_new > m_run + kRescaleTau;
+    if (wave_any(need)) {
+      const float alpha = need ? exp2_fast(m_run - m_new) : 1.0f;
+      m_run = need ? m_new : m_run;
+      l_run *= alpha;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) s[nb][v] = (c_row(v, 0) <= a) ? s[nb][v] : kNegInf;
-        } else if (mask == kMaskLo) {
+      for (int db = 0; db < Gm::ND; ++db) acc[db] *= alpha;
+    }
+    return m_run == kNegInf ? 0.0f : m_run;
+  }
+
+  // P = exp2(s*c2 - mu) rounded to bf16, l += sum P, O^T += V^T P^T for the V
+  // tile v_t.  With NEXT the raw scores of the K tile k_next are computed in
+  // the same instruction stream and returned: each of its MFMAs is followed
+  // by a share of the exponentials (scheduling fences keep that order), so
+  // the matrix core and the vector ALU of the SIMD work at the same time.
+  template <bool NEXT>
+  __device__ __forceinline__ f32x16 fold(const f32x16& s, float mu, float c2, const uint16_t* v_t,
+                                         const uint16_t* k_next, int lane) {
+    constexpr int EPM = 16 / Gm::NC;  // exponentials per score MFMA
+    const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
+    f32x16 sn = {};
+    bf16x8 pb[2];
+    bf16x8 va[Gm::ND];
+    if constexpr (NEXT) {
+      const lds_u16* kbase = lane_base(lds_addr(k_next), KTile<D>::k_lane_off(lane));
+      bf16x8 ka[Gm::NC];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) s[nb][v] = (c_row(v, 0) >= alo) ? s[nb][v] : kNegInf;
-        } else {
+      for (int c = 0; c < Gm::NC; ++c) ka[c] = KTile<D>::k_operand(kbase, c);
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            s[nb][v] = (c_row(v, 0) <= a && c_row(v, 0) >= alo) ? s[nb][v] : kNegInf;
+      for (int db = 0; db < Gm::ND; ++db) va[db] = VTile<D>::vt_operand(vbase, db, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < Gm::NC; ++c) {
+        sn = mfma32(ka[c], q[c], sn);
+#pragma unroll
+        for (int e = 0; e < EPM; ++e) {
+          const int v = c * EPM + e;
+          pb[v >> 3][v & 7] = (__bf16)exp2_fast(fmaf(s[v], c2, -mu));
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db) va[db] = VTile<D>::vt_operand(vbase, db, 0);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) pb[v >> 3][v & 7] = (__bf16)exp2_fast(fmaf(s[v], c2, -mu));
     }
+    // O^T += V^T P^T: keys 16kc .. 16kc+15 per MFMA
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      // raw-score max (scale > 0 commutes with max)
-      float mx = kNegInf;
+    for (int db = 0; db < Gm::ND; ++db) acc[db] = mfma32(va[db], pb[0], acc[db]);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[nb][v]);
-      mx = fmaxf(mx, swap_halves(mx)) * c2;
-      const float m_new = fmaxf(m_run[nb], mx);
-      const bool need = m_new > m_run[nb] + kRescaleTau;
-      if (wave_any(need)) {
-        const float alpha = need ? exp2_fast(m_run[nb] - m_new) : 1.0f;
-        m_run[nb] = need ? m_new : m_run[nb];
-        l_run[nb] *= alpha;
+    for (int db = 0; db < Gm::ND; ++db) va[db] = VTile<D>::vt_operand(vbase, db, 1);
 #pragma unroll
-        for (int db = 0; db < Gm::ND; ++db) acc[nb][db] *= alpha;
-      }
-      const float mu = m_run[nb] == kNegInf ? 0.0f : m_run[nb];
-      bf16x8 pb[2];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) pb[v >> 3][v & 7] = (__bf16)exp2_fast(fmaf(s[nb][v], c2, -mu));
-      l_run[nb] = sum_bf16x16(pb[0], pb[1], l_run[nb]);
-      // O^T += V^T P^T: keys 16kc .. 16kc+15 per MFMA
-      const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-#pragma unroll
-        for (int db = 0; db < Gm::ND; ++db)
-          acc[nb][db] = mfma32(VTile<D>::vt_operand(vbase, db, kc), pb[kc], acc[nb][db]);
-      }
-    }
+    for (int db = 0; db < Gm::ND; ++db) acc[db] = mfma32(va[db], pb[1], acc[db]);
+    l_run = sum_bf16x16(pb[0], pb[1], l_run);
+    return sn;
   }
 
   // O = acc / l in bf16, one 8-byte store per 4 consecutive d.
   __device__ __forceinline__ void store_o(uint16_t* obase, long q_tok, int tw0, int G, int g, int Sq,
                                           int col, int half) {
+    const int tok = tw0 + col / G;
+    const int h = g * G + col % G;
+    const float lt = halves_sum(l_run);
+    if (tok >= Sq) return;
+    const float inv = 1.0f / lt;
+    uint16_t* op = obase + (long)tok * q_tok + (long)h * D;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int tok = tw0 + nb * (32 / G) + col / G;
-      const int h = g * G + col % G;
-      const float lt = l_run[nb] + swap_halves(l_run[nb]);
-      if (tok >= Sq) continue;
-      const float inv = 1.0f / lt;
-      uint16_t* op = obase + (long)tok * q_tok + (long)h * D;
+    for (int db = 0; db < Gm::ND; ++db) {
 #pragma unroll
-      for (int db = 0; db < Gm::ND; ++db) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 y = {acc[nb][db][4 * a4] * inv, acc[nb][db][4 * a4 + 1] * inv,
-                           acc[nb][db][4 * a4 + 2] * inv, acc[nb][db][4 * a4 + 3] * inv};
-          *(bf16x4*)(op + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(y, bf16x4);
-        }
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 y = {acc[db][4 * a4] * inv, acc[db][4 * a4 + 1] * inv, acc[db][4 * a4 + 2] * inv,
+                         acc[db][4 * a4 + 3] * inv};
+        *(bf16x4*)(op + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(y, bf16x4);
       }
     }
   }
@@ -242,15 +290,18 @@ __device__ __forceinline__ bool tile_needed(int kb, int wpos_lo, int wpos_hi, in
 
 // ----------------------------------------------------------------------------
 // One workgroup per block of TB tokens (global attention and general shapes).
-template <int D, int G, int NB, int NW>
+// K tiles are staged one tile ahead of V tiles (three K slots, two V slots),
+// so while a wave exponentiates tile kt it already computes the scores of
+// tile kt + 1.
+template <int D, int G, int NW>
 __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   using Gm = TileGeom<D>;
   constexpr int NT = NW * 64;
-  constexpr int TW = 32 * NB / G;   // tokens per wave
+  constexpr int TW = 32 / G;        // tokens per wave
   constexpr int TB = TW * NW;       // tokens per workgroup
-  static_assert(32 * NB % G == 0, "a 32-row block must hold whole tokens");
+  static_assert(32 % G == 0, "a 32-row block must hold whole tokens");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][Gm::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[3][Gm::K_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][Gm::V_ELEMS];
 
   // XCD-aware work item: workgroups on one XCD (blockIdx % 8) take consecutive
@@ -272,39 +323,70 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   const uint16_t* kg = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
   const uint16_t* vg = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
   const long qoff = (long)b * p.Sq * q_tok;
+  const int W = p.window;
+  const float c2 = p.scale_log2;
 
-  QState<D, NB> st;
+  QState<D> st;
   st.load_q(p.q + qoff, q_tok, tw0, G, g, p.Sq, p.q_offset, col, half);
   st.reset(p.sinks ? p.sinks[g * G + col % G] * kLog2e : kNegInf, half);
 
   const int tlast = min(t0 + TB, p.Sq) - 1;
   const int pos_lo = p.q_offset + t0, pos_hi = p.q_offset + tlast;
-  const int key_lo = p.window > 0 ? max(0, pos_lo - p.window + 1) : 0;
-  const int kt_begin = key_lo / KT, kt_end = pos_hi / KT;
-  const bool wave_active = tw0 < p.Sq;
+  const int kt_begin = (W > 0 ? max(0, pos_lo - W + 1) : 0) / KT, kt_end = pos_hi / KT;
+  // this wave's tiles: [wk0, wk1] (empty when its tokens are all past Sq)
   const int wpos_lo = p.q_offset + tw0;
   const int wpos_hi = p.q_offset + min(tw0 + TW, p.Sq) - 1;
+  const int wk0 = max(kt_begin, (W > 0 ? max(0, wpos_lo - W + 1) : 0) / KT);
+  const int wk1 = tw0 < p.Sq ? wpos_hi / KT : -1;
 
   Stager<D, NT> sg;
+  sg.init(kv_tok, tid);
   sg.load(kg, vg, kv_tok, kt_begin * KT, p.Sk, tid);
   sg.store(k_lds[0], v_lds[0], tid);
-  // Drain the prologue loads (queries, first tile): inside the loop the only
-  // loads in flight are then the next tile's, and no wait for the queries
-  // can stall on them.
+  if (kt_begin < kt_end) {
+    sg.load_k(kg, kv_tok, (kt_begin + 1) * KT, p.Sk, tid);
+    sg.store_k(k_lds[1], tid);
+  }
+  // Drain the prologue loads (queries, first tiles): inside the loop the only
+  // loads in flight are then the prefetches, and no wait for the queries can
+  // stall on them.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int kt = kt_begin; kt <= kt_end; ++kt) {
-    const int buf = (kt - kt_begin) & 1;
-    const bool more = kt < kt_end;
-    if (more) sg.load(kg, vg, kv_tok, (kt + 1) * KT, p.Sk, tid);
-    int mask;
-    if (wave_active && tile_needed(kt * KT, wpos_lo, wpos_hi, p.window, mask))
-      st.attend(k_lds[buf], v_lds[buf], kt * KT, mask, p.window, p.scale_log2, lane);
-    if (more) sg.store(k_lds[buf ^ 1], v_lds[buf ^ 1], tid);
+  // One code path per iteration: a wave inside its range folds tile kt and
+  // computes the scores of tile kt + 1 (discarded after its last tile); in
+  // the iteration before its first tile it folds a fully masked tile, which
+  // adds nothing, to get those scores.  The last tile of the workgroup is
+  // folded after the loop.
+  f32x16 s = {};
+  if (wk0 == kt_begin && wk1 >= 0) s = st.scores(k_lds[0], lane);
+  int ks0 = 0, ks1 = 1, ks2 = 2;  // K slots of tiles kt, kt + 1, kt + 2
+  int vs = 0;                      // V slot of tile kt
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const bool more_k = kt + 2 <= kt_end;
+    if (more_k) sg.load_k(kg, kv_tok, (kt + 2) * KT, p.Sk, tid);
+    sg.load_v(vg, kv_tok, (kt + 1) * KT, p.Sk, tid);
+    if (kt + 1 >= wk0 && kt <= wk1) {
+      int mask;
+      tile_needed(kt * KT, wpos_lo, wpos_hi, W, mask);
+      if (kt < wk0) mask = kMaskAll;
+      const float mu = st.prep(s, kt * KT, mask, W, c2, half);
+      s = st.template fold<true>(s, mu, c2, v_lds[vs], k_lds[ks1], lane);
+    }
+    if (more_k) sg.store_k(k_lds[ks2], tid);
+    sg.store_v(v_lds[vs ^ 1], tid);
     __syncthreads();
+    const int t = ks0;
+    ks0 = ks1; ks1 = ks2; ks2 = t;
+    vs ^= 1;
   }
-  if (wave_active) st.store_o(p.o + qoff, q_tok, tw0, G, g, p.Sq, col, half);
+  if (kt_end >= wk0 && kt_end <= wk1) {
+    int mask;
+    tile_needed(kt_end * KT, wpos_lo, wpos_hi, W, mask);
+    const float mu = st.prep(s, kt_end * KT, mask, W, c2, half);
+    st.template fold<false>(s, mu, c2, v_lds[vs], nullptr, lane);
+  }
+  if (wk1 >= 0) st.store_o(p.o + qoff, q_tok, tw0, G, g, p.Sq, col, half);
 }
 
 // ----------------------------------------------------------------------------
@@ -314,7 +396,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
 // (the G heads of one token), so Q is loaded and O stored in whole rows,
 // half a head_dim at a time, through a private 32 x D/2 LDS staging tile that
 // converts between that layout and the MFMA register layout.
-constexpr int kRingTiles = 7;
+constexpr int kRingTiles = 6;
 
 template <int D, int G>
 __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p) {
@@ -355,23 +437,38 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
 
   auto kt_lo = [&](int blk) { return max(0, p.q_offset + blk * TB - W + 1) / KT; };
   auto kt_hi = [&](int blk) { return (p.q_offset + min(blk * TB + TB, p.Sq) - 1) / KT; };
-  auto row_off = [&](int tw0, int m) {  // rows past Sq read row Sq-1's token (never stored)
-    return qoff + (long)min(tw0 + m / G, p.Sq - 1) * q_tok + (long)(m % G) * D;
+
+  // A wave's Q (or O) rows through a buffer resource over its TW tokens x G
+  // heads: one 16-byte load instruction covers RPI rows (TPI tokens), lane l
+  // taking row l / HC, chunk l % HC; tokens at or past Sq read zeros (their
+  // outputs are never stored) and their stores are dropped.
+  constexpr int RPI = 64 / HC;
+  static_assert(RPI % G == 0, "a load instruction must cover whole tokens");
+  constexpr int TPI = RPI / G;
+  const uint32_t row_voff =
+      (uint32_t)((((lane / HC) / G) * q_tok + ((lane / HC) % G) * D + (lane % HC) * 8) * 2);
+  auto rows_rsrc = [&](const uint16_t* base, int tw0) {
+    const int ntok = min(TW, p.Sq - tw0);
+    const uint32_t bytes = ntok > 0 ? (uint32_t)(((ntok - 1) * q_tok + G * D) * 2) : 0u;
+    return make_rsrc(base + qoff + (long)tw0 * q_tok, bytes);
   };
+  // Every offset goes into the per-lane voffset: the buffer range check
+  // ignores soffset, and a register soffset also makes the compiler drop the
+  // wait state that protects a 16-byte store's data registers from the next
+  // vector-ALU write.
+  auto rows_voff = [&](int it, int hh) { return row_voff + (uint32_t)((it * TPI * q_tok + hh * HD) * 2); };
 
   // Q of a block in whole-row layout: chunk u = it*64 + lane of half hh is
   // row u / HC, 16-byte chunk u % HC of that half.
   u32x4 qpre[2][SIT];
   auto load_q_rows = [&](int tw0) {
+    const rsrc_t r = rows_rsrc(p.q, tw0);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int it = 0; it < SIT; ++it) {
-        const int u = it * 64 + lane;
-        qpre[hh][it] = *(const u32x4*)(p.q + row_off(tw0, u / HC) + hh * HD + (u % HC) * 8);
-      }
+      for (int it = 0; it < SIT; ++it) qpre[hh][it] = buf_load16(r, rows_voff(it, hh), 0);
   };
-  QState<D, 1> st;
+  QState<D> st;
   // whole rows -> LDS -> MFMA B-operand layout (row col, d = 16c + 8*half)
   auto stage_q = [&]() {
 #pragma unroll
@@ -385,13 +482,14 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
       const lds_u16* sbase = lane_base(lds_addr(stg), Stg::k_lane_off(lane));
 #pragma unroll
       for (int c = 0; c < Gm::NC / 2; ++c)
-        st.q[0][hh * (Gm::NC / 2) + c] = Stg::k_operand(sbase, c);
+        st.q[hh * (Gm::NC / 2) + c] = Stg::k_operand(sbase, c);
       wave_lds_sync();
     }
   };
   // O = acc / l: MFMA layout -> LDS -> whole rows, half a head at a time
   auto store_o_rows = [&](int tw0) {
-    const float lt = st.l_run[0] + swap_halves(st.l_run[0]);
+    const rsrc_t orsrc = rows_rsrc(p.o, tw0);
+    const float lt = halves_sum(st.l_run);
     const float inv = 1.0f / lt;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -400,8 +498,8 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
         const int db = hh * (Gm::ND / 2) + db2;
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 y = {st.acc[0][db][4 * a4] * inv, st.acc[0][db][4 * a4 + 1] * inv,
-                           st.acc[0][db][4 * a4 + 2] * inv, st.acc[0][db][4 * a4 + 3] * inv};
+          const f32x4 y = {st.acc[db][4 * a4] * inv, st.acc[db][4 * a4 + 1] * inv,
+                           st.acc[db][4 * a4 + 2] * inv, st.acc[db][4 * a4 + 3] * inv};
           *(bf16x4*)&stg[Stg::off(col, 32 * db2 + 8 * a4 + 4 * half)] = __builtin_convertvector(y, bf16x4);
         }
       }
@@ -409,16 +507,14 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
 #pragma unroll
       for (int it = 0; it < SIT; ++it) {
         const int u = it * 64 + lane;
-        const int m = u / HC;
-        if (tw0 + m / G < p.Sq)
-          *(u32x4*)(p.o + qoff + (long)(tw0 + m / G) * q_tok + (long)(m % G) * D + hh * HD + (u % HC) * 8) =
-              *(const u32x4*)&stg[Stg::off(m, (u % HC) * 8)];
+        buf_store16(*(const u32x4*)&stg[Stg::off(u / HC, (u % HC) * 8)], orsrc, rows_voff(it, hh), 0);
       }
       wave_lds_sync();
     }
   };
 
   Stager<D, NT> sg;
+  sg.init(kv_tok, tid);
   const float sink2 = p.sinks ? p.sinks[g * G + col % G] * kLog2e : kNegInf;
 
   // prologue: the first block's queries and its whole window
@@ -445,18 +541,25 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
     if (have_new) sg.load(kg, vg, kv_tok, new_kt * KT, p.Sk, tid);
 
     // compute this block from the ring
-    st.qpos[0] = p.q_offset + tw0 + col / G;
+    st.qpos = p.q_offset + tw0 + col / G;
     st.reset(sink2, half);
     const bool wave_active = tw0 < p.Sq;
     if (wave_active) {
       const int wpos_lo = p.q_offset + tw0;
       const int wpos_hi = p.q_offset + min(tw0 + TW, p.Sq) - 1;
-      const int k1 = kt_hi(blk);
-      for (int kt = kt_lo(blk); kt <= k1; ++kt) {
-        int mask;
-        if (tile_needed(kt * KT, wpos_lo, wpos_hi, W, mask))
-          st.attend(k_ring[kt % NR], v_ring[kt % NR], kt * KT, mask, W, p.scale_log2, lane);
+      // this wave's tiles, all resident in the ring; the scores of tile
+      // kt + 1 are computed while tile kt is exponentiated
+      const int wk0 = max(0, wpos_lo - W + 1) / KT, wk1 = wpos_hi / KT;
+      f32x16 s = st.scores(k_ring[wk0 % NR], lane);
+      int mask;
+      for (int kt = wk0; kt < wk1; ++kt) {
+        tile_needed(kt * KT, wpos_lo, wpos_hi, W, mask);
+        const float mu = st.prep(s, kt * KT, mask, W, p.scale_log2, half);
+        s = st.template fold<true>(s, mu, p.scale_log2, v_ring[kt % NR], k_ring[(kt + 1) % NR], lane);
       }
+      tile_needed(wk1 * KT, wpos_lo, wpos_hi, W, mask);
+      const float mu = st.prep(s, wk1 * KT, mask, W, p.scale_log2, half);
+      st.template fold<false>(s, mu, p.scale_log2, v_ring[wk1 % NR], nullptr, lane);
       store_o_rows(tw0);
     }
     // the new tile's slot held tile new_kt - NR, older than this block's window
@@ -470,15 +573,15 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
 }
 
 // ----------------------------------------------------------------------------
-template <int D, int G, int NB, int NW>
+template <int D, int G, int NW>
 static hipError_t launch_generic(const PrefillArgs& a0, hipStream_t stream) {
   PrefillArgs a = a0;
-  constexpr int TB = (32 * NB / G) * NW;
+  constexpr int TB = (32 / G) * NW;
   a.n_tb = (a.Sq + TB - 1) / TB;
   a.total = a.B * a.Hkv * a.n_tb;
   a.per_xcd = (a.total + 7) / 8;
   dim3 grid(8 * a.per_xcd), block(NW * 64);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NB, NW>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -496,11 +599,17 @@ static hipError_t launch_strip(const PrefillArgs& a0, int num_cu, hipStream_t st
   return hipGetLastError();
 }
 
+static int floor_div(int x, int y) { return x >= 0 ? x / y : -((-x + y - 1) / y); }
+
 template <int D>
 static hipError_t launch_d(const PrefillArgs& a, int G, hipStream_t s) {
-  // the strip kernel's ring must hold a block's window (at most
-  // floor((W + 30) / 32) + 2 tiles) plus the next block's new tile
-  const bool ring_fits = a.window > 0 && (a.window + 30) / KT + 2 + 1 <= kRingTiles;
+  // The strip kernel's ring must hold a block's window plus the next block's
+  // new tile.  Blocks start at positions p = q_offset (mod 32), and the keys
+  // p - W + 1 .. p + 31 of a block span floor((a + 31) / 32) -
+  // floor((a - W + 1) / 32) + 1 tiles with a = q_offset mod 32.
+  const int al = a.q_offset % KT;
+  const int span = a.window > 0 ? (al + KT - 1) / KT - floor_div(al - a.window + 1, KT) + 1 : 0;
+  const bool ring_fits = a.window > 0 && span + 1 <= kRingTiles;
   if (ring_fits && (G == 8 || G == 4)) {
     int dev = 0, num_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -510,12 +619,12 @@ static hipError_t launch_d(const PrefillArgs& a, int G, hipStream_t s) {
     return G == 8 ? launch_strip<D, 8>(a, num_cu, s) : launch_strip<D, 4>(a, num_cu, s);
   }
   switch (G) {
-    case 1: return launch_generic<D, 1, 1, 8>(a, s);
-    case 2: return launch_generic<D, 2, 1, 8>(a, s);
-    case 4: return launch_generic<D, 4, 1, 8>(a, s);
-    case 8: return launch_generic<D, 8, 1, 8>(a, s);
-    case 16: return launch_generic<D, 16, 1, 8>(a, s);
-    case 32: return launch_generic<D, 32, 1, 8>(a, s);
+    case 1: return launch_generic<D, 1, 8>(a, s);
+    case 2: return launch_generic<D, 2, 8>(a, s);
+    case 4: return launch_generic<D, 4, 8>(a, s);
+    case 8: return launch_generic<D, 8, 8>(a, s);
+    case 16: return launch_generic<D, 16, 8>(a, s);
+    case 32: return launch_generic<D, 32, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

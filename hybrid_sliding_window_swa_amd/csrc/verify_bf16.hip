@@ -205,7 +205,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         sc[nb][v] = x;
         mx = fmaxf(mx, x);
       }
-      mx = fmaxf(mx, swap_halves(mx));
+      mx = halves_max(mx);
       const float m_new = fmaxf(m_run[nb], mx);
       const bool need = m_new > m_run[nb] + kRescaleTau;
       if (wave_any(need)) {
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // ---- merge the waves: common max, then a fixed-order pairwise sum in LDS
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const float lt = l_run[nb] + swap_halves(l_run[nb]);
+    const float lt = halves_sum(l_run[nb]);
     if (half == 0) {
       lds_m[wv][nb * 32 + col] = m_run[nb];
       lds_l[wv][nb * 32 + col] = lt;

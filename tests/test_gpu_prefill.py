@@ -99,6 +99,26 @@ def test_prefill_chunked_equals_oracle():
         assert_close(o, ref[:, c0:c0 + 160], BF16_TOL, f"chunk {c0}")
 
 
+@pytest.mark.parametrize("D,S", [(64, 300), (64, 301), (128, 301)])
+def test_prefill_repeated_calls_stable(D, S):
+    """Many calls of the sliding-window kernel against one oracle result.
+
+    Guards the output path of the strip kernel: a 16-byte store whose data
+    registers are rewritten too early corrupts a few lanes only now and then,
+    so one call is not enough to see it.  S = 301 leaves a partial wave."""
+    dev = device()
+    m = swa()
+    cfg = _cfg(f"repeat_d{D}_s{S}", 2, S, 16, 2, D, 128, "bf16")
+    q, k, v, sinks = prefill_inputs(cfg)
+    ref = oracle.prefill(q, k, v, sinks, cfg.window, 0, cfg.scale)
+    qd, kd, vd, sd = q.to(dev), k.to(dev), v.to(dev), sinks.to(dev)
+    for rep in range(60):
+        out = torch.full_like(qd, float("nan"))
+        m.swa_attn_prefill(qd, kd, vd, sd, cfg.window, 0, cfg.scale, out=out)
+        torch.cuda.synchronize()
+        assert_close(out, ref, BF16_TOL, f"{cfg.name} call {rep}")
+
+
 def test_prefill_deterministic():
     dev = device()
     m = swa()
