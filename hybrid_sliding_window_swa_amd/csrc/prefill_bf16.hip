@@ -36,7 +36,8 @@
 //   are already in flight, and the block's output is stored asynchronously,
 //   so HBM streams continuously.
 // prefill_bf16_kernel (global attention and any other shape): one workgroup
-//   per token block, K tiles staged one ahead of V tiles, XCD-aware order with
+//   per token block, K/V tiles staged two at a time in a four-slot ring (K one
+//   tile ahead of V, one barrier per two tiles), XCD-aware order with
 //   the longest (latest) blocks first.
 #include "common.hpp"
 #include "launch.hpp"
@@ -127,6 +128,7 @@ struct QState {
   bf16x8 q[Gm::NC];
   int qpos;
   float m_run, l_run;
+  float mu;  // exponent shift of the tile being folded
   f32x16 acc[Gm::ND];
 
   __device__ __forceinline__ void load_q(const uint16_t* qbase, long q_tok, int tw0, int G, int g,
@@ -165,11 +167,11 @@ struct QState {
     return s;
   }
 
-  // Causal / window mask of the tile starting at key kb, the row max and the
-  // lazy rescale; returns the shift of the exponents.  mask: kMaskHi if some
-  // key of the tile lies after some query of the wave, kMaskLo if some key
-  // lies below some query's window, kMaskAll to drop the whole tile.
-  __device__ __forceinline__ float prep(f32x16& s, int kb, int mask, int window, float c2, int half) {
+  // Causal / window mask of the tile starting at key kb (masked scores ->
+  // -inf).  mask: kMaskHi if some key of the tile lies after some query of
+  // the wave, kMaskLo if some key lies below some query's window, kMaskAll to
+  // drop the whole tile.
+  __device__ __forceinline__ void apply_mask(f32x16& s, int kb, int mask, int window, int half) const {
     if (mask == kMaskAll) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[v] = kNegInf;
@@ -190,12 +192,13 @@ struct QState {
         for (int v = 0; v < 16; ++v) s[v] = (c_row(v, 0) <= a && c_row(v, 0) >= alo) ? s[v] : kNegInf;
       }
     }
-    // raw-score max (scale > 0 commutes with max)
-    float mx = kNegInf;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) mx = __builtin_fmaxf(mx, s[v]);
+  }
+
+  // Lazy rescale from the raw-score maximum mx of this lane's scores of a
+  // tile (scale > 0 commutes with max), then the exponent shift mu.
+  __device__ __forceinline__ void update_max(float mx, float c2) {
     mx = halves_max(mx) * c2;
-    const float m_new = __builtin_fmaxf(m_run, mx);
+    const float m_new = __builtin_elementwise_maximum(m_run, mx);
     const bool need = m_new > m_run + kRescaleTau;
     if (wave_any(need)) {
       const float alpha = need ? exp2_fast(m_run - m_new) : 1.0f;
@@ -204,54 +207,98 @@ struct QState {
 #pragma unroll
       for (int db = 0; db < Gm::ND; ++db) acc[db] *= alpha;
     }
-    return m_run == kNegInf ? 0.0f : m_run;
+    mu = m_run == kNegInf ? 0.0f : m_run;
+  }
+
+  // Mask, row max and lazy rescale of a tile folded without a predecessor.
+  __device__ __forceinline__ void prep(f32x16& s, int kb, int mask, int window, float c2, int half) {
+    apply_mask(s, kb, mask, window, half);
+    float mx = kNegInf;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = __builtin_elementwise_maximum(mx, s[v]);
+    update_max(mx, c2);
   }
 
   // P = exp2(s*c2 - mu) rounded to bf16, l += sum P, O^T += V^T P^T for the V
-  // tile v_t.  With NEXT the raw scores of the K tile k_next are computed in
-  // the same instruction stream and returned: each of its MFMAs is followed
-  // by a share of the exponentials (scheduling fences keep that order), so
-  // the matrix core and the vector ALU of the SIMD work at the same time.
+  // tile v_t.  With NEXT the scores of the K tile k_next (first key kb_next)
+  // are computed in the same instruction stream, masked, reduced to their
+  // row max and folded into the running max (so mu is ready for them) and
+  // returned.  Each score MFMA is followed by a share of the exponentials,
+  // each P V MFMA by a share of the row sums and of the next row max
+  // (scheduling fences keep that order), so the matrix core and the vector
+  // ALU of the SIMD work at the same time.
   template <bool NEXT>
-  __device__ __forceinline__ f32x16 fold(const f32x16& s, float mu, float c2, const uint16_t* v_t,
-                                         const uint16_t* k_next, int lane) {
+  __device__ __forceinline__ f32x16 fold(const f32x16& s, float c2, const uint16_t* v_t,
+                                         const uint16_t* k_next, int kb_next, int mask_next,
+                                         int window, int half, int lane) {
     constexpr int EPM = 16 / Gm::NC;  // exponentials per score MFMA
     const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
     f32x16 sn = {};
     bf16x8 pb[2];
-    bf16x8 va[Gm::ND];
+    bf16x8 va[2][Gm::ND];
     if constexpr (NEXT) {
       const lds_u16* kbase = lane_base(lds_addr(k_next), KTile<D>::k_lane_off(lane));
       bf16x8 ka[Gm::NC];
 #pragma unroll
       for (int c = 0; c < Gm::NC; ++c) ka[c] = KTile<D>::k_operand(kbase, c);
 #pragma unroll
-      for (int db = 0; db < Gm::ND; ++db) va[db] = VTile<D>::vt_operand(vbase, db, 0);
+      for (int db = 0; db < Gm::ND; ++db) va[0][db] = VTile<D>::vt_operand(vbase, db, 0);
       __builtin_amdgcn_sched_barrier(0);
+      // the packed weights pass through an empty asm so that the
+      // exponentials stay next to their MFMA instead of sinking to the use
+      uint32_t pw[8];
 #pragma unroll
       for (int c = 0; c < Gm::NC; ++c) {
         sn = mfma32(ka[c], q[c], sn);
 #pragma unroll
-        for (int e = 0; e < EPM; ++e) {
+        for (int e = 0; e < EPM; e += 2) {
           const int v = c * EPM + e;
-          pb[v >> 3][v & 7] = (__bf16)exp2_fast(fmaf(s[v], c2, -mu));
+          const bf16x2 w2 = {(__bf16)exp2_fast(fmaf(s[v], c2, -mu)), (__bf16)exp2_fast(fmaf(s[v + 1], c2, -mu))};
+          uint32_t w = __builtin_bit_cast(uint32_t, w2);
+          __asm__ volatile("" : "+v"(w));
+          pw[v >> 1] = w;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      pb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+      apply_mask(sn, kb_next, mask_next, window, half);
+      // O^T += V^T P^T (keys 16kc .. 16kc+15 per MFMA) with the row sums of
+      // P and the row max of the next scores in between; the second key half
+      // of V is read while the first is multiplied
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db) va[1][db] = VTile<D>::vt_operand(vbase, db, 1);
+      float mx = kNegInf;
+      constexpr int NPV = 2 * Gm::ND;
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int kc = i / Gm::ND, db = i % Gm::ND;
+        acc[db] = mfma32(va[kc][db], pb[kc], acc[db]);
+#pragma unroll
+        for (int j = i * 8 / NPV; j < (i + 1) * 8 / NPV; ++j) {
+          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+          const bf16x8& pv = pb[j >> 2];
+          const int e = 2 * (j & 3);
+          const bf16x2 pair = {pv[e], pv[e + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, one, l_run, false);
+          mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sn[2 * j], sn[2 * j + 1]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      update_max(mx, c2);
     } else {
 #pragma unroll
-      for (int db = 0; db < Gm::ND; ++db) va[db] = VTile<D>::vt_operand(vbase, db, 0);
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < Gm::ND; ++db) va[kc][db] = VTile<D>::vt_operand(vbase, db, kc);
 #pragma unroll
       for (int v = 0; v < 16; ++v) pb[v >> 3][v & 7] = (__bf16)exp2_fast(fmaf(s[v], c2, -mu));
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < Gm::ND; ++db) acc[db] = mfma32(va[kc][db], pb[kc], acc[db]);
+      l_run = sum_bf16x16(pb[0], pb[1], l_run);
     }
-    // O^T += V^T P^T: keys 16kc .. 16kc+15 per MFMA
-#pragma unroll
-    for (int db = 0; db < Gm::ND; ++db) acc[db] = mfma32(va[db], pb[0], acc[db]);
-#pragma unroll
-    for (int db = 0; db < Gm::ND; ++db) va[db] = VTile<D>::vt_operand(vbase, db, 1);
-#pragma unroll
-    for (int db = 0; db < Gm::ND; ++db) acc[db] = mfma32(va[db], pb[1], acc[db]);
-    l_run = sum_bf16x16(pb[0], pb[1], l_run);
     return sn;
   }
 
@@ -290,9 +337,8 @@ __device__ __forceinline__ bool tile_needed(int kb, int wpos_lo, int wpos_hi, in
 
 // ----------------------------------------------------------------------------
 // One workgroup per block of TB tokens (global attention and general shapes).
-// K tiles are staged one tile ahead of V tiles (three K slots, two V slots),
-// so while a wave exponentiates tile kt it already computes the scores of
-// tile kt + 1.
+// K tiles are staged one tile ahead of V tiles, so while a wave
+// exponentiates tile kt it already computes the scores of tile kt + 1.
 template <int D, int G, int NW>
 __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   using Gm = TileGeom<D>;
@@ -301,8 +347,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   constexpr int TB = TW * NW;       // tokens per workgroup
   static_assert(32 % G == 0, "a 32-row block must hold whole tokens");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[3][Gm::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][Gm::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[4][Gm::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[4][Gm::V_ELEMS];
 
   // XCD-aware work item: workgroups on one XCD (blockIdx % 8) take consecutive
   // token blocks of one (b, g), latest (longest) first.
@@ -339,53 +385,79 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   const int wk0 = max(kt_begin, (W > 0 ? max(0, wpos_lo - W + 1) : 0) / KT);
   const int wk1 = tw0 < p.Sq ? wpos_hi / KT : -1;
 
-  Stager<D, NT> sg;
-  sg.init(kv_tok, tid);
-  sg.load(kg, vg, kv_tok, kt_begin * KT, p.Sk, tid);
-  sg.store(k_lds[0], v_lds[0], tid);
-  if (kt_begin < kt_end) {
-    sg.load_k(kg, kv_tok, (kt_begin + 1) * KT, p.Sk, tid);
-    sg.store_k(k_lds[1], tid);
-  }
+  // Tile t lives in K slot and V slot (t - kt_begin) % 4.  A step over two
+  // tiles kt, kt + 1 reads K(kt + 1), K(kt + 2), V(kt), V(kt + 1) and stages
+  // K(kt + 3), K(kt + 4), V(kt + 2), V(kt + 3); one barrier per two tiles.
+  Stager<D, NT> s0, s1;
+  s0.init(kv_tok, tid);
+  s1.init(kv_tok, tid);
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (kt_begin + i <= kt_end) {
+      s0.load_k(kg, kv_tok, (kt_begin + i) * KT, p.Sk, tid);
+      s0.store_k(k_lds[i], tid);
+    }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (kt_begin + i <= kt_end) {
+      s0.load_v(vg, kv_tok, (kt_begin + i) * KT, p.Sk, tid);
+      s0.store_v(v_lds[i], tid);
+    }
   // Drain the prologue loads (queries, first tiles): inside the loop the only
   // loads in flight are then the prefetches, and no wait for the queries can
   // stall on them.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // One code path per iteration: a wave inside its range folds tile kt and
+  // One code path per tile: a wave inside its range folds tile kt and
   // computes the scores of tile kt + 1 (discarded after its last tile); in
-  // the iteration before its first tile it folds a fully masked tile, which
-  // adds nothing, to get those scores.  The last tile of the workgroup is
-  // folded after the loop.
-  f32x16 s = {};
-  if (wk0 == kt_begin && wk1 >= 0) s = st.scores(k_lds[0], lane);
-  int ks0 = 0, ks1 = 1, ks2 = 2;  // K slots of tiles kt, kt + 1, kt + 2
-  int vs = 0;                      // V slot of tile kt
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const bool more_k = kt + 2 <= kt_end;
-    if (more_k) sg.load_k(kg, kv_tok, (kt + 2) * KT, p.Sk, tid);
-    sg.load_v(vg, kv_tok, (kt + 1) * KT, p.Sk, tid);
-    if (kt + 1 >= wk0 && kt <= wk1) {
-      int mask;
-      tile_needed(kt * KT, wpos_lo, wpos_hi, W, mask);
-      if (kt < wk0) mask = kMaskAll;
-      const float mu = st.prep(s, kt * KT, mask, W, c2, half);
-      s = st.template fold<true>(s, mu, c2, v_lds[vs], k_lds[ks1], lane);
-    }
-    if (more_k) sg.store_k(k_lds[ks2], tid);
-    sg.store_v(v_lds[vs ^ 1], tid);
-    __syncthreads();
-    const int t = ks0;
-    ks0 = ks1; ks1 = ks2; ks2 = t;
-    vs ^= 1;
-  }
-  if (kt_end >= wk0 && kt_end <= wk1) {
+  // the step before its first tile it folds a fully masked tile, which adds
+  // nothing, to get those scores.  The last tile of the workgroup is folded
+  // after the loop.
+  auto tile_mask = [&](int kt) {  // kMaskAll before this wave's first tile
     int mask;
-    tile_needed(kt_end * KT, wpos_lo, wpos_hi, W, mask);
-    const float mu = st.prep(s, kt_end * KT, mask, W, c2, half);
-    st.template fold<false>(s, mu, c2, v_lds[vs], nullptr, lane);
+    tile_needed(kt * KT, wpos_lo, wpos_hi, W, mask);
+    return kt < wk0 ? kMaskAll : mask;
+  };
+  f32x16 s = {};
+  if (wk0 == kt_begin && wk1 >= 0) {
+    s = st.scores(k_lds[0], lane);
+    st.prep(s, kt_begin * KT, tile_mask(kt_begin), W, c2, half);
   }
+  auto fold_step = [&](int kt) {
+    if (kt + 1 >= wk0 && kt <= wk1) {
+      const int r = kt - kt_begin;
+      if (kt + 1 == wk0) st.prep(s, kt * KT, kMaskAll, W, c2, half);
+      s = st.template fold<true>(s, c2, v_lds[r & 3], k_lds[(r + 1) & 3], (kt + 1) * KT, tile_mask(kt + 1), W,
+                                 half, lane);
+    }
+  };
+  int kt = kt_begin;
+  if ((kt_end - kt_begin) & 1) {  // a single step first, so that pairs remain
+    if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, p.Sk, tid);
+    if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, p.Sk, tid);
+    fold_step(kt);
+    if (kt + 3 <= kt_end) s0.store_k(k_lds[3], tid);
+    if (kt + 2 <= kt_end) s0.store_v(v_lds[2], tid);
+    __syncthreads();
+    ++kt;
+  }
+  for (; kt < kt_end; kt += 2) {
+    const int r = kt - kt_begin;
+    if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, p.Sk, tid);
+    if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, p.Sk, tid);
+    if (kt + 4 <= kt_end) s1.load_k(kg, kv_tok, (kt + 4) * KT, p.Sk, tid);
+    if (kt + 3 <= kt_end) s1.load_v(vg, kv_tok, (kt + 3) * KT, p.Sk, tid);
+    fold_step(kt);
+    fold_step(kt + 1);
+    if (kt + 3 <= kt_end) s0.store_k(k_lds[(r + 3) & 3], tid);
+    if (kt + 2 <= kt_end) s0.store_v(v_lds[(r + 2) & 3], tid);
+    if (kt + 4 <= kt_end) s1.store_k(k_lds[r & 3], tid);
+    if (kt + 3 <= kt_end) s1.store_v(v_lds[(r + 3) & 3], tid);
+    __syncthreads();
+  }
+  if (kt_end >= wk0 && kt_end <= wk1)
+    st.template fold<false>(s, c2, v_lds[(kt_end - kt_begin) & 3], nullptr, 0, 0, W, half, lane);
   if (wk1 >= 0) st.store_o(p.o + qoff, q_tok, tw0, G, g, p.Sq, col, half);
 }
 
@@ -550,16 +622,17 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
       // this wave's tiles, all resident in the ring; the scores of tile
       // kt + 1 are computed while tile kt is exponentiated
       const int wk0 = max(0, wpos_lo - W + 1) / KT, wk1 = wpos_hi / KT;
-      f32x16 s = st.scores(k_ring[wk0 % NR], lane);
-      int mask;
-      for (int kt = wk0; kt < wk1; ++kt) {
+      auto tile_mask = [&](int kt) {
+        int mask;
         tile_needed(kt * KT, wpos_lo, wpos_hi, W, mask);
-        const float mu = st.prep(s, kt * KT, mask, W, p.scale_log2, half);
-        s = st.template fold<true>(s, mu, p.scale_log2, v_ring[kt % NR], k_ring[(kt + 1) % NR], lane);
-      }
-      tile_needed(wk1 * KT, wpos_lo, wpos_hi, W, mask);
-      const float mu = st.prep(s, wk1 * KT, mask, W, p.scale_log2, half);
-      st.template fold<false>(s, mu, p.scale_log2, v_ring[wk1 % NR], nullptr, lane);
+        return mask;
+      };
+      f32x16 s = st.scores(k_ring[wk0 % NR], lane);
+      st.prep(s, wk0 * KT, tile_mask(wk0), W, p.scale_log2, half);
+      for (int kt = wk0; kt < wk1; ++kt)
+        s = st.template fold<true>(s, p.scale_log2, v_ring[kt % NR], k_ring[(kt + 1) % NR], (kt + 1) * KT,
+                                   tile_mask(kt + 1), W, half, lane);
+      st.template fold<false>(s, p.scale_log2, v_ring[wk1 % NR], nullptr, 0, 0, W, half, lane);
       store_o_rows(tw0);
     }
     // the new tile's slot held tile new_kt - NR, older than this block's window
