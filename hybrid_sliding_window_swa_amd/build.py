@@ -4,7 +4,8 @@
 
 Every source is compiled on each call (the build is the "does it compile"
 check); objects go to ``_build/`` next to this file and the shared library
-to ``libswa_attn.so`` beside it.
+to ``libswa_attn.so`` beside it.  The same call builds ``swa_peaks``, a small
+program that measures the HBM and MFMA ceilings the kernels are compared with.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswa_attn.so")
+PEAKS = os.path.join(PKG, "swa_peaks")
 ARCH = os.environ.get("SWA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "validate.c", "prefill_bf16.hip", "verify_bf16.hip", "fp32_kernels.hip", "append.hip"]
@@ -39,19 +41,32 @@ def _compile(src: str) -> str:
         cmd = [hipcc(), "-x", "c", "-std=c99", "-O2", "-fPIC", "-fvisibility=hidden", "-Wall", "-I", INCLUDE, "-I", CSRC,
                "-c", path, "-o", obj]
     else:
-        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-               "-I", INCLUDE, "-I", CSRC, "-c", path, "-o", obj]
+        cmd = [hipcc(), *HIP_FLAGS, "-fPIC", "-fvisibility=hidden", "-I", INCLUDE, "-I", CSRC, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
+HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build_peaks() -> str:
+    cmd = [hipcc(), *HIP_FLAGS, os.path.join(CSRC, "peaks.hip"), "-o", PEAKS + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile of peaks.hip failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(PEAKS + ".tmp", PEAKS)
+    return PEAKS
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        peaks = ex.submit(build_peaks)
         objs = list(ex.map(_compile, SOURCES))
+        peaks.result()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,7 +74,7 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PEAKS)
     return LIB
 
 

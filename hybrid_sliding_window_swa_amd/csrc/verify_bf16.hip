@@ -15,12 +15,16 @@
 //     tiles w, w + NW, ... (32 rows each) and keeps its own online-softmax
 //     state for the 32*NB query rows; the waves are merged through LDS at
 //     the end, in a fixed order (bitwise deterministic).
-//   * K rows go straight from HBM into MFMA A-operand registers (S^T = K Q^T);
-//     V rows are written transposed into a per-wave LDS tile to serve as the A
-//     operand of O^T += V^T P^T.  The next tile's loads are issued before the
-//     current tile is computed.
-//   * Rows past the end of the valid cache range are never loaded (zero-
-//     filled), so unused cache slots may hold anything, NaN included.
+//   * Split workgroups run longest first: all full splits, then each
+//     request's partial split by decreasing length, so the tail is short.
+//   * K and V tiles are staged row-major in a per-wave LDS tile (coalesced
+//     16-byte loads of whole rows); K is read back as the MFMA A operand of
+//     S^T = K Q^T, V with ds_read_b64_tr_b16 as the A operand of
+//     O^T += V^T P^T.  The next tile's loads are issued before the current
+//     tile is computed.
+//   * Rows past the end of the valid cache range are clamped to the last
+//     valid row and masked out, so unused cache slots are never read and may
+//     hold anything, NaN included.
 //   * With one split per (request, KV head) the workgroup folds the sink and
 //     writes O directly; otherwise it writes (max, sum, unnormalised O) to the
 //     workspace and verify_combine merges the splits, folding the sink once.
@@ -50,6 +54,73 @@ __device__ __forceinline__ SplitRange split_range(const VerifyArgs& p, int L) {
   return r;
 }
 
+// Longest-first order of the split workgroups: every full split (split_len
+// rows) first, then the one partial split of each request by decreasing size,
+// KV head innermost.  Workgroups start in linear-id order, so the short work
+// runs last and the tail stays short.  Every wave derives the order from
+// cache_len (requests b = lane + 64c); returns false when linear id i has no
+// work.  Used for up to kLptMaxB requests.
+constexpr int kLptMaxB = 256;
+
+__device__ bool lpt_item(const VerifyArgs& p, int i, int lane, int& b, int& g, int& s) {
+  constexpr int CH = kLptMaxB / 64;
+  int nfull[CH], rem[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int bb = c * 64 + lane;
+    nfull[c] = 0;
+    rem[c] = -1;  // -1: no partial split
+    if (bb < p.B) {
+      const SplitRange sr = split_range(p, p.cache_len[bb]);
+      nfull[c] = sr.ncache / p.split_len;
+      const int rm = sr.ncache - nfull[c] * p.split_len;
+      if (rm > 0 || sr.ncache == 0) rem[c] = rm;
+    }
+  }
+  // full splits, in request order
+  int acc = 0;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if (c * 64 >= p.B) break;
+    for (int l = 0; l < 64 && c * 64 + l < p.B; ++l) {
+      const int n = __builtin_amdgcn_readlane(nfull[c], l) * p.Hkv;
+      if (i < acc + n) {
+        b = c * 64 + l;
+        s = (i - acc) / p.Hkv;
+        g = (i - acc) % p.Hkv;
+        return true;
+      }
+      acc += n;
+    }
+  }
+  // partial splits: this lane's requests ranked by (size desc, index asc)
+  const int j = i - acc;
+  const int target = j / p.Hkv;
+  g = j % p.Hkv;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    if (c * 64 >= p.B) break;
+    int rank = 0;
+#pragma unroll
+    for (int c2 = 0; c2 < CH; ++c2) {
+      if (c2 * 64 >= p.B) break;
+      for (int l = 0; l < 64 && c2 * 64 + l < p.B; ++l) {
+        const int r2 = __builtin_amdgcn_readlane(rem[c2], l);
+        const int b2 = c2 * 64 + l;
+        rank += (r2 > rem[c] || (r2 == rem[c] && b2 < c * 64 + lane)) ? 1 : 0;
+      }
+    }
+    const uint64_t hit = __ballot(rem[c] >= 0 && rank == target);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      b = c * 64 + l;
+      s = __builtin_amdgcn_readlane(nfull[c], l);
+      return true;
+    }
+  }
+  return false;
+}
+
 }  // namespace
 
 template <int D, int NB, int NW, bool DIRECT>
@@ -77,7 +148,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // linear id, so with (request, KV head) as the fastest dimension every XCD
   // gets the same mix of long and short requests (with 8 KV heads, XCD = KV
   // head); splits past a request's length exit at once.
-  const int g = blockIdx.x % p.Hkv, b = blockIdx.x / p.Hkv, s = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  int g, b, s;
+  if (DIRECT || p.B > kLptMaxB) {
+    g = blockIdx.x % p.Hkv;
+    b = blockIdx.x / p.Hkv;
+    s = blockIdx.y;
+  } else if (!lpt_item(p, blockIdx.x + blockIdx.y * gridDim.x, lane, b, g, s)) {
+    return;
+  }
   const int L = p.cache_len[b];
   const SplitRange sr = split_range(p, L);
   if (s >= sr.ns) return;
@@ -88,7 +167,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const int G = p.Hq / p.Hkv;
   const int R = G * p.T;
-  const int tid = threadIdx.x, lane = tid & 63, wv = wave_index();
+  const int tid = threadIdx.x, wv = wave_index();
   const int half = lane >> 5, col = lane & 31;
   const long kv_tok = (long)p.Hkv * D;
   // ring: slot of the oldest committed position held, to map slot -> position
@@ -373,11 +452,12 @@ VerifyPlan plan_verify_bf16(int B, int T, int Hq, int Hkv, int D, int slots, int
   long max_rows = slots;
   if (!ring && window > 0 && window - 1 < max_rows) max_rows = window - 1;
   if (max_rows < 1) max_rows = 1;
-  // aim for >= ~1024 workgroups, splits of at most 8192 rows (measured best on
-  // the 64-request global-cache verify: fewer partials, short enough tail)
+  // aim for >= ~1024 workgroups, splits of at most 16384 rows (measured best
+  // on the 64-request global-cache verify with longest-first order: fewer
+  // workgroups and partials, and the short partial splits close the tail)
   long want = max_rows * (long)B * Hkv / 1024;
   long sl = unit;
-  while (sl < want && sl < 8192) sl *= 2;
+  while (sl < want && sl < 16384) sl *= 2;
   if (sl < unit) sl = unit;
   sl = (sl + unit - 1) / unit * unit;
   pl.split_len = (int)sl;

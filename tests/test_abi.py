@@ -113,9 +113,9 @@ def test_workspace_sizes(lib):
     assert ws(64, 4, 64, 8, 128, 65536, 0, 0, F32) == 0
     # invalid arguments -> 0
     assert ws(64, 4, 64, 8, 100, 65536, 0, 0, BF16) == 0
-    # global cache of 65536 rows: splits of <= 8192 rows, (D + 2) floats per row and split
+    # global cache of 65536 rows: splits of <= 16384 rows, (D + 2) floats per row and split
     b = ws(64, 4, 64, 8, 128, 65536, 0, 0, BF16)
-    assert b == 64 * 8 * 8 * 32 * 130 * 4
+    assert b == 64 * 8 * 4 * 32 * 130 * 4
     # one request of 262148 rows: splits of 2048 rows
     assert ws(1, 4, 64, 8, 128, 262148, 0, 0, BF16) == 1 * 8 * 129 * 32 * 130 * 4
 
