@@ -115,6 +115,26 @@ def time_launches(fn, steps, stream, before=None):
     return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
 
 
+def read_peaks():
+    """Ceilings measured on this GPU by swa_peaks (profiles/mi355x_peaks.txt),
+    or None when the file is absent."""
+    path = os.path.join(PROFILE_DIR, "mi355x_peaks.txt")
+    if not os.path.exists(path):
+        return None
+    out = {}
+    for line in open(path):
+        if line.startswith("{"):
+            d = json.loads(line)
+            if d["measure"] == "hbm_read":
+                out["hbm_read_GBs"] = d["GB/s"]
+            elif d["measure"] == "hbm_copy":
+                out["hbm_copy_GBs"] = d["GB/s"]
+            elif d["measure"].startswith("mfma_bf16"):
+                out["mfma_bf16_TFLOPs"] = d["TFLOP/s"]
+    out["source"] = "profiles/mi355x_peaks.txt (swa_peaks)"
+    return out
+
+
 def settle(fn, seconds):
     """Repeat fn() untimed for `seconds` of wall time so that the GPU clocks
     reach their sustained-load level before anything is timed."""
@@ -313,6 +333,20 @@ def main():
     if args.only is None and not args.no_verify:
         result["ga_prefill"] = run_ga(args, swa, torch, dev, stream)
         result["verify"] = run_verify(args, swa, torch, dev, stream)
+    peaks = read_peaks()
+    if peaks is not None:
+        # fractions of the ceilings measured on this GPU: the SWA prefill moves
+        # as many bytes out as in (copy-like), the verify reads, the global
+        # prefill is a contraction
+        result["measured_ceilings"] = peaks
+        result["roofline"]["frac_of_measured_copy"] = round(
+            result["roofline"]["achieved"] / peaks["hbm_copy_GBs"], 4)
+        if "verify" in result:
+            v = result["verify"]["roofline"]
+            v["frac_of_measured_read"] = round(v["achieved"] / peaks["hbm_read_GBs"], 4)
+        if "ga_prefill" in result:
+            gp = result["ga_prefill"]
+            gp["frac_of_measured_mfma"] = round(gp["TFLOP/s"] / peaks["mfma_bf16_TFLOPs"], 4)
     if args.only is None and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, *tensors, args.cpu_seconds)
     print(json.dumps(result), flush=True)
