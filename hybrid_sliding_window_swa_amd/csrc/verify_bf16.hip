@@ -124,7 +124,7 @@ __device__ bool lpt_item(const VerifyArgs& p, int i, int lane, int& b, int& g, i
 }  // namespace
 
 template <int D, int NB, int NW, bool DIRECT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_bf16_kernel(VerifyArgs p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1, NB == 1 ? 2 : 1))) void verify_bf16_kernel(VerifyArgs p) {
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
