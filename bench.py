@@ -9,7 +9,8 @@ the window; masked or skipped tile work is not counted), over K timed steps
 with inputs resident in HBM.  The same run also times the q_len=4 MTP verify
 on 64 requests (global-layer cache with contexts U[4096, 65536] and a
 128-slot SWA ring) and reports its HBM GB/s from algorithmic bytes (every
-K/V row the windows need read once, plus Q, the new rows and O).
+K/V row the windows need read once, plus Q, the new rows and O), and the
+same for a plain q_len=1 decode step on the same shapes.
 
 Prints ONE JSON line.  Inputs are seeded synthetic N(0,1) tensors rounded to
 bf16 (random numbers, no dataset).  --gpus above 1 is refused: this build
@@ -220,12 +221,13 @@ def run_ga(args, swa, torch, dev, stream):
     }
 
 
-def run_verify(args, swa, torch, dev, stream):
-    """Time the q_len=4 verify on the global-layer cache and the SWA ring."""
+def run_verify(args, swa, torch, dev, stream, names=("verify_ga_b64", "verify_swa_b64")):
+    """Time the q_len=4 verify (or, with the decode names, the q_len=1 decode)
+    on the global-layer cache and the SWA ring."""
     from swa_inputs import VERIFY_CONFIGS, verify_inputs
     vres = {}
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    for name in ("verify_ga_b64", "verify_swa_b64"):
+    for name in names:
         vc = VERIFY_CONFIGS[name]
         inp = verify_inputs(vc, device=dev)
         cl = inp["cache_len"].to(torch.int32).to(dev)
@@ -264,7 +266,9 @@ def run_verify(args, swa, torch, dev, stream):
         }
         del inp, ws, ov
         torch.cuda.empty_cache()
-    ga = vres["verify_ga_b64"]
+    ga = vres[names[0]]
+    if names[0].startswith("decode"):
+        return {"metric": "q_len=1 decode HBM GB/s", "value": ga["GB/s"], "unit": "GB/s", "workloads": vres}
     return {
         "metric": "q_len=4 verify-decode HBM GB/s",
         "value": ga["GB/s"], "unit": "GB/s", "workloads": vres,
@@ -333,6 +337,7 @@ def main():
     if args.only is None and not args.no_verify:
         result["ga_prefill"] = run_ga(args, swa, torch, dev, stream)
         result["verify"] = run_verify(args, swa, torch, dev, stream)
+        result["decode"] = run_verify(args, swa, torch, dev, stream, ("decode_ga_b64", "decode_swa_b64"))
     peaks = read_peaks()
     if peaks is not None:
         # fractions of the ceilings measured on this GPU: the SWA prefill moves

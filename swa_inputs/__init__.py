@@ -117,6 +117,12 @@ VERIFY_CONFIGS = {
     # global-layer verify of the 256K stack: one request, 262144 committed tokens
     "verify_ga_256k": VerifyConfig("verify_ga_256k", 1, 4, 64, 8, 128, 0, False, 262144 + 4,
                                    262144, 262144, "bf16", seed=5),
+    # plain single-token decode (q_len=1, also the MTP draft layers' step) on the
+    # same 64-request shapes: global-layer cache and 128-slot SWA ring
+    "decode_ga_b64": VerifyConfig("decode_ga_b64", 64, 1, 64, 8, 128, 0, False, 65536,
+                                  4096, 65536, "bf16", seed=6),
+    "decode_swa_b64": VerifyConfig("decode_swa_b64", 64, 1, 64, 8, 128, 128, True, 128,
+                                   4096, 65536, "bf16", seed=6),
 }
 
 

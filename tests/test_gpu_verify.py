@@ -206,6 +206,20 @@ def test_full_size_verify_swa_b64():
     _full_verify(cfg, range(cfg.B))
 
 
+def test_full_size_decode_ga_b64():
+    """q_len = 1 decode over the 64-request global cache (the verify entry point)."""
+    cfg = VERIFY_CONFIGS["decode_ga_b64"]
+    from swa_inputs import draw_lengths
+    L = draw_lengths(cfg.B, cfg.len_lo, cfg.len_hi, cfg.seed)
+    picks = sorted({int(L.argmin()), int(L.argmax()), 0, 31, cfg.B - 1})
+    _full_verify(cfg, picks)
+
+
+def test_full_size_decode_swa_b64():
+    cfg = VERIFY_CONFIGS["decode_swa_b64"]
+    _full_verify(cfg, range(cfg.B))
+
+
 def test_full_size_verify_ga_256k():
     cfg = VERIFY_CONFIGS["verify_ga_256k"]
     _full_verify(cfg, [0])
