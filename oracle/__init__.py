@@ -13,7 +13,10 @@ itself): torch's scaled-dot-product attention in fp64 with a sink column and
 with band / causal masks, closed forms for W=1 and for Q=0 with one-hot
 values, the sigmoid(LSE - sink) identity, weights + sink mass = 1, GQA vs
 repeated KV heads, verify vs successive single-token decodes and vs prefill
-rows, chunked vs unchunked prefill, and hand-derived golden values.
+rows, chunked vs unchunked prefill, and hand-derived golden values.  The
+greedy draft acceptance is pinned by hand-built cases (the release blog's
+accept, accept, reject, discard example among them), tie breaking and
+numpy's argmax.
 """
 from __future__ import annotations
 
@@ -59,6 +62,9 @@ def _bind(lib):
     lib.oracle_ring_append.argtypes = [c_u8, c_u8, c_u8, c_u8, c_i64, c_i64,
                                        i, i, i, i, l, i, i]
     lib.oracle_ring_append.restype = i
+    lib.oracle_greedy_accept.argtypes = [c_f, ctypes.POINTER(ctypes.c_int32), i, i, l,
+                                         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.oracle_greedy_accept.restype = i
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i
     return lib
@@ -222,3 +228,19 @@ def ring_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_n
                                    _p(cl, ctypes.c_int64), _p(na, ctypes.c_int64),
                                    B, T, Hkv, D, slots, int(bool(ring)), k_cache.dtype.itemsize)
     _check(rc, "ring_append")
+
+
+def greedy_accept(logits, draft):
+    """Greedy acceptance of drafts: logits [B,T,V] (any float dtype, upcast to
+    fp32), draft [B,T-1] int.  Returns (target [B,T] int32: argmax with the
+    lowest index among equal maxima, n_append [B] int32: 1 + accepted drafts)."""
+    lg = _f32(logits)
+    B, T, V = lg.shape
+    dr = np.ascontiguousarray(np.asarray(draft.cpu() if hasattr(draft, "cpu") else draft), dtype=np.int32)
+    assert dr.shape == (B, T - 1)
+    target = np.empty((B, T), dtype=np.int32)
+    n_append = np.empty((B,), dtype=np.int32)
+    rc = load().oracle_greedy_accept(_p(lg, ctypes.c_float), _p(dr, ctypes.c_int32), B, T, V,
+                                     _p(target, ctypes.c_int32), _p(n_append, ctypes.c_int32))
+    _check(rc, "greedy_accept")
+    return target, n_append

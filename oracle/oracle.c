@@ -331,3 +331,42 @@ int oracle_ring_append(unsigned char *k_cache, unsigned char *v_cache,
     }
     return ORC_OK;
 }
+
+/*
+ * Greedy acceptance of draft tokens after a verify pass (self-speculative
+ * decoding with the MTP heads as the draft model: release blog, section
+ * "Multi-Token Prediction", and its verify diagram).
+ *   logits [B, T, V]: the target model's scores at the T positions under
+ *   verification; draft [B, T - 1]: the token proposed for position t + 1.
+ *   target[b, t] = argmax_v logits[b, t, v]  (the lowest index among equal
+ *   maxima).  Draft t is accepted when target[b, t] == draft[b, t] and every
+ *   earlier draft was accepted.  n_append[b] = 1 + accepted: the first
+ *   verified token (already committed by the model) plus the accepted drafts
+ *   are the rows whose K/V join the cache.
+ */
+int oracle_greedy_accept(const float *logits, const int32_t *draft, int B, int T, long V,
+                         int32_t *target, int32_t *n_append)
+{
+    if (B < 0 || T < 1 || V < 1)
+        return ORC_BAD_ARGS;
+    int b;
+    for (b = 0; b < B; ++b) {
+        int t, accepted = 0, open = 1;
+        for (t = 0; t < T; ++t) {
+            const float *row = logits + ((size_t)b * T + t) * (size_t)V;
+            long best = 0, v;
+            for (v = 1; v < V; ++v)
+                if (row[v] > row[best])
+                    best = v;
+            target[(size_t)b * T + t] = (int32_t)best;
+        }
+        for (t = 0; t + 1 < T && open; ++t) {
+            if (target[(size_t)b * T + t] == draft[(size_t)b * (T - 1) + t])
+                ++accepted;
+            else
+                open = 0;
+        }
+        n_append[b] = 1 + accepted;
+    }
+    return ORC_OK;
+}

@@ -18,6 +18,11 @@ What pins what:
   * verify == successive single-token decodes == the last rows of a prefill;
     chunked prefill == unchunked; sampled rows == full prefill.
   * ring append: every slot checked against the stated placement rule.
+  * greedy draft acceptance: the release blog's verify diagram (accept,
+    accept, reject, discard gives three rows to append), a match after the
+    first rejection that must not count, ties resolved to the lowest index,
+    T=1 and all-accepted edge cases, and numpy's argmax (first occurrence of
+    the maximum) plus a brute-force prefix count on random integer logits.
 """
 from __future__ import annotations
 
@@ -295,6 +300,75 @@ def pin_ring_append_placement():
                     assert np.array_equal(kc[b, s], k0[b, s]) and np.array_equal(vc[b, s], v0[b, s])
 
 
+def _onehot_logits(tokens, V, base=-3.0, peak=5.0):
+    """logits [B,T,V] whose row (b,t) peaks at tokens[b][t]."""
+    B, T = len(tokens), len(tokens[0])
+    lg = np.full((B, T, V), base, dtype=np.float32)
+    for b in range(B):
+        for t in range(T):
+            lg[b, t, tokens[b][t]] = peak
+    return lg
+
+
+def pin_accept_blog_example():
+    # verify diagram: token i and drafts i+1..i+3 go in; the model's outputs
+    # for i+1 and i+2 match the drafts (accepted), the one for i+3 does not
+    # (rejected: it becomes the corrected token) and the one for i+4 is
+    # discarded.  Rows i, i+1, i+2 join the cache.
+    V = 11
+    target = [[4, 9, 2, 7]]
+    draft = np.array([[4, 9, 5]], dtype=np.int32)
+    tg, na = oracle.greedy_accept(_onehot_logits(target, V), draft)
+    assert tg.tolist() == target and na.tolist() == [3]
+
+
+def pin_accept_stops_at_first_rejection():
+    V = 7
+    target = [[1, 2, 3, 4], [1, 2, 3, 4], [1, 2, 3, 4]]
+    draft = np.array([[0, 2, 3],      # first draft wrong: later matches discarded
+                      [1, 0, 3],      # second wrong
+                      [1, 2, 3]],     # all three accepted
+                     dtype=np.int32)
+    tg, na = oracle.greedy_accept(_onehot_logits(target, V), draft)
+    assert tg.tolist() == target and na.tolist() == [1, 2, 4]
+
+
+def pin_accept_ties_and_edges():
+    V = 9
+    lg = np.zeros((3, 2, V), dtype=np.float32)
+    lg[0, 0, [2, 5]] = 1.0           # tie between 2 and 5 -> 2
+    lg[0, 1, [8, 3]] = 2.0           # tie between 3 and 8 -> 3
+    lg[1, :, :] = -np.inf            # every entry equal -> 0
+    lg[2, 0, V - 1] = 0.5            # maximum at the last index
+    lg[2, 1, :] = -1.0
+    draft = np.array([[2], [1], [V - 1]], dtype=np.int32)
+    tg, na = oracle.greedy_accept(lg, draft)
+    assert tg.tolist() == [[2, 3], [0, 0], [V - 1, 0]]
+    assert na.tolist() == [2, 1, 2]
+    # q_len = 1 (plain decode): nothing to accept, one row appended
+    tg1, na1 = oracle.greedy_accept(lg[:, :1], np.zeros((3, 0), dtype=np.int32))
+    assert tg1.tolist() == [[2], [0], [V - 1]] and na1.tolist() == [1, 1, 1]
+
+
+def pin_accept_vs_numpy_argmax():
+    rng = np.random.default_rng(11)
+    B, T, V = 40, 4, 37
+    # small integer logits: many exact ties
+    lg = rng.integers(-3, 4, size=(B, T, V)).astype(np.float32)
+    ref_t = np.argmax(lg, axis=-1)   # numpy returns the first maximal index
+    # drafts agree with the reference target with probability 3/4 each
+    draft = np.where(rng.random((B, T - 1)) < 0.75, ref_t[:, :T - 1],
+                     rng.integers(0, V, size=(B, T - 1))).astype(np.int32)
+    tg, na = oracle.greedy_accept(lg, draft)
+    assert np.array_equal(tg, ref_t)
+    for b in range(B):
+        n = 0
+        while n < T - 1 and draft[b, n] == ref_t[b, n]:
+            n += 1
+        assert na[b] == n + 1
+    assert len(set(na.tolist())) == T   # every acceptance length occurs
+
+
 ALL_PINS = [
     pin_sdpa_with_sink_column,
     pin_no_sink_is_band_softmax,
@@ -308,4 +382,8 @@ ALL_PINS = [
     pin_verify_equals_successive_decodes,
     pin_chunked_prefill_equals_unchunked,
     pin_ring_append_placement,
+    pin_accept_blog_example,
+    pin_accept_stops_at_first_rejection,
+    pin_accept_ties_and_edges,
+    pin_accept_vs_numpy_argmax,
 ]

@@ -3,7 +3,9 @@
 Each mutant is a copy of oracle/oracle.c with one plausible mistake planted
 (an off-by-one window edge, a dropped sink term, a dropped scale, a wrong GQA
 index, values swapped for keys, an ignored causal offset, a wrong sign in the
-exponent, a reversed operand, a verify that hides the query's own token, ...).
+exponent, a reversed operand, a verify that hides the query's own token, an argmax
+that breaks ties the other way, an acceptance that continues past a
+rejection, ...).
 Each is compiled with gcc into a temporary library and every pin is run
 against it: at least one pin must fail, or the pins would not detect that
 mistake.
@@ -36,6 +38,11 @@ MUTANTS = {
     "verify_drops_oldest_key": ("long nA = lo < L ? L - lo : 0;", "long nA = lo < L ? L - lo - 1 : 0;"),
     "ring_slot_shifted": ("long slot = ring ? p % slots : p;", "long slot = ring ? (p + 1) % slots : p;"),
     "lse_without_max": ("*lse_out = m + log(z);", "*lse_out = log(z);"),
+    "argmax_ties_to_highest": ("if (row[v] > row[best])", "if (row[v] >= row[best])"),
+    "append_count_without_committed_row": ("n_append[b] = 1 + accepted;", "n_append[b] = accepted;"),
+    "accept_after_rejection": ("for (t = 0; t + 1 < T && open; ++t) {", "for (t = 0; t + 1 < T; ++t) {"),
+    "accept_compares_shifted_target": ("if (target[(size_t)b * T + t] == draft",
+                                       "if (target[(size_t)b * T + t + 1] == draft"),
 }
 
 
