@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="time the SWA prefill only")
-    ap.add_argument("--only", choices=["prefill", "ga", "verify"], default=None,
+    ap.add_argument("--only", choices=["prefill", "ga", "verify", "mtp"], default=None,
                     help="run one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--settle-seconds", type=float, default=0.5,
                     help="untimed repetition of each step before its warmup, so the clocks are at "
@@ -281,6 +281,146 @@ def run_verify(args, swa, torch, dev, stream, names=("verify_ga_b64", "verify_sw
     }
 
 
+# The model's 48 layers: 39 sliding-window and 9 global (technical-report
+# digest, "Model Architecture" hyper-parameters).  Which layers are global is
+# not given; the order does not change the step time.
+N_SWA_LAYERS, N_GA_LAYERS = 39, 9
+
+
+def run_mtp(args, swa, torch, dev, stream):
+    """One self-speculative decode step of the attention path for 64 requests:
+    the q_len=4 verify of all 48 layers (9 global layers on linear caches with
+    contexts U[4096, 65536], 39 SWA layers on 128-slot rings), greedy
+    acceptance on bf16 logits over a 152064-token vocabulary, the append of
+    the accepted rows to all 48 caches, and the length advance.  Compared with
+    the plain q_len=1 decode step (same layers, argmax, append of one row)."""
+    import dataclasses
+    from swa_inputs import ACCEPT_CONFIGS, VERIFY_CONFIGS, accept_inputs, derive_seed, normal, verify_inputs
+
+    acfg = ACCEPT_CONFIGS["accept_b64"]
+    gcfg = VERIFY_CONFIGS["verify_ga_b64"]
+    scfg = VERIFY_CONFIGS["verify_swa_b64"]
+    B, T, V = gcfg.B, gcfg.T, acfg.vocab
+    assert acfg.B == B and acfg.T == T and scfg.B == B and scfg.T == T
+    # room for the appended rows behind the longest context
+    gcfg = dataclasses.replace(gcfg, slots=gcfg.len_hi + 4 * T)
+    ga_in = verify_inputs(gcfg, device=dev)
+    sw_in = verify_inputs(scfg, device=dev)
+    assert torch.equal(ga_in["cache_len"], sw_in["cache_len"])
+    cl0 = ga_in["cache_len"].to(torch.int32).to(dev)
+    L = ga_in["cache_len"].to(torch.int64)
+    cl = cl0.clone()
+    layers = []
+    for li in range(N_SWA_LAYERS + N_GA_LAYERS):
+        is_ga = li == 0 or li % 6 == 5     # 9 global layers among 48
+        cfg, src = (gcfg, ga_in) if is_ga else (scfg, sw_in)
+        first = not any(l["cfg"] is cfg for l in layers)
+        kc = src["k_cache"] if first else src["k_cache"].clone()
+        vc = src["v_cache"] if first else src["v_cache"].clone()
+        shp_q, shp_kv = (B, T, cfg.Hq, cfg.D), (B, T, cfg.Hkv, cfg.D)
+        q = normal(shp_q, derive_seed("mtp_bench", li, "q"), dev, torch.bfloat16)
+        kn = normal(shp_kv, derive_seed("mtp_bench", li, "k"), dev, torch.bfloat16)
+        vn = normal(shp_kv, derive_seed("mtp_bench", li, "v"), dev, torch.bfloat16)
+        layers.append(dict(cfg=cfg, k=kc, v=vc, q=q, kn=kn, vn=vn, o=torch.empty_like(q),
+                           q1=q[:, :1].contiguous(), kn1=kn[:, :1].contiguous(),
+                           vn1=vn[:, :1].contiguous(), o1=torch.empty_like(q[:, :1]),
+                           sinks=src["sinks"]))
+    assert sum(l["cfg"] is gcfg for l in layers) == N_GA_LAYERS
+    ws_need = max(swa.swa_attn_verify_workspace_bytes(B, t, gcfg.Hq, gcfg.Hkv, gcfg.D, gcfg.slots,
+                                                      False, 0) for t in (1, T))
+    ws = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+    n_sets = 4
+    sets = [accept_inputs(acfg, device=dev, step=i) for i in range(n_sets)]
+    sets1 = [(lg[:, :1].contiguous(), None) for lg, _ in sets]
+    aws = torch.empty(max(swa.swa_mtp_accept_workspace_bytes(B, T, V), 1), dtype=torch.uint8, device=dev)
+    tgt = torch.empty((B, T), dtype=torch.int32, device=dev)
+    tgt1 = torch.empty((B, 1), dtype=torch.int32, device=dev)
+    na = torch.empty((B,), dtype=torch.int32, device=dev)
+    mean_tokens = 0.0
+    for lg, dr in sets:
+        swa.swa_mtp_greedy_accept(lg, dr, workspace=aws, target=tgt, n_append=na)
+        mean_tokens += float(na.sum()) / B / n_sets
+    it = [0]
+
+    def verify_all(decode=False):
+        for l in layers:
+            c = l["cfg"]
+            if decode:
+                swa.swa_attn_verify(l["q1"], l["kn1"], l["vn1"], l["k"], l["v"], cl, l["sinks"], c.window,
+                                    c.ring, c.scale, workspace=ws, out=l["o1"])
+            else:
+                swa.swa_attn_verify(l["q"], l["kn"], l["vn"], l["k"], l["v"], cl, l["sinks"], c.window,
+                                    c.ring, c.scale, workspace=ws, out=l["o"])
+
+    def accept(decode=False):
+        lg, dr = (sets1 if decode else sets)[it[0] % n_sets]
+        it[0] += 1
+        swa.swa_mtp_greedy_accept(lg, dr, workspace=aws, target=tgt1 if decode else tgt, n_append=na)
+
+    def commit(decode=False):
+        for l in layers:
+            swa.kv_ring_append(l["k"], l["v"], l["kn1"] if decode else l["kn"],
+                               l["vn1"] if decode else l["vn"], cl, na, l["cfg"].ring)
+        swa.swa_cache_advance(cl, na)
+
+    def mtp_step():
+        verify_all()
+        accept()
+        commit()
+
+    def decode_step():
+        verify_all(True)
+        accept(True)
+        commit(True)
+
+    filler = next(l for l in layers if l["cfg"] is gcfg)
+
+    def before():
+        # restore the committed lengths, then queue two global-layer verifies
+        # (about 3 ms of GPU work) so that the host has enqueued all of the
+        # timed launches before the GPU reaches them: the timed region then
+        # holds GPU time only, not the host's launch latency
+        cl.copy_(cl0)
+        for _ in range(2):
+            swa.swa_attn_verify(filler["q"], filler["kn"], filler["vn"], filler["k"], filler["v"], cl,
+                                filler["sinks"], 0, False, gcfg.scale, workspace=ws, out=filler["o"])
+
+    def timed(fn):
+        def once():
+            cl.copy_(cl0)
+            fn()
+        settle(once, args.settle_seconds)
+        for _ in range(args.warmup):
+            once()
+        return time_launches(fn, max(args.steps, 5), stream, before)
+
+    mtp_ms = timed(mtp_step)
+    dec_ms = timed(decode_step)
+    ver_ms = timed(verify_all)
+    acc_ms = timed(accept)
+    com_ms = timed(commit)
+    logit_bytes = B * T * V * 2
+    per_tok = mtp_ms / mean_tokens
+    del layers, ga_in, sw_in, ws, sets, sets1
+    torch.cuda.empty_cache()
+    return {
+        "workload": "mtp_step_b64: 39 SWA ring layers + 9 global linear layers, q_len=4, vocab 152064",
+        "metric": "attention-path tokens/s of self-speculative decoding (verify + accept + append)",
+        "value": round(B * mean_tokens / (mtp_ms * 1e-3), 1), "unit": "tokens/s",
+        "batch": B, "q_len": T, "layers": {"swa": N_SWA_LAYERS, "global": N_GA_LAYERS},
+        "context_lengths": [gcfg.len_lo, gcfg.len_hi], "vocab": V,
+        "per_draft_agreement": acfg.p_accept, "mean_tokens_per_step": round(mean_tokens, 4),
+        "ms_per_step": round(mtp_ms, 4), "ms_verify_48_layers": round(ver_ms, 4),
+        "ms_accept": round(acc_ms, 4), "ms_append_48_layers_and_advance": round(com_ms, 4),
+        "attention_ms_per_token": round(per_tok, 4),
+        "decode_ms_per_step": round(dec_ms, 4),
+        "decode_tokens_per_s": round(B / (dec_ms * 1e-3), 1),
+        "speedup_vs_decode": round(dec_ms / per_tok, 3),
+        "accept_logits_bytes": logit_bytes,
+        "accept_GB/s": round(logit_bytes / (acc_ms * 1e-3) / 1e9, 1),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -314,6 +454,9 @@ def main():
     if args.only == "verify":
         print(json.dumps({"verify": run_verify(args, swa, torch, dev, stream)}), flush=True)
         return
+    if args.only == "mtp":
+        print(json.dumps({"mtp_step": run_mtp(args, swa, torch, dev, stream)}), flush=True)
+        return
 
     cfg = PREFILL_CONFIGS["swa_32k"]
     pres, tensors = run_prefill(args, swa, torch, dev, stream, cfg)
@@ -338,6 +481,7 @@ def main():
         result["ga_prefill"] = run_ga(args, swa, torch, dev, stream)
         result["verify"] = run_verify(args, swa, torch, dev, stream)
         result["decode"] = run_verify(args, swa, torch, dev, stream, ("decode_ga_b64", "decode_swa_b64"))
+        result["mtp_step"] = run_mtp(args, swa, torch, dev, stream)
     peaks = read_peaks()
     if peaks is not None:
         # fractions of the ceilings measured on this GPU: the SWA prefill moves

@@ -7,6 +7,9 @@ declared in ``include/swa_attn.h``).  The functions carry the C names:
     swa_attn_verify_workspace_bytes(...)
     swa_attn_verify(q, k_new, v_new, k_cache, v_cache, cache_len, sinks, window, ring, ...)
     kv_ring_append(k_cache, v_cache, k_new, v_new, cache_len, n_append, ring)
+    swa_mtp_accept_workspace_bytes(B, q_len, vocab)
+    swa_mtp_greedy_accept(logits, draft, ...) -> (target, n_append)
+    swa_cache_advance(cache_len, n_append)
 
 They only check and marshal arguments (device, dtype, contiguity, shapes)
 and pass raw device pointers plus torch's current HIP stream; every step of
@@ -24,6 +27,7 @@ import torch
 __all__ = [
     "SwaError", "library_path", "load_library", "swa_attn_prefill",
     "swa_attn_verify_workspace_bytes", "swa_attn_verify", "kv_ring_append",
+    "swa_mtp_accept_workspace_bytes", "swa_mtp_greedy_accept", "swa_cache_advance",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -33,7 +37,8 @@ _lib = None
 
 SWA_F32, SWA_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("swa_status_string", "swa_attn_prefill", "swa_attn_verify_workspace_bytes",
-                    "swa_attn_verify", "kv_ring_append")
+                    "swa_attn_verify", "kv_ring_append", "swa_mtp_accept_workspace_bytes",
+                    "swa_mtp_greedy_accept", "swa_cache_advance")
 
 
 class SwaError(RuntimeError):
@@ -66,6 +71,13 @@ def load_library():
     lib.swa_attn_verify.restype = i
     lib.kv_ring_append.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, i, p]
     lib.kv_ring_append.restype = i
+    i64 = ctypes.c_int64
+    lib.swa_mtp_accept_workspace_bytes.argtypes = [i, i, i64]
+    lib.swa_mtp_accept_workspace_bytes.restype = sz
+    lib.swa_mtp_greedy_accept.argtypes = [p, p, p, p, i, i, i64, i, p, sz, p]
+    lib.swa_mtp_greedy_accept.restype = i
+    lib.swa_cache_advance.argtypes = [p, p, i, p]
+    lib.swa_cache_advance.restype = i
     _lib = lib
     return lib
 
@@ -209,3 +221,59 @@ def kv_ring_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Te
                             _ptr(cache_len), _ptr(n_append), B, T, Hkv, D, slots,
                             int(bool(ring)), _dtype_code(k_cache), _stream(stream))
     _check(st, "kv_ring_append")
+
+
+def swa_mtp_accept_workspace_bytes(B: int, q_len: int, vocab: int) -> int:
+    return int(load_library().swa_mtp_accept_workspace_bytes(B, q_len, vocab))
+
+
+def swa_mtp_greedy_accept(logits: torch.Tensor, draft: Optional[torch.Tensor],
+                          workspace: Optional[torch.Tensor] = None,
+                          target: Optional[torch.Tensor] = None,
+                          n_append: Optional[torch.Tensor] = None, stream=None):
+    """Greedy draft acceptance: logits [B,q_len,vocab] (bf16 or fp32), draft
+    [B,q_len-1] int32 (None when q_len == 1).  Returns (target [B,q_len]
+    int32: per-row argmax, lowest index on ties; n_append [B] int32:
+    1 + accepted leading drafts)."""
+    lib = load_library()
+    _dev(logits, "logits", ndim=3)
+    B, T, V = logits.shape
+    if draft is not None:
+        _dev(draft, "draft", torch.int32, 2)
+        if draft.shape != (B, T - 1):
+            raise ValueError("draft must be [B, q_len - 1]")
+    elif T > 1:
+        raise ValueError("draft is required when q_len > 1")
+    if target is None:
+        target = torch.empty((B, T), dtype=torch.int32, device=logits.device)
+    else:
+        _dev(target, "target", torch.int32, 2)
+        if target.shape != (B, T):
+            raise ValueError("target must be [B, q_len]")
+    if n_append is None:
+        n_append = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    else:
+        _dev(n_append, "n_append", torch.int32, 1)
+        if n_append.shape[0] != B:
+            raise ValueError("n_append must have B entries")
+    need = swa_mtp_accept_workspace_bytes(B, T, V)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.swa_mtp_greedy_accept(_ptr(logits), _ptr(draft), _ptr(target), _ptr(n_append), B, T, V,
+                                   _dtype_code(logits), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "swa_mtp_greedy_accept")
+    return target, n_append
+
+
+def swa_cache_advance(cache_len: torch.Tensor, n_append: torch.Tensor, stream=None) -> None:
+    """cache_len[b] += n_append[b] on the GPU (both int32 [B]).  In place."""
+    lib = load_library()
+    _dev(cache_len, "cache_len", torch.int32, 1)
+    _dev(n_append, "n_append", torch.int32, 1)
+    if n_append.shape != cache_len.shape:
+        raise ValueError("cache_len and n_append must have the same length")
+    st = lib.swa_cache_advance(_ptr(cache_len), _ptr(n_append), cache_len.shape[0], _stream(stream))
+    _check(st, "swa_cache_advance")

@@ -129,4 +129,39 @@ swa_status_t kv_ring_append(void* k_cache, void* v_cache, const void* k_new, con
   return from_hip(launch_append(a, (hipStream_t)stream));
 }
 
+size_t swa_mtp_accept_workspace_bytes(int B, int q_len, int64_t vocab) {
+  if (swa_validate_accept((const void*)1, (const void*)1, (const void*)1, (const void*)1, B, q_len,
+                          vocab, SWA_F32) != SWA_OK || B == 0)
+    return 0;
+  return plan_accept(B, q_len, (long)vocab).ws_bytes;
+}
+
+swa_status_t swa_mtp_greedy_accept(const void* logits, const int32_t* draft, int32_t* target,
+                                   int32_t* n_append, int B, int q_len, int64_t vocab,
+                                   swa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  swa_status_t st = swa_validate_accept(logits, draft, target, n_append, B, q_len, vocab, dtype);
+  if (st != SWA_OK || B == 0) return st;
+  const AcceptPlan plan = plan_accept(B, q_len, (long)vocab);
+  if (!workspace || workspace_bytes < plan.ws_bytes || ((uintptr_t)workspace & 3u) != 0)
+    return SWA_ERR_WORKSPACE;
+  AcceptArgs a = {};
+  a.logits = logits;
+  a.draft = draft;
+  a.target = target;
+  a.n_append = n_append;
+  a.ws_v = (float*)workspace;
+  a.V = (long)vocab;
+  a.B = B;
+  a.T = q_len;
+  a.elem_bytes = dtype == SWA_BF16 ? 2 : 4;
+  return from_hip(launch_accept(a, plan, (hipStream_t)stream));
+}
+
+swa_status_t swa_cache_advance(int32_t* cache_len, const int32_t* n_append, int B, void* stream) {
+  swa_status_t st = swa_validate_advance(cache_len, n_append, B);
+  if (st != SWA_OK || B == 0) return st;
+  return from_hip(launch_advance(cache_len, n_append, B, (hipStream_t)stream));
+}
+
 }  // extern "C"

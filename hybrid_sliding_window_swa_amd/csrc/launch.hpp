@@ -68,4 +68,26 @@ hipError_t launch_verify_f32(const VerifyArgs& a, hipStream_t s);
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
+struct AcceptArgs {
+  const void* logits;     // [B][T][V] fp32 or bf16 bits
+  const int32_t* draft;   // [B][T-1]
+  int32_t* target;        // [B][T]
+  int32_t* n_append;      // [B]
+  float* ws_v;            // [B*T][nchunk] chunk maxima
+  int32_t* ws_i;          // [B*T][nchunk] lowest index of each chunk maximum (set by the launcher)
+  long V;
+  int B, T, elem_bytes;
+  long chunk_len;         // set by the launcher
+  int nchunk;             // set by the launcher
+};
+
+struct AcceptPlan {
+  long chunk_len;  // logits per chunk (a multiple of 1024)
+  int nchunk;      // chunks per row
+  size_t ws_bytes;
+};
+AcceptPlan plan_accept(int B, int T, long V);
+hipError_t launch_accept(AcceptArgs a, const AcceptPlan& p, hipStream_t s);
+hipError_t launch_advance(int32_t* cache_len, const int32_t* n_append, int B, hipStream_t s);
+
 }  // namespace swa

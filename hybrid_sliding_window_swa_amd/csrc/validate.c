@@ -98,3 +98,30 @@ swa_status_t swa_validate_append(const void *k_cache, const void *v_cache, const
         return SWA_ERR_NULL;
     return SWA_OK;
 }
+
+swa_status_t swa_validate_accept(const void *logits, const void *draft, const void *target,
+                                 const void *n_append, int B, int q_len, long long vocab,
+                                 swa_dtype_t dtype)
+{
+    if (!dtype_ok(dtype))
+        return SWA_ERR_UNSUPPORTED;
+    if (B < 0 || q_len < 1 || q_len > 16 || vocab < 1 || vocab > 2147483647LL ||
+        (long long)B * q_len > 65535)
+        return SWA_ERR_SHAPE;
+    if (B == 0)
+        return SWA_OK;
+    if (!logits || !target || !n_append || (q_len > 1 && !draft))
+        return SWA_ERR_NULL;
+    return SWA_OK;
+}
+
+swa_status_t swa_validate_advance(const void *cache_len, const void *n_append, int B)
+{
+    if (B < 0)
+        return SWA_ERR_SHAPE;
+    if (B == 0)
+        return SWA_OK;
+    if (!cache_len || !n_append)
+        return SWA_ERR_NULL;
+    return SWA_OK;
+}

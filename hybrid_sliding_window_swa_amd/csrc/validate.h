@@ -28,6 +28,13 @@ swa_status_t swa_validate_append(const void *k_cache, const void *v_cache, const
                                  int B, int q_len, int Hkv, int D, int cache_slots, int ring,
                                  swa_dtype_t dtype);
 
+/* B * q_len <= 65535 (one workgroup row per logits row), 1 <= vocab < 2^31. */
+swa_status_t swa_validate_accept(const void *logits, const void *draft, const void *target,
+                                 const void *n_append, int B, int q_len, long long vocab,
+                                 swa_dtype_t dtype);
+
+swa_status_t swa_validate_advance(const void *cache_len, const void *n_append, int B);
+
 #ifdef __cplusplus
 }
 #endif

@@ -162,6 +162,49 @@ SWA_API swa_status_t kv_ring_append(void *k_cache, void *v_cache,
                             int B, int q_len, int Hkv, int D, int cache_slots, int ring,
                             swa_dtype_t dtype, void *stream);
 
+/*
+ * Bytes of device workspace swa_mtp_greedy_accept needs (per-chunk maxima
+ * and their indices).  0 when the sizes are invalid or B == 0.
+ */
+SWA_API size_t swa_mtp_accept_workspace_bytes(int B, int q_len, int64_t vocab);
+
+/*
+ * Greedy acceptance of draft tokens after a verify pass (self-speculative
+ * decoding with the MTP heads as the draft model; release blog, section
+ * "Multi-Token Prediction", verify diagram: accept a prefix, reject the first
+ * mismatch, discard the rest).
+ *   logits   [B, q_len, vocab] DEVICE, fp32 (SWA_F32) or bf16 (SWA_BF16):
+ *            the main model's scores at the q_len verified positions; bf16 is
+ *            widened to fp32 exactly before comparing.
+ *   draft    [B, q_len - 1] int32 DEVICE: the token drafted for position t+1,
+ *            compared with the prediction at position t; may be NULL when
+ *            q_len == 1.
+ *   target   [B, q_len] int32 DEVICE output: argmax over the vocabulary of
+ *            each row, the lowest index among equal maxima.  target[b, t] is
+ *            the main model's token for position t + 1; the entry at the
+ *            first rejected draft is the corrected token.
+ *   n_append [B] int32 DEVICE output: 1 + the number of leading drafts with
+ *            draft[b, t] == target[b, t] (1 <= n_append <= q_len): the rows of
+ *            the verified tokens whose K/V enter the caches (kv_ring_append).
+ *   workspace  device buffer, 4-byte aligned, of at least
+ *            swa_mtp_accept_workspace_bytes(B, q_len, vocab) bytes; scratch.
+ * Sizes: 1 <= q_len <= 16, 1 <= vocab < 2^31, B * q_len <= 65535.
+ * NaN logits are never selected (a row of only NaN gives index 0).
+ * B == 0 is a no-op.  Calls sharing a workspace must not overlap.
+ */
+SWA_API swa_status_t swa_mtp_greedy_accept(const void *logits, const int32_t *draft,
+                                   int32_t *target, int32_t *n_append,
+                                   int B, int q_len, int64_t vocab, swa_dtype_t dtype,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * cache_len[b] += n_append[b] for b < B (both [B] int32 DEVICE arrays): the
+ * committed length after every layer's kv_ring_append of the same step (the
+ * appends read the old length).  B == 0 is a no-op.
+ */
+SWA_API swa_status_t swa_cache_advance(int32_t *cache_len, const int32_t *n_append, int B,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

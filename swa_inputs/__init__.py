@@ -26,6 +26,7 @@ __all__ = [
     "PrefillConfig", "VerifyConfig", "PREFILL_CONFIGS", "VERIFY_CONFIGS",
     "derive_seed", "normal", "prefill_inputs", "verify_inputs",
     "ring_from_history", "linear_from_history", "sample_rows", "torch_dtype",
+    "AcceptConfig", "ACCEPT_CONFIGS", "accept_inputs", "tied_logits",
 ]
 
 
@@ -236,3 +237,54 @@ def sample_rows(S: int, n: int, seed: int, forced=()) -> torch.Tensor:
     pick = torch.randperm(S, generator=g)[:n]
     forced = torch.tensor([r for r in forced if 0 <= r < S], dtype=torch.int64)
     return torch.unique(torch.cat([pick, forced]))
+
+
+@dataclasses.dataclass(frozen=True)
+class AcceptConfig:
+    name: str
+    B: int
+    T: int            # verified positions per request (1 committed + T-1 drafts)
+    vocab: int
+    p_accept: float   # probability that a draft equals the planted top token
+    dtype: str        # logits dtype
+    seed: int
+
+
+ACCEPT_CONFIGS = {
+    # 64 requests, 3 drafts; per-draft agreement 0.83 gives a mean of
+    # 1 + p + p^2 + p^3 = 3.09 tokens per step, inside the reported 2.8-3.6.
+    # The vocabulary size is not on the pages; 152064 is assumed.
+    "accept_b64": AcceptConfig("accept_b64", 64, 4, 152064, 0.83, "bf16", seed=8),
+}
+
+
+def accept_inputs(cfg: AcceptConfig, device="cpu", step: int = 0):
+    """Synthetic verify logits [B,T,vocab] and drafts [B,T-1] int32.
+
+    Logits are N(0,1) with one planted entry of +8 per row (at a uniformly
+    drawn token), far above every other draw.  Draft t equals the planted
+    token of row t with probability ``p_accept`` and otherwise is another
+    uniformly drawn token, so the acceptance length follows the geometric
+    prefix law of independent per-draft agreement."""
+    dt = torch_dtype(cfg.dtype)
+    B, T, V = cfg.B, cfg.T, cfg.vocab
+    logits = normal((B, T, V), derive_seed(cfg.seed, step, "logits"), device, torch.float32)
+    g = torch.Generator()
+    g.manual_seed(derive_seed(cfg.seed, step, "tokens"))
+    top = torch.randint(0, V, (B, T), generator=g)
+    agree = torch.rand((B, max(T - 1, 0)), generator=g) < cfg.p_accept
+    other = (top[:, :T - 1] + 1 + torch.randint(0, max(V - 1, 1), (B, max(T - 1, 0)), generator=g)) % V
+    draft = torch.where(agree, top[:, :T - 1], other).to(torch.int32)
+    logits = logits.view(B * T, V)
+    logits[torch.arange(B * T, device=logits.device), top.reshape(-1).to(logits.device)] = 8.0
+    logits = logits.view(B, T, V).to(dt)
+    return logits, draft.to(device)
+
+
+def tied_logits(B: int, T: int, V: int, seed: int, lo: int = -2, hi: int = 2,
+                device="cpu", dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Integer-valued logits in [lo, hi]: every row has many equal maxima."""
+    g = torch.Generator()
+    g.manual_seed(derive_seed(seed, "tied", B, T, V))
+    x = torch.randint(lo, hi + 1, (B, T, V), generator=g).to(torch.float32)
+    return x.to(device=device, dtype=dtype)

@@ -133,3 +133,42 @@ def test_append_validation(lib):
     assert _append(lib, ring=5) == SHAPE
     assert _append(lib, Hkv=1, D=3) == UNSUP        # row not a multiple of 16 bytes
     assert _append(lib, B=0, ptr=0) == OK
+
+
+def _accept(lib, ptr=1, draft=1, B=64, T=4, V=152064, dt=BF16, ws=256, ws_bytes=1 << 30):
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.swa_mtp_greedy_accept(P(ptr), P(draft), P(ptr), P(ptr), B, T, V, dt, P(ws), ws_bytes, None)
+
+
+def test_accept_validation(lib):
+    assert _accept(lib, ptr=0) == NULL
+    assert _accept(lib, draft=0) == NULL             # drafts are needed when q_len > 1
+    assert _accept(lib, T=0) == SHAPE
+    assert _accept(lib, T=17) == SHAPE
+    assert _accept(lib, V=0) == SHAPE
+    assert _accept(lib, V=1 << 31) == SHAPE          # indices are int32
+    assert _accept(lib, B=16384, T=4) == SHAPE       # B * q_len > 65535
+    assert _accept(lib, dt=9) == UNSUP
+    assert _accept(lib, ws=0) == WS
+    need = lib.swa_mtp_accept_workspace_bytes(64, 4, 152064)
+    assert need > 0
+    assert _accept(lib, ws_bytes=need - 1) == WS
+    assert _accept(lib, ws=258, ws_bytes=need) == WS  # not 4-byte aligned
+    assert _accept(lib, B=0, ptr=0, draft=0, ws=0, ws_bytes=0) == OK
+
+
+def test_accept_workspace_sizes(lib):
+    ws = lib.swa_mtp_accept_workspace_bytes
+    # every row is split into chunks of a multiple of 1024 logits, about 2048
+    # workgroups per launch; 8 bytes (max, index) per row and chunk
+    assert ws(64, 4, 152064) == 64 * 4 * 8 * 8        # 8 chunks of 19456
+    assert ws(1, 1, 152064) == 149 * 8                # 149 chunks of 1024
+    assert ws(1, 1, 5) == 8                           # one short chunk
+    assert ws(0, 4, 100) == 0 and ws(2, 0, 100) == 0 and ws(2, 4, 0) == 0
+
+
+def test_advance_validation(lib):
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    assert lib.swa_cache_advance(P(0), P(1), 4, None) == NULL
+    assert lib.swa_cache_advance(P(1), P(1), -1, None) == SHAPE
+    assert lib.swa_cache_advance(P(0), P(0), 0, None) == OK
