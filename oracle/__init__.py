@@ -16,7 +16,10 @@ repeated KV heads, verify vs successive single-token decodes and vs prefill
 rows, chunked vs unchunked prefill, and hand-derived golden values.  The
 greedy draft acceptance is pinned by hand-built cases (the release blog's
 accept, accept, reject, discard example among them), tie breaking and
-numpy's argmax.
+numpy's argmax.  The partial rotary embedding is pinned by closed forms
+(one-hot inputs at known angles), position 0 as the identity, composition of
+rotations, preserved pair norms and the relative-position property of the
+rotated dot product.
 """
 from __future__ import annotations
 
@@ -65,6 +68,8 @@ def _bind(lib):
     lib.oracle_greedy_accept.argtypes = [c_f, ctypes.POINTER(ctypes.c_int32), i, i, l,
                                          ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.oracle_greedy_accept.restype = i
+    lib.oracle_rope.argtypes = [c_d, c_d, c_i64, l, i, i, i, d]
+    lib.oracle_rope.restype = i
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i
     return lib
@@ -244,3 +249,25 @@ def greedy_accept(logits, draft):
                                      _p(target, ctypes.c_int32), _p(n_append, ctypes.c_int32))
     _check(rc, "greedy_accept")
     return target, n_append
+
+
+def rope_dims(D: int, factor: float = 0.334) -> int:
+    """Rotated dimensions per head: the largest even number <= factor * D."""
+    return 2 * int(factor * D / 2)
+
+
+def rope(x, positions, rot: int, base: float):
+    """Partial rotary embedding of x [..., H, D] (leading dims flattened to
+    rows; positions broadcast to them).  Returns float64 of x's shape."""
+    xd = _f64(x)
+    shape = xd.shape
+    H, D = shape[-2], shape[-1]
+    rows = int(np.prod(shape[:-2])) if len(shape) > 2 else 1
+    pos = np.ascontiguousarray(np.broadcast_to(_i64(positions), shape[:-2]).reshape(-1), dtype=np.int64)
+    assert pos.shape[0] == rows
+    xd = np.ascontiguousarray(xd.reshape(rows, H, D))
+    out = np.empty_like(xd)
+    rc = load().oracle_rope(_p(xd, ctypes.c_double), _p(out, ctypes.c_double), _p(pos, ctypes.c_int64),
+                            rows, H, D, int(rot), float(base))
+    _check(rc, "rope")
+    return out.reshape(shape)

@@ -370,3 +370,44 @@ int oracle_greedy_accept(const float *logits, const int32_t *draft, int B, int T
     }
     return ORC_OK;
 }
+
+/*
+ * Partial rotary position embedding on the query / key rows.
+ *   Technical-report digest, "Pre-training" (long-context extension): RoPE
+ *   base 10000 for the sliding-window layers, 640000 for the global layers,
+ *   raised to 5000000 for the 256K stage; the model card's config extract
+ *   ("lightweight multi-token prediction" section of the model download
+ *   page) gives partial_rotary_factor 0.334.
+ * Readings (the pages fix neither): only the first `rot` dimensions of each
+ * head rotate, in rot/2 pairs (i, i + rot/2) (the half-split pairing), with
+ * pair i turned by the angle pos * base^(-2i / rot); the other dimensions pass
+ * through.  x, out: [rows, H, D]; pos[r] is the position of row r.
+ *   out[i]         = x[i] cos(a_i) - x[i + rot/2] sin(a_i)
+ *   out[i + rot/2] = x[i + rot/2] cos(a_i) + x[i] sin(a_i)
+ */
+int oracle_rope(const double *x, double *out, const int64_t *pos, long rows, int H, int D,
+                int rot, double base)
+{
+    if (rows < 0 || H <= 0 || D <= 0 || rot < 0 || rot > D || (rot & 1) || !(base > 0.0))
+        return ORC_BAD_ARGS;
+    const int half = rot / 2;
+    long r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        int h, i;
+        for (h = 0; h < H; ++h) {
+            const double *xr = x + ((size_t)r * H + h) * D;
+            double *orow = out + ((size_t)r * H + h) * D;
+            for (i = 0; i < D; ++i)
+                orow[i] = xr[i];
+            for (i = 0; i < half; ++i) {
+                const double angle = (double)pos[r] * pow(base, -2.0 * i / rot);
+                const double c = cos(angle), s = sin(angle);
+                const double a = xr[i], b = xr[i + half];
+                orow[i] = a * c - b * s;
+                orow[i + half] = b * c + a * s;
+            }
+        }
+    }
+    return ORC_OK;
+}

@@ -23,6 +23,10 @@ What pins what:
     first rejection that must not count, ties resolved to the lowest index,
     T=1 and all-accepted edge cases, and numpy's argmax (first occurrence of
     the maximum) plus a brute-force prefix count on random integer logits.
+  * partial rotary embedding: one-hot inputs at known angles (cos / sin of
+    pos * base^(-2i/rot) by hand), position 0 as the identity, R(a) R(b) =
+    R(a + b), preserved pair norms with untouched tail dimensions, and the
+    relative-position property <R(p+c) q, R(p'+c) k> = <R(p) q, R(p') k>.
 """
 from __future__ import annotations
 
@@ -369,6 +373,53 @@ def pin_accept_vs_numpy_argmax():
     assert len(set(na.tolist())) == T   # every acceptance length occurs
 
 
+def pin_rope_closed_form():
+    # D = 8, rot = 4, base 100: pairs (0, 2) and (1, 3) turn by p and p / 10
+    p = 3
+    eye = np.eye(8).reshape(8, 1, 8)
+    out = oracle.rope(eye, np.full(8, p), 4, 100.0)[:, 0, :]
+    a0, a1 = 3.0, 3.0 * 100.0 ** (-2.0 / 4.0)
+    exp = np.eye(8)
+    exp[0, [0, 2]] = [math.cos(a0), math.sin(a0)]
+    exp[2, [0, 2]] = [-math.sin(a0), math.cos(a0)]
+    exp[1, [1, 3]] = [math.cos(a1), math.sin(a1)]
+    exp[3, [1, 3]] = [-math.sin(a1), math.cos(a1)]
+    assert np.abs(out - exp).max() < TOL
+    assert oracle.rope_dims(128) == 42 and oracle.rope_dims(64) == 20 and oracle.rope_dims(192) == 64
+
+
+def pin_rope_identity_composition_norm():
+    x = _rand((5, 3, 128), "rope")
+    rot, base = 42, 640000.0
+    assert np.array_equal(oracle.rope(x, np.zeros(5), rot, base), x.numpy())
+    p1 = np.array([1, 17, 4096, 65535, 262147])
+    p2 = np.array([5, 0, 123, 1, 99])
+    twice = oracle.rope(oracle.rope(x, p1, rot, base), p2, rot, base)
+    once = oracle.rope(x, p1 + p2, rot, base)
+    assert np.abs(twice - once).max() < 1e-9
+    y = oracle.rope(x, p1, rot, base)
+    xn = x.numpy()
+    assert np.array_equal(y[..., rot:], xn[..., rot:])
+    h = rot // 2
+    n_in = xn[..., :h] ** 2 + xn[..., h:rot] ** 2
+    n_out = y[..., :h] ** 2 + y[..., h:rot] ** 2
+    assert np.abs(n_in - n_out).max() < 1e-12
+    assert oracle.rope(x, p1, 0, base).tolist() == xn.tolist()
+
+
+def pin_rope_relative_position():
+    q = _rand((1, 1, 64), "rope_q")
+    k = _rand((1, 1, 64), "rope_k")
+    rot, base = 20, 10000.0
+    ref = None
+    for c in (0, 7, 1000, 250000):
+        qq = oracle.rope(q, [100 + c], rot, base)[0, 0]
+        kk = oracle.rope(k, [37 + c], rot, base)[0, 0]
+        dot = float(qq @ kk)
+        ref = dot if ref is None else ref
+        assert abs(dot - ref) < 1e-9
+
+
 ALL_PINS = [
     pin_sdpa_with_sink_column,
     pin_no_sink_is_band_softmax,
@@ -386,4 +437,7 @@ ALL_PINS = [
     pin_accept_stops_at_first_rejection,
     pin_accept_ties_and_edges,
     pin_accept_vs_numpy_argmax,
+    pin_rope_closed_form,
+    pin_rope_identity_composition_norm,
+    pin_rope_relative_position,
 ]

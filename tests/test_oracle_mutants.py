@@ -5,7 +5,7 @@ Each mutant is a copy of oracle/oracle.c with one plausible mistake planted
 index, values swapped for keys, an ignored causal offset, a wrong sign in the
 exponent, a reversed operand, a verify that hides the query's own token, an argmax
 that breaks ties the other way, an acceptance that continues past a
-rejection, ...).
+rejection, a rotary embedding with the wrong pairing or sign, ...).
 Each is compiled with gcc into a temporary library and every pin is run
 against it: at least one pin must fail, or the pins would not detect that
 mistake.
@@ -43,6 +43,11 @@ MUTANTS = {
     "accept_after_rejection": ("for (t = 0; t + 1 < T && open; ++t) {", "for (t = 0; t + 1 < T; ++t) {"),
     "accept_compares_shifted_target": ("if (target[(size_t)b * T + t] == draft",
                                        "if (target[(size_t)b * T + t + 1] == draft"),
+    "rope_interleaved_pairs": ("const double a = xr[i], b = xr[i + half];",
+                               "const double a = xr[(2 * i) % rot], b = xr[(2 * i + 1) % rot];"),
+    "rope_sign_flipped": ("orow[i] = a * c - b * s;", "orow[i] = a * c + b * s;"),
+    "rope_frequency_over_head_dim": ("pow(base, -2.0 * i / rot)", "pow(base, -2.0 * i / D)"),
+    "rope_tail_dropped": ("orow[i] = xr[i];", "orow[i] = i < rot ? xr[i] : 0.0;"),
 }
 
 
