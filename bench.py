@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="time the SWA prefill only")
-    ap.add_argument("--only", choices=["prefill", "ga", "verify", "mtp"], default=None,
+    ap.add_argument("--only", choices=["prefill", "ga", "verify", "mtp", "rope"], default=None,
                     help="run one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--settle-seconds", type=float, default=0.5,
                     help="untimed repetition of each step before its warmup, so the clocks are at "
@@ -421,6 +421,55 @@ def run_mtp(args, swa, torch, dev, stream):
     }
 
 
+def run_rope(args, swa, torch, dev, stream, cfg, prefill_ms):
+    """Partial rotary embedding (rot = 42 of 128 dims) around the 32768-token
+    sliding-window prefill: the standalone in-place kernel on q and k (its HBM
+    rate), and the prefill that rotates q as it stages it after one
+    standalone pass over k (its cost over the plain prefill)."""
+    from swa_inputs import prefill_inputs
+    q, k, v, sinks = prefill_inputs(cfg, device=dev)
+    rot = swa.rope_dims(cfg.D)
+    base = 10000.0
+    o = torch.empty_like(q)
+
+    def rope_qk():
+        swa.swa_rope_apply(q, rot, base)
+        swa.swa_rope_apply(k, rot, base)
+
+    def rope_k_fused_prefill():
+        swa.swa_rope_apply(k, rot, base)
+        swa.swa_attn_prefill_rope(q, k, v, sinks, cfg.window, rot, base, 0, cfg.scale, out=o)
+
+    def fused_prefill():
+        swa.swa_attn_prefill_rope(q, k, v, sinks, cfg.window, rot, base, 0, cfg.scale, out=o)
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    res = {}
+    for name, fn in (("standalone_q_and_k", rope_qk), ("k_then_fused_prefill", rope_k_fused_prefill),
+                     ("fused_prefill_only", fused_prefill)):
+        settle(fn, args.settle_seconds)
+        for _ in range(args.warmup):
+            fn()
+        res[name] = time_launches(fn, max(args.steps, 5), stream, lambda: flush.zero_())
+    rows = cfg.B * cfg.keys * (cfg.Hq + cfg.Hkv)
+    nbytes = rows * rot * 2 * 2           # rotated bf16 elements, read and written
+    ms = res["standalone_q_and_k"]
+    del q, k, v, o, flush
+    torch.cuda.empty_cache()
+    return {
+        "workload": "rope_swa_32k: q [1,32768,64,128] and k [1,32768,8,128] bf16, rot 42, base 1e4",
+        "rot_dim": rot,
+        "standalone": {"algorithmic_bytes": nbytes, "ms": round(ms, 5),
+                       "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                       "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "fraction_of_swa_prefill_time": round(ms / prefill_ms, 4)},
+        "fused": {"ms_rope_k_plus_prefill_rotating_q": round(res["k_then_fused_prefill"], 5),
+                  "ms_prefill_rotating_q": round(res["fused_prefill_only"], 5),
+                  "ms_plain_prefill": round(prefill_ms, 5),
+                  "overhead_vs_plain_prefill": round(res["k_then_fused_prefill"] / prefill_ms - 1.0, 4)},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -457,6 +506,10 @@ def main():
     if args.only == "mtp":
         print(json.dumps({"mtp_step": run_mtp(args, swa, torch, dev, stream)}), flush=True)
         return
+    if args.only == "rope":
+        print(json.dumps({"rope": run_rope(args, swa, torch, dev, stream, PREFILL_CONFIGS["swa_32k"], 0.28)}),
+              flush=True)
+        return
 
     cfg = PREFILL_CONFIGS["swa_32k"]
     pres, tensors = run_prefill(args, swa, torch, dev, stream, cfg)
@@ -482,6 +535,7 @@ def main():
         result["verify"] = run_verify(args, swa, torch, dev, stream)
         result["decode"] = run_verify(args, swa, torch, dev, stream, ("decode_ga_b64", "decode_swa_b64"))
         result["mtp_step"] = run_mtp(args, swa, torch, dev, stream)
+        result["rope"] = run_rope(args, swa, torch, dev, stream, cfg, pres["roofline"]["kernel_ms"])
     peaks = read_peaks()
     if peaks is not None:
         # fractions of the ceilings measured on this GPU: the SWA prefill moves

@@ -10,6 +10,8 @@ declared in ``include/swa_attn.h``).  The functions carry the C names:
     swa_mtp_accept_workspace_bytes(B, q_len, vocab)
     swa_mtp_greedy_accept(logits, draft, ...) -> (target, n_append)
     swa_cache_advance(cache_len, n_append)
+    swa_rope_apply(x, rot_dim, base, pos0=None, pos_offset=0)
+    swa_attn_prefill_rope(q, k, v, sinks, window, rot_dim, rope_base, q_offset=0, ...)
 
 They only check and marshal arguments (device, dtype, contiguity, shapes)
 and pass raw device pointers plus torch's current HIP stream; every step of
@@ -28,7 +30,7 @@ __all__ = [
     "SwaError", "library_path", "load_library", "swa_attn_prefill",
     "swa_attn_verify_workspace_bytes", "swa_attn_verify", "kv_ring_append",
     "swa_mtp_accept_workspace_bytes", "swa_mtp_greedy_accept", "swa_cache_advance",
-    "EXPORTED_SYMBOLS",
+    "swa_rope_apply", "rope_dims", "swa_attn_prefill_rope", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +40,8 @@ _lib = None
 SWA_F32, SWA_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("swa_status_string", "swa_attn_prefill", "swa_attn_verify_workspace_bytes",
                     "swa_attn_verify", "kv_ring_append", "swa_mtp_accept_workspace_bytes",
-                    "swa_mtp_greedy_accept", "swa_cache_advance")
+                    "swa_mtp_greedy_accept", "swa_cache_advance", "swa_rope_apply",
+                    "swa_attn_prefill_rope")
 
 
 class SwaError(RuntimeError):
@@ -78,6 +81,10 @@ def load_library():
     lib.swa_mtp_greedy_accept.restype = i
     lib.swa_cache_advance.argtypes = [p, p, i, p]
     lib.swa_cache_advance.restype = i
+    lib.swa_rope_apply.argtypes = [p, p, i, i, i, i, i, i, f, i, p]
+    lib.swa_rope_apply.restype = i
+    lib.swa_attn_prefill_rope.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, f, i, p]
+    lib.swa_attn_prefill_rope.restype = i
     _lib = lib
     return lib
 
@@ -148,6 +155,39 @@ def swa_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               B, Sq, Sk, Hq, Hkv, D, int(window), int(q_offset), float(sm_scale),
                               _dtype_code(q), _stream(stream))
     _check(st, "swa_attn_prefill")
+    return out
+
+
+def swa_attn_prefill_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          sinks: Optional[torch.Tensor], window: int, rot_dim: int, rope_base: float,
+                          q_offset: int = 0, sm_scale: Optional[float] = None,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Prefill with the queries rotated on load (q is only read; k must be
+    rotated already).  Raises SwaError (unsupported) outside the
+    sliding-window strip configurations."""
+    lib = load_library()
+    _dev(q, "q", ndim=4)
+    _dev(k, "k", q.dtype, 4)
+    _dev(v, "v", q.dtype, 4)
+    _dev(sinks, "sinks", torch.float32, 1)
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError("k/v shape mismatch")
+    if sinks is not None and sinks.shape[0] != Hq:
+        raise ValueError("sinks must have Hq entries")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", q.dtype, 4)
+        if out.shape != q.shape:
+            raise ValueError("out shape mismatch")
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    st = lib.swa_attn_prefill_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), B, Sq, Sk, Hq, Hkv, D,
+                                   int(window), int(q_offset), float(sm_scale), int(rot_dim),
+                                   float(rope_base), _dtype_code(q), _stream(stream))
+    _check(st, "swa_attn_prefill_rope")
     return out
 
 
@@ -277,3 +317,26 @@ def swa_cache_advance(cache_len: torch.Tensor, n_append: torch.Tensor, stream=No
         raise ValueError("cache_len and n_append must have the same length")
     st = lib.swa_cache_advance(_ptr(cache_len), _ptr(n_append), cache_len.shape[0], _stream(stream))
     _check(st, "swa_cache_advance")
+
+
+def rope_dims(D: int, factor: float = 0.334) -> int:
+    """Rotated dimensions per head for a partial-rotary factor: the largest
+    even number <= factor * D (42 for D = 128 at the model's 0.334)."""
+    return 2 * int(factor * D / 2)
+
+
+def swa_rope_apply(x: torch.Tensor, rot_dim: int, base: float, pos0: Optional[torch.Tensor] = None,
+                   pos_offset: int = 0, stream=None) -> torch.Tensor:
+    """Rotate the first rot_dim dims of every head of x [B,S,H,D] in place;
+    row s of request b is at position pos0[b] + pos_offset + s (pos0: int32
+    [B] on the GPU, or None for 0).  Returns x."""
+    lib = load_library()
+    _dev(x, "x", ndim=4)
+    _dev(pos0, "pos0", torch.int32, 1)
+    B, S, H, D = x.shape
+    if pos0 is not None and pos0.shape[0] != B:
+        raise ValueError("pos0 must have B entries")
+    st = lib.swa_rope_apply(_ptr(x), _ptr(pos0), int(pos_offset), B, S, H, D, int(rot_dim), float(base),
+                            _dtype_code(x), _stream(stream))
+    _check(st, "swa_rope_apply")
+    return x

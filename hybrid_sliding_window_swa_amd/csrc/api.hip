@@ -30,12 +30,10 @@ const char* swa_status_string(swa_status_t status) {
   return "unknown status";
 }
 
-swa_status_t swa_attn_prefill(const void* q, const void* k, const void* v, const float* sinks,
-                              void* o, int B, int Sq, int Sk, int Hq, int Hkv, int D, int window,
-                              int q_offset, float sm_scale, swa_dtype_t dtype, void* stream) {
-  swa_status_t st = swa_validate_prefill(q, k, v, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset,
-                                         sm_scale, dtype);
-  if (st != SWA_OK || B == 0 || Sq == 0) return st;
+namespace {
+
+PrefillArgs prefill_args(const void* q, const void* k, const void* v, const float* sinks, void* o, int B,
+                         int Sq, int Sk, int Hq, int Hkv, int D, int window, int q_offset, float sm_scale) {
   PrefillArgs a = {};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -52,6 +50,37 @@ swa_status_t swa_attn_prefill(const void* q, const void* k, const void* v, const
   a.q_offset = q_offset;
   a.scale = sm_scale;
   a.scale_log2 = sm_scale * kLog2eHost;
+  return a;
+}
+
+}  // namespace
+
+swa_status_t swa_attn_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                              void* o, int B, int Sq, int Sk, int Hq, int Hkv, int D, int window,
+                              int q_offset, float sm_scale, swa_dtype_t dtype, void* stream) {
+  swa_status_t st = swa_validate_prefill(q, k, v, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset,
+                                         sm_scale, dtype);
+  if (st != SWA_OK || B == 0 || Sq == 0) return st;
+  const PrefillArgs a = prefill_args(q, k, v, sinks, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset, sm_scale);
+  hipStream_t s = (hipStream_t)stream;
+  return from_hip(dtype == SWA_BF16 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s));
+}
+
+swa_status_t swa_attn_prefill_rope(const void* q, const void* k, const void* v, const float* sinks,
+                                   void* o, int B, int Sq, int Sk, int Hq, int Hkv, int D, int window,
+                                   int q_offset, float sm_scale, int rot_dim, float rope_base,
+                                   swa_dtype_t dtype, void* stream) {
+  swa_status_t st = swa_validate_prefill(q, k, v, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset,
+                                         sm_scale, dtype);
+  if (st != SWA_OK) return st;
+  if (rot_dim < 0 || (rot_dim & 1) || rot_dim > D) return SWA_ERR_SHAPE;
+  if (!(rope_base > 0.0f) || rope_base > 3.0e38f) return SWA_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0) return SWA_OK;
+  PrefillArgs a = prefill_args(q, k, v, sinks, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset, sm_scale);
+  if (rot_dim > 0 && (dtype != SWA_BF16 || rot_dim > D / 2 || !prefill_uses_strip(a)))
+    return SWA_ERR_UNSUPPORTED;
+  a.rope_hr = rot_dim / 2;
+  for (int i = 0; i < a.rope_hr; ++i) a.rope_inv_freq[i] = pow((double)rope_base, -2.0 * i / rot_dim);
   hipStream_t s = (hipStream_t)stream;
   return from_hip(dtype == SWA_BF16 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s));
 }
@@ -162,6 +191,25 @@ swa_status_t swa_cache_advance(int32_t* cache_len, const int32_t* n_append, int 
   swa_status_t st = swa_validate_advance(cache_len, n_append, B);
   if (st != SWA_OK || B == 0) return st;
   return from_hip(launch_advance(cache_len, n_append, B, (hipStream_t)stream));
+}
+
+swa_status_t swa_rope_apply(void* x, const int32_t* pos0, int pos_offset, int B, int S, int H, int D,
+                            int rot_dim, float base, swa_dtype_t dtype, void* stream) {
+  swa_status_t st = swa_validate_rope(x, B, S, H, D, rot_dim, pos_offset, base, dtype);
+  if (st != SWA_OK || B == 0 || S == 0 || rot_dim == 0) return st;
+  RopeArgs a = {};
+  a.x = x;
+  a.pos0 = pos0;
+  a.pos_offset = pos_offset;
+  a.rows = (long)B * S * H;
+  a.B = B;
+  a.S = S;
+  a.H = H;
+  a.D = D;
+  a.rot = rot_dim;
+  a.esize = dtype == SWA_BF16 ? 2 : 4;
+  a.log2_base = log2((double)base);
+  return from_hip(launch_rope(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

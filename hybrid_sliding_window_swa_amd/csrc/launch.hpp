@@ -17,6 +17,11 @@ struct PrefillArgs {
   int window, q_offset;
   float scale;        // sm_scale
   float scale_log2;   // sm_scale * log2(e)
+  // partial rotary embedding of the queries, applied as they are staged
+  // (sliding-window strip kernel only): rope_hr pairs (i, i + rope_hr), pair
+  // i turned by position * rope_inv_freq[i]; rope_hr == 0 leaves q as is
+  int rope_hr;
+  double rope_inv_freq[32];
   // filled by the launcher
   int n_tb, total, per_xcd;
 };
@@ -52,6 +57,9 @@ struct AppendArgs {
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+// Whether launch_prefill_bf16 runs these arguments on the sliding-window strip
+// kernel (the only prefill kernel that rotates queries as it stages them).
+bool prefill_uses_strip(const PrefillArgs& a);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 
 // Verify plan shared by the workspace query and the launch.
@@ -89,5 +97,24 @@ struct AcceptPlan {
 AcceptPlan plan_accept(int B, int T, long V);
 hipError_t launch_accept(AcceptArgs a, const AcceptPlan& p, hipStream_t s);
 hipError_t launch_advance(int32_t* cache_len, const int32_t* n_append, int B, hipStream_t s);
+
+struct RopeArgs {
+  void* x;               // [B][S][H][D], rotated in place
+  const int32_t* pos0;   // [B] or null
+  long rows;             // B * S * H
+  int pos_offset;
+  int B, S, H, D, rot, esize;
+  double log2_base;
+  int nv, pitch_dw, rows_blk;  // set by the launcher
+};
+
+struct RopePlan {
+  int nv;          // 16-byte vectors per row that hold the rotated dimensions
+  int pitch_dw;    // LDS row pitch in dwords (odd)
+  int rows_blk;    // rows per workgroup
+  size_t lds_bytes;
+};
+RopePlan plan_rope(int H, int D, int rot, int esize);
+hipError_t launch_rope(RopeArgs a, hipStream_t s);
 
 }  // namespace swa

@@ -470,7 +470,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
 // converts between that layout and the MFMA register layout.
 constexpr int kRingTiles = 6;
 
-template <int D, int G>
+constexpr double kRopeTwoPi = 6.283185307179586476925286766559;
+constexpr double kRopeInvTwoPi = 0.15915494309189533576888376337251;
+
+template <int D, int G, bool ROPE>
 __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p) {
   using Gm = TileGeom<D>;
   constexpr int NW = G;
@@ -486,6 +489,10 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
   __shared__ __attribute__((aligned(16))) uint16_t k_ring[NR][Gm::K_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t v_ring[NR][Gm::V_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t stage_lds[NW][Stg::ELEMS];
+  // rotary embedding of the queries: cos / sin of (token, pair) for a wave's
+  // TW tokens (entry tok * 32 + i), and of the turn by one block (TB tokens)
+  __shared__ float2 rope_tab[ROPE ? NW : 1][ROPE ? TW * 32 : 1];
+  __shared__ float2 rope_step[ROPE ? 32 : 1];
 
   // strip -> (b, g, block range)
   const int strip = blockIdx.x;
@@ -541,8 +548,71 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
       for (int it = 0; it < SIT; ++it) qpre[hh][it] = buf_load16(r, rows_voff(it, hh), 0);
   };
   QState<D> st;
+  // Partial rotary embedding of the staged first half-head (every rotated
+  // dimension lies there: 2 * rope_hr <= D / 2) of rows at tokens tw0 ...
+  // The wave's TW x rope_hr (cos, sin) live in LDS from block to block: the
+  // first block of a strip and every 8th after it computes them exactly (the
+  // angle reduced modulo 2*pi in fp64, then fp32 sincosf); the blocks between
+  // turn the previous entries by the one-block step (TB more tokens), four
+  // fp32 FMAs instead of a sine and a cosine.  Then all 64 lanes rotate the
+  // 32 x rope_hr pairs in LDS, rounding back to bf16 (nearest even).
+  auto rope_angle = [&](long pos, int i) {
+    const double th = (double)pos * p.rope_inv_freq[i];
+    const double r = th - rint(th * kRopeInvTwoPi) * kRopeTwoPi;
+    float sn, cs;
+    sincosf((float)r, &sn, &cs);
+    return make_float2(cs, sn);
+  };
+  auto rotate_staged = [&](int tw0, bool exact) {
+    const int hr = p.rope_hr;
+    float2* tab = rope_tab[wv];
+    // an opaque copy of the lane index: the per-lane addresses below are
+    // recomputed here instead of being hoisted out of the block loop, where
+    // they would hold registers through the attention itself
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    for (int e = ln; e < TW * 32; e += 64) {
+      const int tok = e >> 5, i = e & 31;
+      if (i < hr) {
+        if (exact) {
+          tab[e] = rope_angle(p.q_offset + tw0 + tok, i);
+        } else {
+          const float2 c = tab[e], d = rope_step[i];
+          tab[e] = make_float2(c.x * d.x - c.y * d.y, c.y * d.x + c.x * d.y);
+        }
+      }
+    }
+    wave_lds_sync();
+    // lane ln takes pairs it = ln + 64 j (row m = it / hr, pair i = it % hr);
+    // every read is issued before the first write so the wave waits for LDS once
+    constexpr int kMaxPairs = 32 * 32 / 64;
+    const float inv_hr = 1.0f / (float)hr;
+    uint32_t uw[kMaxPairs];
+    float2 cs[kMaxPairs];
+    int at[kMaxPairs];
+#pragma unroll
+    for (int j = 0; j < kMaxPairs; ++j) {
+      const int it = ln + 64 * j;
+      if (it < 32 * hr) {
+        const int m = (int)(((float)it + 0.5f) * inv_hr), i = it - m * hr;
+        at[j] = Stg::off(m, i);
+        uw[j] = (uint32_t)stg[at[j]] | ((uint32_t)stg[at[j] + hr] << 16);
+        cs[j] = tab[(m / G) * 32 + i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxPairs; ++j) {
+      const int it = ln + 64 * j;
+      if (it < 32 * hr) {
+        const float u = __uint_as_float(uw[j] << 16), w = __uint_as_float(uw[j] & 0xffff0000u);
+        stg[at[j]] = __builtin_bit_cast(uint16_t, (__bf16)(u * cs[j].x - w * cs[j].y));
+        stg[at[j] + hr] = __builtin_bit_cast(uint16_t, (__bf16)(w * cs[j].x + u * cs[j].y));
+      }
+    }
+    wave_lds_sync();
+  };
   // whole rows -> LDS -> MFMA B-operand layout (row col, d = 16c + 8*half)
-  auto stage_q = [&]() {
+  auto stage_q = [&](int tw0, bool exact) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
@@ -551,6 +621,9 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
         *(u32x4*)&stg[Stg::off(u / HC, (u % HC) * 8)] = qpre[hh][it];
       }
       wave_lds_sync();
+      if constexpr (ROPE) {
+        if (hh == 0) rotate_staged(tw0, exact);
+      }
       const lds_u16* sbase = lane_base(lds_addr(stg), Stg::k_lane_off(lane));
 #pragma unroll
       for (int c = 0; c < Gm::NC / 2; ++c)
@@ -596,7 +669,10 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
     sg.load(kg, vg, kv_tok, kt * KT, p.Sk, tid);
     sg.store(k_ring[kt % NR], v_ring[kt % NR], tid);
   }
-  stage_q();
+  if constexpr (ROPE) {
+    if (tid < p.rope_hr) rope_step[tid] = rope_angle(TB, tid);
+  }
+  stage_q(blk0 * TB + wv * TW, true);
   // Drain every prologue load here, so that inside the loop the only loads in
   // flight are the prefetches and no wait inserted for the current queries
   // can stall on them.
@@ -640,7 +716,7 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
       sg.store(k_ring[new_kt % NR], v_ring[new_kt % NR], tid);
       loaded_hi = new_kt;
     }
-    if (nxt) stage_q();
+    if (nxt) stage_q(tw0 + TB, ((blk + 1 - blk0) & 7) == 0);
     __syncthreads();
   }
 }
@@ -660,6 +736,7 @@ static hipError_t launch_generic(const PrefillArgs& a0, hipStream_t stream) {
 
 template <int D, int G>
 static hipError_t launch_strip(const PrefillArgs& a0, int num_cu, hipStream_t stream) {
+  // prefill_swa_strip_kernel<D, G, true> also rotates the queries
   PrefillArgs a = a0;
   a.n_tb = (a.Sq + 31) / 32;
   const int bgs = a.B * a.Hkv;
@@ -668,22 +745,30 @@ static hipError_t launch_strip(const PrefillArgs& a0, int num_cu, hipStream_t st
   if (spb > a.n_tb) spb = a.n_tb;
   a.per_xcd = spb;
   a.total = bgs * spb;
-  hipLaunchKernelGGL((prefill_swa_strip_kernel<D, G>), dim3(a.total), dim3(G * 64), 0, stream, a);
+  if (a.rope_hr > 0)
+    hipLaunchKernelGGL((prefill_swa_strip_kernel<D, G, true>), dim3(a.total), dim3(G * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_swa_strip_kernel<D, G, false>), dim3(a.total), dim3(G * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 static int floor_div(int x, int y) { return x >= 0 ? x / y : -((-x + y - 1) / y); }
 
-template <int D>
-static hipError_t launch_d(const PrefillArgs& a, int G, hipStream_t s) {
+bool prefill_uses_strip(const PrefillArgs& a) {
   // The strip kernel's ring must hold a block's window plus the next block's
   // new tile.  Blocks start at positions p = q_offset (mod 32), and the keys
   // p - W + 1 .. p + 31 of a block span floor((a + 31) / 32) -
   // floor((a - W + 1) / 32) + 1 tiles with a = q_offset mod 32.
+  const int G = a.Hq / a.Hkv;
   const int al = a.q_offset % KT;
   const int span = a.window > 0 ? (al + KT - 1) / KT - floor_div(al - a.window + 1, KT) + 1 : 0;
   const bool ring_fits = a.window > 0 && span + 1 <= kRingTiles;
-  if (ring_fits && (G == 8 || G == 4)) {
+  return ring_fits && (G == 8 || G == 4) && (a.D == 64 || a.D == 128);
+}
+
+template <int D>
+static hipError_t launch_d(const PrefillArgs& a, int G, hipStream_t s) {
+  if (prefill_uses_strip(a)) {
     int dev = 0, num_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||

@@ -125,3 +125,23 @@ swa_status_t swa_validate_advance(const void *cache_len, const void *n_append, i
         return SWA_ERR_NULL;
     return SWA_OK;
 }
+
+swa_status_t swa_validate_rope(const void *x, int B, int S, int H, int D, int rot_dim,
+                               int pos_offset, float base, swa_dtype_t dtype)
+{
+    if (!dtype_ok(dtype))
+        return SWA_ERR_UNSUPPORTED;
+    if (B < 0 || S < 0 || H <= 0 || pos_offset < 0)
+        return SWA_ERR_SHAPE;
+    if (D <= 0 || D > 256 || D % 8 != 0 || rot_dim < 0 || rot_dim > D || (rot_dim & 1))
+        return SWA_ERR_SHAPE;
+    if (!(base > 0.0f) || base > 3.0e38f)
+        return SWA_ERR_UNSUPPORTED;
+    if (B == 0 || S == 0 || rot_dim == 0)
+        return SWA_OK;
+    if (!x)
+        return SWA_ERR_NULL;
+    if (((unsigned long long)(size_t)x) % 16 != 0)
+        return SWA_ERR_UNSUPPORTED;
+    return SWA_OK;
+}

@@ -35,6 +35,10 @@ swa_status_t swa_validate_accept(const void *logits, const void *draft, const vo
 
 swa_status_t swa_validate_advance(const void *cache_len, const void *n_append, int B);
 
+/* D % 8 == 0, D <= 256, rot_dim even in [0, D], x 16-byte aligned. */
+swa_status_t swa_validate_rope(const void *x, int B, int S, int H, int D, int rot_dim,
+                               int pos_offset, float base, swa_dtype_t dtype);
+
 #ifdef __cplusplus
 }
 #endif

@@ -103,6 +103,29 @@ SWA_API swa_status_t swa_attn_prefill(const void *q, const void *k, const void *
                               swa_dtype_t dtype, void *stream);
 
 /*
+ * Causal prefill with the queries' partial rotary embedding applied as they
+ * are loaded: O = attention(R(q), k, v), where R rotates the first rot_dim
+ * dimensions of every query head by its position (q_offset + r) exactly as
+ * swa_rope_apply does (pairs (i, i + rot_dim/2), angle pos *
+ * rope_base^(-2i/rot_dim); technical-report digest, "Pre-training", and the
+ * model card config extract for the factor 0.334).  q is only read.  The keys
+ * must already be rotated (swa_rope_apply once, or a cache of rotated keys).
+ * Other arguments as swa_attn_prefill; rot_dim == 0 is swa_attn_prefill.
+ * Supported with rot_dim > 0: SWA_BF16, rot_dim even and <= D / 2, and the
+ * sliding-window configurations of the strip kernel (window >= 1 with at most
+ * about 128 + 31 keys per 32-query block, Hq / Hkv of 4 or 8); otherwise
+ * SWA_ERR_UNSUPPORTED, and the caller applies swa_rope_apply to a copy of q
+ * and calls swa_attn_prefill (for global attention that extra pass costs
+ * under one percent of the prefill).
+ */
+SWA_API swa_status_t swa_attn_prefill_rope(const void *q, const void *k, const void *v,
+                                   const float *sinks, void *o,
+                                   int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                                   int window, int q_offset, float sm_scale,
+                                   int rot_dim, float rope_base,
+                                   swa_dtype_t dtype, void *stream);
+
+/*
  * Bytes of device workspace swa_attn_verify needs for these sizes (split-KV
  * partial results: running max, running sum and unnormalised output per
  * query row and split).  0 when the arguments are invalid.
@@ -204,6 +227,31 @@ SWA_API swa_status_t swa_mtp_greedy_accept(const void *logits, const int32_t *dr
  */
 SWA_API swa_status_t swa_cache_advance(int32_t *cache_len, const int32_t *n_append, int B,
                                void *stream);
+
+/*
+ * Partial rotary position embedding, in place, on query or key rows before
+ * attention (technical-report digest, "Pre-training": RoPE base 10000 for the
+ * sliding-window layers, 640000 for the global layers, 5000000 after the
+ * 256K extension; model card config extract: partial_rotary_factor 0.334).
+ *   x  [B, S, H, D] DEVICE (bf16 or fp32), 16-byte aligned, rotated in place.
+ *      Row s of request b sits at position (pos0 ? pos0[b] : 0) + pos_offset + s.
+ *   pos0  [B] int32 DEVICE or NULL (e.g. cache_len for the rows under
+ *      verification); pos_offset >= 0 (e.g. q_offset for a prefill chunk).
+ *   rot_dim  even, 0 <= rot_dim <= D: the first rot_dim dimensions of each
+ *      head rotate in rot_dim/2 pairs (i, i + rot_dim/2) by the angle
+ *      pos * base^(-2i / rot_dim); the rest are untouched.  With the model's
+ *      factor 0.334, rot_dim = 2 * floor(0.334 * D / 2) (42 for D = 128).
+ *   base  finite and > 0.
+ * The angle is reduced modulo 2*pi in fp64 before an fp32 sine / cosine, so
+ * rotations stay accurate at positions of 2^18 and beyond.  Keys go through
+ * it once (before prefill, or k_new before verify and kv_ring_append, so the
+ * caches hold rotated keys); queries before every attention call.
+ * Requires D % 8 == 0 and D <= 256.  Device-side precondition: positions are
+ * >= 0 and below 2^31.  B == 0, S == 0 or rot_dim == 0 is a no-op.
+ */
+SWA_API swa_status_t swa_rope_apply(void *x, const int32_t *pos0, int pos_offset,
+                            int B, int S, int H, int D, int rot_dim, float base,
+                            swa_dtype_t dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -172,3 +172,42 @@ def test_advance_validation(lib):
     assert lib.swa_cache_advance(P(0), P(1), 4, None) == NULL
     assert lib.swa_cache_advance(P(1), P(1), -1, None) == SHAPE
     assert lib.swa_cache_advance(P(0), P(0), 0, None) == OK
+
+
+def _rope(lib, x=256, B=2, S=8, H=8, D=128, rot=42, off=0, base=10000.0, dt=BF16):
+    P = lambda v: ctypes.c_void_p(v) if v else None
+    return lib.swa_rope_apply(P(x), None, off, B, S, H, D, rot, base, dt, None)
+
+
+def test_rope_validation(lib):
+    assert _rope(lib, x=0) == NULL
+    assert _rope(lib, x=264) == UNSUP            # not 16-byte aligned
+    assert _rope(lib, rot=43) == SHAPE           # odd
+    assert _rope(lib, rot=130) == SHAPE          # beyond D
+    assert _rope(lib, D=100) == SHAPE            # D % 8 != 0
+    assert _rope(lib, D=264, rot=42) == SHAPE    # D > 256
+    assert _rope(lib, off=-1) == SHAPE
+    assert _rope(lib, H=0) == SHAPE
+    assert _rope(lib, base=0.0) == UNSUP
+    assert _rope(lib, base=float("nan")) == UNSUP
+    assert _rope(lib, dt=5) == UNSUP
+    assert _rope(lib, x=0, B=0) == OK and _rope(lib, x=0, S=0) == OK and _rope(lib, x=0, rot=0) == OK
+
+
+def test_rope_dims_rule():
+    assert swa.rope_dims(128) == 42 and swa.rope_dims(64) == 20 and swa.rope_dims(192) == 64
+
+
+def test_prefill_rope_validation(lib):
+    P = lambda v: ctypes.c_void_p(v) if v else None
+    f = lambda rot=42, W=128, Hq=16, Hkv=2, D=128, dt=BF16, base=10000.0, ptr=256: lib.swa_attn_prefill_rope(
+        P(ptr), P(ptr), P(ptr), None, P(ptr), 1, 64, 64, Hq, Hkv, D, W, 0, 0.1, rot, base, dt, None)
+    assert f(rot=41) == SHAPE
+    assert f(rot=130) == SHAPE
+    assert f(base=-1.0) == UNSUP
+    assert f(ptr=0) == NULL
+    # host-visible unsupported configurations return before any launch
+    assert f(rot=66) == UNSUP          # beyond D / 2
+    assert f(W=0) == UNSUP             # global attention: not the strip kernel
+    assert f(Hq=32, Hkv=2) == UNSUP    # G = 16
+    assert f(dt=F32) == UNSUP
