@@ -19,7 +19,10 @@ accept, accept, reject, discard example among them), tie breaking and
 numpy's argmax.  The partial rotary embedding is pinned by closed forms
 (one-hot inputs at known angles), position 0 as the identity, composition of
 rotations, preserved pair norms and the relative-position property of the
-rotated dot product.
+rotated dot product.  The backward is pinned by central finite differences
+of the forward oracle, by torch fp64 autograd through scaled-dot-product
+attention with the sink column, and by the sink-gradient identity
+dsink_h = -sum_i p_sink,i <dO_i, O_i>.
 """
 from __future__ import annotations
 
@@ -68,6 +71,9 @@ def _bind(lib):
     lib.oracle_greedy_accept.argtypes = [c_f, ctypes.POINTER(ctypes.c_int32), i, i, l,
                                          ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
     lib.oracle_greedy_accept.restype = i
+    lib.oracle_prefill_backward.argtypes = [c_f, c_f, c_f, c_d, c_f, c_d, c_d, c_d, c_d,
+                                            i, i, i, i, i, i, i, i, d]
+    lib.oracle_prefill_backward.restype = i
     lib.oracle_rope.argtypes = [c_d, c_d, c_i64, l, i, i, i, d]
     lib.oracle_rope.restype = i
     lib.oracle_num_threads.argtypes = []
@@ -215,6 +221,28 @@ def verify(q, k_new, v_new, k_hist, v_hist, hist_base, cache_len, sinks=None,
                               B, T, Hq, Hkv, D, Hlen, int(window), float(scale))
     _check(rc, "verify")
     return o
+
+
+def prefill_backward(q, k, v, dout, sinks=None, window: int = 0, q_offset: int = 0, scale: float = None):
+    """Gradients of sum(dout * prefill(q, k, v, sinks)): returns (dq, dk, dv,
+    dsink) as float64 (dsink [Hq], zeros when sinks is None)."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, Sq, Hq, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    assert dout.shape == q.shape and v.shape == k.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    s = None if sinks is None else _f64(sinks)
+    dq = np.empty(q.shape, np.float64)
+    dk = np.empty(k.shape, np.float64)
+    dv = np.empty(k.shape, np.float64)
+    ds = np.zeros((Hq,), np.float64)
+    rc = load().oracle_prefill_backward(_p(q, ctypes.c_float), _p(k, ctypes.c_float), _p(v, ctypes.c_float),
+                                        _nullable_d(s), _p(dout, ctypes.c_float), _p(dq, ctypes.c_double),
+                                        _p(dk, ctypes.c_double), _p(dv, ctypes.c_double), _p(ds, ctypes.c_double),
+                                        B, Sq, Sk, Hq, Hkv, D, int(window), int(q_offset), float(scale))
+    _check(rc, "prefill_backward")
+    return dq, dk, dv, ds
 
 
 def ring_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,

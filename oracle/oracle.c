@@ -411,3 +411,114 @@ int oracle_rope(const double *x, double *out, const int64_t *pos, long rows, int
     }
     return ORC_OK;
 }
+
+/*
+ * Backward of the prefill: gradients of L = sum(dout * O) with respect to q,
+ * k, v and the sinks (the definition above differentiated; the pages give
+ * no training kernel, and the MTP-accelerated RL training the report digest
+ * describes in "Model Architecture" needs these gradients).
+ *   For a query row with weights w_j (the softmax over its window with the
+ *   sink in the denominator), sink mass p_s and output O:
+ *     delta  = <dout, O>
+ *     dP_j   = <dout, V_j>
+ *     dS_j   = w_j * (dP_j - delta)
+ *     dq     = sm_scale * sum_j dS_j K_j
+ *     dK_j  += sm_scale * dS_j q         dV_j += w_j * dout
+ *     dsink_h += -p_s * delta            (the sink logit is not scaled and
+ *                                         carries no value)
+ *   q, dout [B, Sq, Hq, D]; k, v [B, Sk, Hkv, D] (fp32 in); dq, dk, dv fp64 of
+ *   the same shapes; dsink [Hq] fp64 (ignored when sinks == NULL).
+ * One thread owns every query row of a (request, KV head), so the key
+ * gradients need no atomics; per-request sink gradients are summed last.
+ */
+int oracle_prefill_backward(const float *q, const float *k, const float *v, const double *sinks,
+                            const float *dout, double *dq, double *dk, double *dv, double *dsink,
+                            int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                            int window, int q_offset, double sm_scale)
+{
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 ||
+        q_offset < 0 || (long)q_offset + Sq > Sk)
+        return ORC_BAD_ARGS;
+    const int G = Hq / Hkv;
+    const long groups = (long)B * Hkv;
+    double *dsink_b = (double *)calloc((size_t)B * Hq + 1, sizeof(double));
+    if (!dsink_b)
+        return ORC_NO_MEMORY;
+    memset(dk, 0, sizeof(double) * (size_t)B * Sk * Hkv * D);
+    memset(dv, 0, sizeof(double) * (size_t)B * Sk * Hkv * D);
+    int err = ORC_OK;
+
+#pragma omp parallel
+    {
+        double *sbuf = (double *)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        double *wbuf = (double *)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        double *obuf = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!sbuf || !wbuf || !obuf) {
+#pragma omp atomic write
+            err = ORC_NO_MEMORY;
+        } else {
+            long bg;
+#pragma omp for schedule(dynamic, 1)
+            for (bg = 0; bg < groups; ++bg) {
+                const long b = bg / Hkv;
+                const int g = (int)(bg % Hkv);
+                long r;
+                int hh, d;
+                for (r = 0; r < Sq; ++r) {
+                    for (hh = 0; hh < G; ++hh) {
+                        const int h = g * G + hh;
+                        const long i = (long)q_offset + r;
+                        const long lo = window_lo(i, window);
+                        const long n = i - lo + 1;
+                        const long row = (b * Sq + r) * Hq + h;
+                        const float *qv = q + row * (long)D;
+                        const float *go = dout + row * (long)D;
+                        const float *kb = k + ((b * Sk + lo) * Hkv + g) * (long)D;
+                        const float *vb = v + ((b * Sk + lo) * Hkv + g) * (long)D;
+                        double psink = 0.0;
+                        attend(qv, D, sm_scale, sinks ? &sinks[h] : NULL, kb, vb, n, (long)Hkv * D,
+                               NULL, NULL, 0, 0, obuf, NULL, &psink, wbuf, sbuf);
+                        double delta = 0.0;
+                        for (d = 0; d < D; ++d)
+                            delta += (double)go[d] * obuf[d];
+                        double *dqv = dq + row * (long)D;
+                        for (d = 0; d < D; ++d)
+                            dqv[d] = 0.0;
+                        long j;
+                        for (j = 0; j < n; ++j) {
+                            const float *kr = kb + j * (long)Hkv * D;
+                            const float *vr = vb + j * (long)Hkv * D;
+                            double dp = 0.0;
+                            for (d = 0; d < D; ++d)
+                                dp += (double)go[d] * (double)vr[d];
+                            const double ds = wbuf[j] * (dp - delta);
+                            double *dkr = dk + ((b * Sk + lo + j) * Hkv + g) * (long)D;
+                            double *dvr = dv + ((b * Sk + lo + j) * Hkv + g) * (long)D;
+                            for (d = 0; d < D; ++d) {
+                                dqv[d] += sm_scale * ds * (double)kr[d];
+                                dkr[d] += sm_scale * ds * (double)qv[d];
+                                dvr[d] += wbuf[j] * (double)go[d];
+                            }
+                        }
+                        dsink_b[b * Hq + h] += -psink * delta;
+                    }
+                }
+            }
+        }
+        free(sbuf);
+        free(wbuf);
+        free(obuf);
+    }
+    if (dsink) {
+        int h;
+        long b;
+        for (h = 0; h < Hq; ++h) {
+            double acc = 0.0;
+            for (b = 0; b < B; ++b)
+                acc += dsink_b[b * Hq + h];
+            dsink[h] = sinks ? acc : 0.0;
+        }
+    }
+    free(dsink_b);
+    return err;
+}

@@ -27,6 +27,10 @@ What pins what:
     pos * base^(-2i/rot) by hand), position 0 as the identity, R(a) R(b) =
     R(a + b), preserved pair norms with untouched tail dimensions, and the
     relative-position property <R(p+c) q, R(p'+c) k> = <R(p) q, R(p') k>.
+  * backward: central finite differences of the forward oracle's loss
+    sum(dO * O) on inputs on the bf16 grid (so the +-2^-10 steps are exact in
+    fp32), torch fp64 autograd through the SDPA-with-sink-column reference,
+    and dsink_h = -sum_i p_sink,i <dO_i, O_i> from the forward's sink mass.
 """
 from __future__ import annotations
 
@@ -420,6 +424,97 @@ def pin_rope_relative_position():
         assert abs(dot - ref) < 1e-9
 
 
+BWD_CASES = [
+    # B, Sq, Sk, Hq, Hkv, D, window, q_offset
+    (1, 7, 7, 2, 1, 4, 3, 0),
+    (2, 5, 9, 4, 2, 4, 0, 4),
+    (1, 6, 6, 2, 2, 3, 1, 0),
+]
+
+
+def _bwd_inputs(n, B, Sq, Sk, Hq, Hkv, D):
+    r = lambda shape, tag: _rand(shape, "bwd", tag, n).to(torch.bfloat16).double()
+    return (r((B, Sq, Hq, D), "q"), r((B, Sk, Hkv, D), "k"), r((B, Sk, Hkv, D), "v"),
+            r((B, Sq, Hq, D), "do"), _rand((Hq,), "bwd", "s", n))
+
+
+def pin_backward_finite_differences():
+    eps = 2.0 ** -10
+    rng = np.random.default_rng(3)
+    for n, (B, Sq, Sk, Hq, Hkv, D, W, off) in enumerate(BWD_CASES):
+        q, k, v, do, sinks = _bwd_inputs(n, B, Sq, Sk, Hq, Hkv, D)
+        scale = 0.7
+        grads = oracle.prefill_backward(q, k, v, do, sinks, W, off, scale)
+        dn = do.numpy()
+
+        def loss(qq, kk, vv, ss):
+            return float((oracle.prefill(qq, kk, vv, ss, W, off, scale) * dn).sum())
+
+        for which, (x, g) in enumerate(zip((q, k, v), grads[:3])):
+            flat = x.reshape(-1)
+            for idx in rng.choice(flat.numel(), size=min(10, flat.numel()), replace=False):
+                args = [q, k, v]
+                hi, lo = flat.clone(), flat.clone()
+                hi[idx] += eps
+                lo[idx] -= eps
+                args[which] = hi.view(x.shape)
+                f_hi = loss(*args, sinks)
+                args[which] = lo.view(x.shape)
+                f_lo = loss(*args, sinks)
+                fd = (f_hi - f_lo) / (2 * eps)
+                assert abs(fd - g.reshape(-1)[idx]) < 2e-5, (n, which, int(idx), fd, g.reshape(-1)[idx])
+        for h in range(Hq):
+            e = torch.zeros(Hq, dtype=torch.float64)
+            e[h] = 1e-4
+            fd = (loss(q, k, v, sinks + e) - loss(q, k, v, sinks - e)) / 2e-4
+            assert abs(fd - grads[3][h]) < 1e-6, (n, h, fd, grads[3][h])
+
+
+def pin_backward_vs_torch_autograd():
+    for n, (B, Sq, Sk, Hq, Hkv, D, W, off) in enumerate(BWD_CASES + [(2, 17, 23, 4, 2, 16, 4, 6)]):
+        q, k, v, do, sinks = _bwd_inputs(n + 10, B, Sq, Sk, Hq, Hkv, D)
+        scale = 1.0 / math.sqrt(D)
+        got = oracle.prefill_backward(q, k, v, do, sinks, W, off, scale)
+        ts = [t.clone().requires_grad_(True) for t in (q, k, v, sinks)]
+        G = Hq // Hkv
+        qt = ts[0].permute(0, 2, 1, 3)
+        kt = ts[1].repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+        vt = ts[2].repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+        i = torch.arange(Sq).view(-1, 1) + off
+        j = torch.arange(Sk).view(1, -1)
+        allowed = j <= i
+        if W > 0:
+            allowed &= j > i - W
+        bias = torch.zeros(Sq, Sk, dtype=torch.float64).masked_fill(~allowed, float("-inf"))
+        bias = bias.view(1, 1, Sq, Sk).expand(B, Hq, Sq, Sk)
+        zk = torch.zeros(B, Hq, 1, D, dtype=torch.float64)
+        kt = torch.cat([kt, zk], dim=2)
+        vt = torch.cat([vt, zk], dim=2)
+        bias = torch.cat([bias, ts[3].view(1, Hq, 1, 1).expand(B, Hq, Sq, 1)], dim=3)
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous(),
+                                                             attn_mask=bias, scale=scale)
+        (o.permute(0, 2, 1, 3) * do).sum().backward()
+        for name, a, t in zip(("dq", "dk", "dv", "dsink"), got, ts):
+            err = np.abs(a - t.grad.numpy()).max()
+            assert err < 1e-10, (n, name, err)
+
+
+def pin_backward_sink_identity():
+    B, Sq, Sk, Hq, Hkv, D, W, off = 2, 12, 12, 4, 2, 8, 5, 0
+    q, k, v, do, sinks = _bwd_inputs(99, B, Sq, Sk, Hq, Hkv, D)
+    fwd = oracle.prefill(q, k, v, sinks, W, off, 0.5, want_psink=True)
+    delta = (fwd["o"] * do.numpy()).sum(-1)                       # [B, Sq, Hq]
+    ref = -(fwd["psink"] * delta).sum(axis=(0, 1))
+    got = oracle.prefill_backward(q, k, v, do, sinks, W, off, 0.5)[3]
+    assert np.abs(got - ref).max() < 1e-12
+    # no sink: no sink gradient, and the other gradients equal those of -inf
+    a = oracle.prefill_backward(q, k, v, do, None, W, off, 0.5)
+    b = oracle.prefill_backward(q, k, v, do, torch.full((Hq,), float("-inf")), W, off, 0.5)
+    assert not a[3].any()
+    for x, y in zip(a[:3], b[:3]):
+        assert np.abs(x - y).max() < 1e-12
+
+
 ALL_PINS = [
     pin_sdpa_with_sink_column,
     pin_no_sink_is_band_softmax,
@@ -440,4 +535,7 @@ ALL_PINS = [
     pin_rope_closed_form,
     pin_rope_identity_composition_norm,
     pin_rope_relative_position,
+    pin_backward_finite_differences,
+    pin_backward_vs_torch_autograd,
+    pin_backward_sink_identity,
 ]

@@ -5,7 +5,8 @@ Each mutant is a copy of oracle/oracle.c with one plausible mistake planted
 index, values swapped for keys, an ignored causal offset, a wrong sign in the
 exponent, a reversed operand, a verify that hides the query's own token, an argmax
 that breaks ties the other way, an acceptance that continues past a
-rejection, a rotary embedding with the wrong pairing or sign, ...).
+rejection, a rotary embedding with the wrong pairing or sign, a backward without
+the delta term or with the sink gradient's sign flipped, ...).
 Each is compiled with gcc into a temporary library and every pin is run
 against it: at least one pin must fail, or the pins would not detect that
 mistake.
@@ -48,6 +49,12 @@ MUTANTS = {
     "rope_sign_flipped": ("orow[i] = a * c - b * s;", "orow[i] = a * c + b * s;"),
     "rope_frequency_over_head_dim": ("pow(base, -2.0 * i / rot)", "pow(base, -2.0 * i / D)"),
     "rope_tail_dropped": ("orow[i] = xr[i];", "orow[i] = i < rot ? xr[i] : 0.0;"),
+    "backward_delta_dropped": ("const double ds = wbuf[j] * (dp - delta);", "const double ds = wbuf[j] * dp;"),
+    "backward_dk_unscaled": ("dkr[d] += sm_scale * ds * (double)qv[d];", "dkr[d] += ds * (double)qv[d];"),
+    "backward_dv_uses_ds": ("dvr[d] += wbuf[j] * (double)go[d];", "dvr[d] += ds * (double)go[d];"),
+    "backward_dq_uses_values": ("dqv[d] += sm_scale * ds * (double)kr[d];",
+                                "dqv[d] += sm_scale * ds * (double)vr[d];"),
+    "backward_sink_sign": ("dsink_b[b * Hq + h] += -psink * delta;", "dsink_b[b * Hq + h] += psink * delta;"),
 }
 
 
