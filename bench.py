@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="time the SWA prefill only")
-    ap.add_argument("--only", choices=["prefill", "ga", "verify", "mtp", "rope"], default=None,
+    ap.add_argument("--only", choices=["prefill", "ga", "verify", "mtp", "rope", "backward"], default=None,
                     help="run one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--settle-seconds", type=float, default=0.5,
                     help="untimed repetition of each step before its warmup, so the clocks are at "
@@ -470,6 +470,49 @@ def run_rope(args, swa, torch, dev, stream, cfg, prefill_ms):
     }
 
 
+def run_backward(args, swa, torch, dev, stream, cfg):
+    """One training step of the attention on the 32768-token sliding-window
+    workload: the forward that saves the log-sum-exp, and the backward (dq,
+    dk, dv, dsink).  Algorithmic FLOP per (query head, in-window key) pair:
+    4*D forward (QK^T, PV) and 10*D backward (QK^T recomputed, dO V^T, P^T dO,
+    dS^T Q, dS K)."""
+    from swa_inputs import derive_seed, normal, prefill_inputs
+    q, k, v, sinks = prefill_inputs(cfg, device=dev)
+    dout = normal(q.shape, derive_seed(cfg.seed, "dout"), dev, torch.bfloat16)
+    pairs = swa_pairs(cfg.S, cfg.window, cfg.q_offset) * cfg.B * cfg.Hq
+    o, lse = swa.swa_attn_prefill_lse(q, k, v, sinks, cfg.window, cfg.q_offset, cfg.scale)
+    ws = torch.empty(swa.swa_attn_backward_workspace_bytes(cfg.B, cfg.S, cfg.Hq), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        swa.swa_attn_prefill_lse(q, k, v, sinks, cfg.window, cfg.q_offset, cfg.scale)
+
+    def bwd():
+        swa.swa_attn_backward(q, k, v, sinks, o, lse, dout, cfg.window, cfg.q_offset, cfg.scale, workspace=ws)
+
+    res = {}
+    for name, fn in (("forward_lse", fwd), ("backward", bwd)):
+        settle(fn, args.settle_seconds)
+        for _ in range(args.warmup):
+            fn()
+        res[name] = time_launches(fn, max(args.steps, 5), stream)
+    ms_f, ms_b = res["forward_lse"], res["backward"]
+    # HBM bytes the backward must move at least: q, o, dO read, dq written
+    # (B*S*Hq*D each), k, v read and dk, dv written (B*Sk*Hkv*D each), the
+    # lse read, all bf16 except lse (fp32)
+    bytes_b = (4 * cfg.B * cfg.S * cfg.Hq * cfg.D + 4 * cfg.B * cfg.keys * cfg.Hkv * cfg.D) * 2 + cfg.B * cfg.S * cfg.Hq * 4
+    del q, k, v, o, lse, dout, ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": "swa_32k training step: B1 S32768 Hq64 Hkv8 D128 W128 bf16 with sinks",
+        "ms_forward_lse": round(ms_f, 5), "ms_backward": round(ms_b, 5),
+        "forward_TFLOP/s": round(4.0 * cfg.D * pairs / (ms_f * 1e-3) / 1e12, 1),
+        "backward_TFLOP/s": round(10.0 * cfg.D * pairs / (ms_b * 1e-3) / 1e12, 1),
+        "backward_min_bytes": bytes_b,
+        "backward_GB/s_of_min_bytes": round(bytes_b / (ms_b * 1e-3) / 1e9, 1),
+        "step_ms": round(ms_f + ms_b, 5),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -506,6 +549,10 @@ def main():
     if args.only == "mtp":
         print(json.dumps({"mtp_step": run_mtp(args, swa, torch, dev, stream)}), flush=True)
         return
+    if args.only == "backward":
+        print(json.dumps({"backward": run_backward(args, swa, torch, dev, stream, PREFILL_CONFIGS["swa_32k"])}),
+              flush=True)
+        return
     if args.only == "rope":
         print(json.dumps({"rope": run_rope(args, swa, torch, dev, stream, PREFILL_CONFIGS["swa_32k"], 0.28)}),
               flush=True)
@@ -536,6 +583,7 @@ def main():
         result["decode"] = run_verify(args, swa, torch, dev, stream, ("decode_ga_b64", "decode_swa_b64"))
         result["mtp_step"] = run_mtp(args, swa, torch, dev, stream)
         result["rope"] = run_rope(args, swa, torch, dev, stream, cfg, pres["roofline"]["kernel_ms"])
+        result["backward"] = run_backward(args, swa, torch, dev, stream, cfg)
     peaks = read_peaks()
     if peaks is not None:
         # fractions of the ceilings measured on this GPU: the SWA prefill moves

@@ -12,6 +12,8 @@ declared in ``include/swa_attn.h``).  The functions carry the C names:
     swa_cache_advance(cache_len, n_append)
     swa_rope_apply(x, rot_dim, base, pos0=None, pos_offset=0)
     swa_attn_prefill_rope(q, k, v, sinks, window, rot_dim, rope_base, q_offset=0, ...)
+    swa_attn_prefill_lse(q, k, v, sinks, window, q_offset=0, ...) -> (o, lse)
+    swa_attn_backward(q, k, v, sinks, o, lse, dout, window, ...) -> (dq, dk, dv, dsink)
 
 They only check and marshal arguments (device, dtype, contiguity, shapes)
 and pass raw device pointers plus torch's current HIP stream; every step of
@@ -30,7 +32,8 @@ __all__ = [
     "SwaError", "library_path", "load_library", "swa_attn_prefill",
     "swa_attn_verify_workspace_bytes", "swa_attn_verify", "kv_ring_append",
     "swa_mtp_accept_workspace_bytes", "swa_mtp_greedy_accept", "swa_cache_advance",
-    "swa_rope_apply", "rope_dims", "swa_attn_prefill_rope", "EXPORTED_SYMBOLS",
+    "swa_rope_apply", "rope_dims", "swa_attn_prefill_rope", "swa_attn_prefill_lse",
+    "swa_attn_backward_workspace_bytes", "swa_attn_backward", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +44,8 @@ SWA_F32, SWA_BF16 = 0, 1
 EXPORTED_SYMBOLS = ("swa_status_string", "swa_attn_prefill", "swa_attn_verify_workspace_bytes",
                     "swa_attn_verify", "kv_ring_append", "swa_mtp_accept_workspace_bytes",
                     "swa_mtp_greedy_accept", "swa_cache_advance", "swa_rope_apply",
-                    "swa_attn_prefill_rope")
+                    "swa_attn_prefill_rope", "swa_attn_prefill_lse", "swa_attn_backward_workspace_bytes",
+                    "swa_attn_backward")
 
 
 class SwaError(RuntimeError):
@@ -85,6 +89,12 @@ def load_library():
     lib.swa_rope_apply.restype = i
     lib.swa_attn_prefill_rope.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, f, i, p]
     lib.swa_attn_prefill_rope.restype = i
+    lib.swa_attn_prefill_lse.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, p]
+    lib.swa_attn_prefill_lse.restype = i
+    lib.swa_attn_backward_workspace_bytes.argtypes = [i, i, i]
+    lib.swa_attn_backward_workspace_bytes.restype = sz
+    lib.swa_attn_backward.argtypes = [p, p, p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, p, sz, p]
+    lib.swa_attn_backward.restype = i
     _lib = lib
     return lib
 
@@ -340,3 +350,63 @@ def swa_rope_apply(x: torch.Tensor, rot_dim: int, base: float, pos0: Optional[to
                             _dtype_code(x), _stream(stream))
     _check(st, "swa_rope_apply")
     return x
+
+
+def swa_attn_prefill_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: Optional[torch.Tensor],
+                         window: int, q_offset: int = 0, sm_scale: Optional[float] = None, stream=None):
+    """Training forward (bf16): returns (o [B,Sq,Hq,D], lse [B,Sq,Hq] fp32)."""
+    lib = load_library()
+    _dev(q, "q", torch.bfloat16, 4)
+    _dev(k, "k", torch.bfloat16, 4)
+    _dev(v, "v", torch.bfloat16, 4)
+    _dev(sinks, "sinks", torch.float32, 1)
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError("k/v shape mismatch")
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Sq, Hq), dtype=torch.float32, device=q.device)
+    st = lib.swa_attn_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv,
+                                  D, int(window), int(q_offset), float(sm_scale), SWA_BF16, _stream(stream))
+    _check(st, "swa_attn_prefill_lse")
+    return o, lse
+
+
+def swa_attn_backward_workspace_bytes(B: int, Sq: int, Hq: int) -> int:
+    return int(load_library().swa_attn_backward_workspace_bytes(B, Sq, Hq))
+
+
+def swa_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: Optional[torch.Tensor],
+                      o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, window: int,
+                      q_offset: int = 0, sm_scale: Optional[float] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of sum(dout * O) (bf16): returns (dq, dk, dv, dsink or None)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _dev(t, name, torch.bfloat16, 4)
+    _dev(sinks, "sinks", torch.float32, 1)
+    _dev(lse, "lse", torch.float32, 3)
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if lse.shape != (B, Sq, Hq):
+        raise ValueError("lse must be [B, Sq, Hq]")
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    need = int(lib.swa_attn_backward_workspace_bytes(B, Sq, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dsink = None if sinks is None else torch.empty_like(sinks)
+    st = lib.swa_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                               _ptr(dk), _ptr(dv), _ptr(dsink), B, Sq, Sk, Hq, Hkv, D, int(window), int(q_offset),
+                               float(sm_scale), SWA_BF16, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "swa_attn_backward")
+    return dq, dk, dv, dsink

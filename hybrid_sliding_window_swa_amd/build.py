@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libswa_attn.so")
 PEAKS = os.path.join(PKG, "swa_peaks")
 ARCH = os.environ.get("SWA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "validate.c", "prefill_bf16.hip", "verify_bf16.hip", "fp32_kernels.hip", "append.hip", "accept.hip", "rope.hip"]
+SOURCES = ["api.hip", "validate.c", "prefill_bf16.hip", "verify_bf16.hip", "fp32_kernels.hip", "append.hip", "accept.hip", "rope.hip", "backward_bf16.hip"]
 
 
 def hipcc() -> str:

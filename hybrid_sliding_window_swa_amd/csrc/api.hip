@@ -85,6 +85,66 @@ swa_status_t swa_attn_prefill_rope(const void* q, const void* k, const void* v, 
   return from_hip(dtype == SWA_BF16 ? launch_prefill_bf16(a, s) : launch_prefill_f32(a, s));
 }
 
+swa_status_t swa_attn_prefill_lse(const void* q, const void* k, const void* v, const float* sinks,
+                                  void* o, float* lse, int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                                  int window, int q_offset, float sm_scale, swa_dtype_t dtype, void* stream) {
+  swa_status_t st = swa_validate_prefill(q, k, v, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset,
+                                         sm_scale, dtype);
+  if (st != SWA_OK) return st;
+  if (dtype != SWA_BF16) return SWA_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0) return SWA_OK;
+  if (!lse) return SWA_ERR_NULL;
+  PrefillArgs a = prefill_args(q, k, v, sinks, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset, sm_scale);
+  a.lse = lse;
+  return from_hip(launch_prefill_bf16(a, (hipStream_t)stream));
+}
+
+size_t swa_attn_backward_workspace_bytes(int B, int Sq, int Hq) {
+  if (B < 0 || Sq < 0 || Hq <= 0) return 0;
+  return plan_backward(B, Sq, Hq).ws_bytes;
+}
+
+swa_status_t swa_attn_backward(const void* q, const void* k, const void* v, const float* sinks,
+                               const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                               void* dv, float* dsink, int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                               int window, int q_offset, float sm_scale, swa_dtype_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  swa_status_t st = swa_validate_prefill(q, k, v, o, B, Sq, Sk, Hq, Hkv, D, window, q_offset,
+                                         sm_scale, dtype);
+  if (st != SWA_OK) return st;
+  if (dtype != SWA_BF16) return SWA_ERR_UNSUPPORTED;
+  if (B == 0) return SWA_OK;
+  if (!dk || !dv || (Sq > 0 && (!lse || !dout || !dq))) return SWA_ERR_NULL;
+  const BwdPlan plan = plan_backward(B, Sq, Hq);
+  if (!workspace || workspace_bytes < plan.ws_bytes || ((uintptr_t)workspace & 255u) != 0)
+    return SWA_ERR_WORKSPACE;
+  BwdArgs a = {};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.sinks = sinks;
+  a.o = (const uint16_t*)o;
+  a.dout = (const uint16_t*)dout;
+  a.lse = lse;
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.dsink = dsink;
+  a.delta = (float*)workspace;
+  a.sink_part = (float*)((char*)workspace + plan.delta_bytes);
+  a.B = B;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.window = window > 0 ? window : 0;
+  a.q_offset = q_offset;
+  a.scale = sm_scale;
+  a.scale_log2 = sm_scale * kLog2eHost;
+  return from_hip(launch_backward_bf16(a, plan, (hipStream_t)stream));
+}
+
 size_t swa_attn_verify_workspace_bytes(int B, int q_len, int Hq, int Hkv, int D, int cache_slots,
                                        int ring, int window, swa_dtype_t dtype) {
   if (swa_validate_verify_shape(B, q_len, Hq, Hkv, D, cache_slots, ring, window, dtype) != SWA_OK)

@@ -15,6 +15,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_inff();
 
 // Lazy-rescale threshold (log2 units): the running maximum used to shift the

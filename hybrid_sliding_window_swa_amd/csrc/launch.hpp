@@ -13,6 +13,7 @@ struct PrefillArgs {
   const uint16_t* v;
   const float* sinks;
   uint16_t* o;
+  float* lse;         // [B, Sq, Hq] natural-log softmax denominators, or null
   int B, Sq, Sk, Hq, Hkv, D;
   int window, q_offset;
   float scale;        // sm_scale
@@ -57,6 +58,35 @@ struct AppendArgs {
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+
+struct BwdArgs {
+  const uint16_t* q;      // [B, Sq, Hq, D] bf16
+  const uint16_t* k;      // [B, Sk, Hkv, D]
+  const uint16_t* v;
+  const float* sinks;     // [Hq] or null
+  const uint16_t* o;      // forward output [B, Sq, Hq, D]
+  const uint16_t* dout;   // dL/dO [B, Sq, Hq, D]
+  const float* lse;       // forward log-sum-exp [B, Sq, Hq] (natural log, sink included)
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dsink;           // [Hq] or null
+  float* delta;           // workspace: <dO, O> per row [B, Sq, Hq]
+  float* sink_part;       // workspace: [pre_blocks][Hq] partial sink gradients
+  int B, Sq, Sk, Hq, Hkv, D;
+  int window, q_offset;
+  float scale, scale_log2;
+  int pre_tokens, pre_blocks;  // set by the launcher
+};
+
+struct BwdPlan {
+  int pre_tokens;     // tokens per preprocess workgroup
+  int pre_blocks;
+  size_t delta_bytes; // bytes of the delta array (256-byte rounded)
+  size_t ws_bytes;
+};
+BwdPlan plan_backward(int B, int Sq, int Hq);
+hipError_t launch_backward_bf16(BwdArgs a, const BwdPlan& p, hipStream_t s);
 // Whether launch_prefill_bf16 runs these arguments on the sliding-window strip
 // kernel (the only prefill kernel that rotates queries as it stages them).
 bool prefill_uses_strip(const PrefillArgs& a);

@@ -302,6 +302,16 @@ struct QState {
     return sn;
   }
 
+  // Natural-log softmax denominator of each row, sink included, for the
+  // backward: lse = (m + log2 l) * ln 2 (m and l share the lazy shift, so the
+  // sum is exact whatever the shift).  lse_b points at [b][0][0] of [B, Sq, Hq].
+  __device__ __forceinline__ void store_lse(float* lse_b, int Hq, int tw0, int G, int g, int Sq, int col,
+                                            int half) const {
+    const float lt = halves_sum(l_run);
+    const int tok = tw0 + col / G;
+    if (half == 0 && tok < Sq) lse_b[(long)tok * Hq + g * G + col % G] = (m_run + log2f(lt)) * kLn2;
+  }
+
   // O = acc / l in bf16, one 8-byte store per 4 consecutive d.
   __device__ __forceinline__ void store_o(uint16_t* obase, long q_tok, int tw0, int G, int g, int Sq,
                                           int col, int half) {
@@ -458,7 +468,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   }
   if (kt_end >= wk0 && kt_end <= wk1)
     st.template fold<false>(s, c2, v_lds[(kt_end - kt_begin) & 3], nullptr, 0, 0, W, half, lane);
-  if (wk1 >= 0) st.store_o(p.o + qoff, q_tok, tw0, G, g, p.Sq, col, half);
+  if (wk1 >= 0) {
+    st.store_o(p.o + qoff, q_tok, tw0, G, g, p.Sq, col, half);
+    if (p.lse) st.store_lse(p.lse + (long)b * p.Sq * p.Hq, p.Hq, tw0, G, g, p.Sq, col, half);
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -710,6 +723,7 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
                                    tile_mask(kt + 1), W, half, lane);
       st.template fold<false>(s, p.scale_log2, v_ring[wk1 % NR], nullptr, 0, 0, W, half, lane);
       store_o_rows(tw0);
+      if (p.lse) st.store_lse(p.lse + (long)b * p.Sq * p.Hq, p.Hq, tw0, G, g, p.Sq, col, half);
     }
     // the new tile's slot held tile new_kt - NR, older than this block's window
     if (have_new) {

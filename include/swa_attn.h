@@ -126,6 +126,51 @@ SWA_API swa_status_t swa_attn_prefill_rope(const void *q, const void *k, const v
                                    swa_dtype_t dtype, void *stream);
 
 /*
+ * Training forward: swa_attn_prefill that also saves, per query row, the
+ * natural-log softmax denominator with the sink,
+ *   lse[b, r, h] = log(exp(sink_h) + sum_{j in J(i)} exp(s_j)),
+ * which swa_attn_backward needs.  lse [B, Sq, Hq] fp32 DEVICE.  SWA_BF16 only;
+ * other arguments and rules as swa_attn_prefill.
+ */
+SWA_API swa_status_t swa_attn_prefill_lse(const void *q, const void *k, const void *v,
+                                  const float *sinks, void *o, float *lse,
+                                  int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                                  int window, int q_offset, float sm_scale,
+                                  swa_dtype_t dtype, void *stream);
+
+/* Bytes of device workspace swa_attn_backward needs (per-row <dO, O> and the
+ * per-workgroup partial sink gradients).  0 for invalid sizes. */
+SWA_API size_t swa_attn_backward_workspace_bytes(int B, int Sq, int Hq);
+
+/*
+ * Backward of the prefill: the gradients of L = sum(dout * O) for
+ * O = swa_attn_prefill(q, k, v, sinks) (the definition at the top of this
+ * file differentiated; the pages give no training kernel, and MTP-accelerated
+ * RL training, report digest "Model Architecture", needs one):
+ *   P = exp(s - lse), D_i = <dout_i, O_i>, dS = P (dout V^T - D),
+ *   dq = sm_scale dS K, dk = sm_scale dS^T q, dv = P^T dout,
+ *   dsink_h = -sum_i exp(sink_h - lse_i) D_i   (the sink is not scaled and
+ *   carries no value).
+ *   q, o, dout, dq   [B, Sq, Hq, D] bf16 DEVICE;  k, v, dk, dv [B, Sk, Hkv, D];
+ *   o, lse           from swa_attn_prefill_lse on the same inputs;
+ *   sinks [Hq] fp32 or NULL;  dsink [Hq] fp32 DEVICE output, or NULL to skip
+ *   (zeros when sinks is NULL);
+ *   workspace        device buffer, 256-byte aligned, of at least
+ *                    swa_attn_backward_workspace_bytes(B, Sq, Hq) bytes.
+ * Every element of dq, dk and dv is written (keys no query sees get zeros).
+ * Accumulation is fp32; P and dS are rounded to bf16 for the matrix cores;
+ * dq, dk, dv are rounded to bf16 (nearest even); dsink is summed in a fixed
+ * order (deterministic).  SWA_BF16 only; shape rules as swa_attn_prefill.
+ * Calls sharing a workspace must not overlap.
+ */
+SWA_API swa_status_t swa_attn_backward(const void *q, const void *k, const void *v,
+                               const float *sinks, const void *o, const float *lse,
+                               const void *dout, void *dq, void *dk, void *dv, float *dsink,
+                               int B, int Sq, int Sk, int Hq, int Hkv, int D,
+                               int window, int q_offset, float sm_scale, swa_dtype_t dtype,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace swa_attn_verify needs for these sizes (split-KV
  * partial results: running max, running sum and unnormalised output per
  * query row and split).  0 when the arguments are invalid.

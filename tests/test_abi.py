@@ -211,3 +211,24 @@ def test_prefill_rope_validation(lib):
     assert f(W=0) == UNSUP             # global attention: not the strip kernel
     assert f(Hq=32, Hkv=2) == UNSUP    # G = 16
     assert f(dt=F32) == UNSUP
+
+
+def test_backward_validation(lib):
+    P = lambda v: ctypes.c_void_p(v) if v else None
+    need = lib.swa_attn_backward_workspace_bytes(1, 64, 16)
+    assert need > 0 and lib.swa_attn_backward_workspace_bytes(1, 64, 0) == 0
+
+    def f(ptr=256, ws=256, ws_bytes=need, dt=BF16, Hq=16, Hkv=2, D=128, lse=256):
+        return lib.swa_attn_backward(P(ptr), P(ptr), P(ptr), None, P(ptr), P(lse), P(ptr), P(ptr), P(ptr), P(ptr),
+                                     None, 1, 64, 64, Hq, Hkv, D, 128, 0, 0.1, dt, P(ws), ws_bytes, None)
+    assert f(dt=F32) == UNSUP
+    assert f(lse=0) == NULL
+    assert f(ws=0) == WS
+    assert f(ws_bytes=need - 1) == WS
+    assert f(ws=512 + 16) == WS                # not 256-byte aligned
+    assert f(D=96) == UNSUP
+    assert f(Hq=64, Hkv=1) == UNSUP            # 32 % G != 0
+    assert lib.swa_attn_prefill_lse(P(256), P(256), P(256), None, P(256), None, 1, 8, 8, 16, 2, 128, 128, 0, 0.1,
+                                    BF16, None) == NULL
+    assert lib.swa_attn_prefill_lse(P(256), P(256), P(256), None, P(256), P(256), 1, 8, 8, 16, 2, 128, 128, 0, 0.1,
+                                    F32, None) == UNSUP
