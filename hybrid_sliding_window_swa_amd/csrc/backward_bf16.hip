@@ -13,8 +13,8 @@
 // (the sink adds exp(sink) to the denominator and carries no value).
 //
 // Kernels
-//   * bwd_preprocess: D_i for every row (16-byte loads of O and dO, one
-//     16-lane group per row), and per workgroup and head the partial sum of
+//   * bwd_dq (first): besides dQ, D_i = <dO_i, O_i> for its rows (written for
+//     bwd_dkdv) and, per workgroup and head, the partial sum of
 //     exp(sink - LSE) D in a fixed order; bwd_sink_reduce adds the partials
 //     in a fixed order, so dsink is deterministic.
 //   * bwd_dkdv: KV-parallel.  A wave owns 32 keys of one KV head and keeps
@@ -26,7 +26,7 @@
 //     dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed
 //     from the row-major LDS tiles by ds_read_b64_tr_b16 (the forward's V^T
 //     trick, with the query as the contraction index).
-//   * bwd_dq: Q-parallel, the forward's structure.  A wave owns 32 query rows
+//   * bwd_dq: Q-parallel, the forward's structure, launched first.  A wave owns 32 query rows
 //     with q and dO in registers; S^T = K Q^T and dP^T = V dO^T give a lane
 //     one query's column, dS^T is the B operand of dQ^T += K^T dS^T with K^T
 //     read transposed from the K tile.
@@ -60,54 +60,27 @@ __device__ __forceinline__ bool visible(int i, int j, int window) {
   return j <= i && (window <= 0 || j > i - window);
 }
 
-// ---------------------------------------------------------------- preprocess
-template <int D>
-__global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8;          // lanes per row
-  constexpr int RPI = 256 / LPR;      // rows per block-wide step
-  extern __shared__ float term[];     // [tokens of this block][Hq]
-  const int tid = threadIdx.x;
-  const long tok0 = (long)blockIdx.x * a.pre_tokens;
-  const long ntok_all = (long)a.B * a.Sq;
-  const int ntok = (int)(ntok_all - tok0 < a.pre_tokens ? ntok_all - tok0 : a.pre_tokens);
-  const int nrows = ntok * a.Hq;
-  const long row0 = tok0 * a.Hq;
-  const int sub = tid % LPR;
-  for (int r = tid / LPR; r < nrows; r += RPI) {
-    const long row = row0 + r;
-    const u32x4 o = *(const u32x4*)(a.o + row * D + sub * 8);
-    const u32x4 g = *(const u32x4*)(a.dout + row * D + sub * 8);
-    float acc = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(__uint_as_float(o[e] << 16), __uint_as_float(g[e] << 16), acc);
-      acc = fmaf(__uint_as_float(o[e] & 0xffff0000u), __uint_as_float(g[e] & 0xffff0000u), acc);
-    }
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-    if (sub == 0) {
-      a.delta[row] = acc;
-      if (a.sinks) {
-        const int h = (int)(row % a.Hq);
-        term[r] = __expf(a.sinks[h] - a.lse[row]) * acc;
-      }
-    }
-  }
-  if (!a.sinks) return;
-  __syncthreads();
-  for (int h = tid; h < a.Hq; h += 256) {
-    float s = 0.0f;
-    for (int t = 0; t < ntok; ++t) s += term[t * a.Hq + h];
-    a.sink_part[(long)blockIdx.x * a.Hq + h] = -s;
-  }
+__global__ __launch_bounds__(256) void bwd_zero_kernel(float* x, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) x[i] = 0.0f;
 }
 
+// ---------------------------------------------------------------- dsink
+// dsink_h = sum of the per-workgroup partials the dQ kernel leaves (one per
+// (request, token block) and head): one workgroup per head, each lane adding
+// a fixed stride of partials, then a fixed-order tree in LDS (deterministic).
 __global__ __launch_bounds__(256) void bwd_sink_reduce_kernel(BwdArgs a) {
-  for (int h = threadIdx.x; h < a.Hq; h += 256) {
-    float s = 0.0f;
-    for (int blk = 0; blk < a.pre_blocks; ++blk) s += a.sink_part[(long)blk * a.Hq + h];
-    a.dsink[h] = s;
+  __shared__ float part[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  float s = 0.0f;
+  for (int i = tid; i < a.n_sink_parts; i += 256) s += a.sink_part[(long)i * a.Hq + h];
+  part[tid] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) part[tid] += part[tid + w];
+    __syncthreads();
   }
+  if (tid == 0) a.dsink[h] = part[0];
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -314,21 +287,32 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   const int tok = tw0 + col / G, h = g * G + col % G;
   const int qpos = a.q_offset + tok;
 
-  // q and dO of this lane's query row as B operands (d = 16c + 8 half + 0..7)
+  // q and dO of this lane's query row as B operands (d = 16c + 8 half + 0..7);
+  // D = <dO, O> from the lane's half of the row and its partner's
+  __shared__ float sink_term[NW][32];
   bf16x8 qop[Gm::NC], oop[Gm::NC];
   float lse2 = __builtin_inff(), del = 0.0f;
   {
     const long qoff = ((long)b * a.Sq + tok) * q_tok + (long)h * D + half * 8;
+    float part = 0.0f;
 #pragma unroll
     for (int c = 0; c < Gm::NC; ++c) {
       qop[c] = tok < a.Sq ? *(const bf16x8*)(a.q + qoff + c * 16) : bf16x8{};
       oop[c] = tok < a.Sq ? *(const bf16x8*)(a.dout + qoff + c * 16) : bf16x8{};
+      const bf16x8 ov = tok < a.Sq ? *(const bf16x8*)(a.o + qoff + c * 16) : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)oop[c][e], (float)ov[e], part);
     }
+    del = halves_sum(part);
+    float term = 0.0f;
     if (tok < a.Sq) {
       const long row = ((long)b * a.Sq + tok) * a.Hq + h;
-      lse2 = a.lse[row] * kLog2e;
-      del = a.delta[row];
+      const float lse = a.lse[row];
+      lse2 = lse * kLog2e;
+      if (half == 0) a.delta[row] = del;
+      if (a.sinks) term = __expf(a.sinks[h] - lse) * del;
     }
+    if (half == 0) sink_term[wv][col] = term;
   }
   f32x16 dq[Gm::ND];
 #pragma unroll
@@ -372,6 +356,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   load_tile(kt_begin);
   store_tile(0);
   __syncthreads();
+  // this workgroup's share of dsink for the G heads of group g, fixed order
+  if (a.sinks && tid < G) {
+    float sum = 0.0f;
+    for (int wq = 0; wq < NW; ++wq)
+      for (int c = tid; c < 32; c += G) sum += sink_term[wq][c];
+    a.sink_part[((long)b * n_tb + tb) * a.Hq + g * G + tid] = -sum;
+  }
   const float c2 = a.scale_log2;
   for (int kt = kt_begin; kt <= kt_end; ++kt) {
     const int buf = (kt - kt_begin) & 1;
@@ -422,18 +413,31 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int D, int G>
-hipError_t launch_bwd_dg(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_dg(BwdArgs a, hipStream_t s) {
+  // dQ first: it also leaves D = <dO, O> for dK/dV and the dsink partials
+  const int TB = (BKT / G) * 8;
+  const int n_tb = (a.Sq + TB - 1) / TB;
+  a.n_sink_parts = a.B * n_tb;
+  if (n_tb > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(n_tb * a.B * a.Hkv), dim3(512), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.dsink) {
+    if (a.sinks && n_tb > 0) {
+      hipLaunchKernelGGL(bwd_sink_reduce_kernel, dim3(a.Hq), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(bwd_zero_kernel, dim3((a.Hq + 255) / 256), dim3(256), 0, s, a.dsink, a.Hq);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int n_kb = (a.Sk + 4 * BKT - 1) / (4 * BKT);
   if (n_kb > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(n_kb * a.B * a.Hkv), dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
   }
-  const int TB = (BKT / G) * 8;
-  const int n_tb = (a.Sq + TB - 1) / TB;
-  if (n_tb == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(n_tb * a.B * a.Hkv), dim3(512), 0, s, a);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 template <int D>
@@ -453,32 +457,17 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
 
 BwdPlan plan_backward(int B, int Sq, int Hq) {
   BwdPlan p = {};
-  p.pre_tokens = Hq >= 4096 ? 1 : 4096 / Hq;
-  p.pre_blocks = (int)(((long)B * Sq + p.pre_tokens - 1) / p.pre_tokens);
+  // partials: one per (request, dQ token block) and head; blocks hold at
+  // least 8 tokens (G <= 32)
+  const long parts = (long)B * ((Sq + 7) / 8);
   const size_t delta_bytes = ((size_t)B * Sq * Hq * 4 + 255) / 256 * 256;
   p.delta_bytes = delta_bytes;
-  p.ws_bytes = delta_bytes + (size_t)p.pre_blocks * Hq * 4;
+  p.ws_bytes = delta_bytes + (size_t)parts * Hq * 4;
   return p;
 }
 
 hipError_t launch_backward_bf16(BwdArgs a, const BwdPlan& p, hipStream_t s) {
-  a.pre_tokens = p.pre_tokens;
-  a.pre_blocks = p.pre_blocks;
-  hipError_t e = hipSuccess;
-  if (p.pre_blocks > 0) {
-    const size_t lds = (size_t)p.pre_tokens * a.Hq * sizeof(float);
-    if (a.D == 128)
-      hipLaunchKernelGGL(bwd_preprocess_kernel<128>, dim3(p.pre_blocks), dim3(256), lds, s, a);
-    else
-      hipLaunchKernelGGL(bwd_preprocess_kernel<64>, dim3(p.pre_blocks), dim3(256), lds, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.sinks && a.dsink) {
-    hipLaunchKernelGGL(bwd_sink_reduce_kernel, dim3(1), dim3(256), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  (void)p;
   return a.D == 128 ? launch_bwd_d<128>(a, s) : launch_bwd_d<64>(a, s);
 }
 

@@ -72,16 +72,14 @@ struct BwdArgs {
   uint16_t* dv;
   float* dsink;           // [Hq] or null
   float* delta;           // workspace: <dO, O> per row [B, Sq, Hq]
-  float* sink_part;       // workspace: [pre_blocks][Hq] partial sink gradients
+  float* sink_part;       // workspace: [n_sink_parts][Hq] partial sink gradients
   int B, Sq, Sk, Hq, Hkv, D;
   int window, q_offset;
   float scale, scale_log2;
-  int pre_tokens, pre_blocks;  // set by the launcher
+  int n_sink_parts;       // set by the launcher
 };
 
 struct BwdPlan {
-  int pre_tokens;     // tokens per preprocess workgroup
-  int pre_blocks;
   size_t delta_bytes; // bytes of the delta array (256-byte rounded)
   size_t ws_bytes;
 };
