@@ -40,6 +40,8 @@ namespace swa {
 namespace {
 
 constexpr int BKT = 32;  // keys per tile / rows per query block
+constexpr int kDqWaves = 8;      // waves (32-row query blocks) per dQ workgroup
+constexpr int kDkdvPrefetch = 1;  // query blocks loaded ahead in the dK/dV kernel (deeper measured slower)
 
 template <int D>
 struct BwdGeom {
@@ -95,7 +97,7 @@ __device__ __forceinline__ void load_rows_operand(bf16x8 (&x)[D / 16], const uin
   for (int c = 0; c < D / 16; ++c) x[c] = __builtin_bit_cast(bf16x8, buf_load16(r, voff + c * 32, 0));
 }
 
-template <int D, int G>
+template <int D, int G, int PF>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   using Gm = BwdGeom<D>;
   using Tile = typename Gm::Tile;
@@ -106,13 +108,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ float lse_lds[2][BKT];
   __shared__ float del_lds[2][BKT];
 
-  // work item: (b, g, block of NW key tiles), heaviest (earliest keys) first
+  // work item: (b, g, block of NW key tiles).  Workgroups are dealt to the 8
+  // XCDs in turn; each XCD takes a contiguous range of work items, i.e.
+  // consecutive key blocks of one (b, g), whose query blocks overlap, so the
+  // re-read Q / dO rows come from that XCD's L2.
   const int n_kb = (a.Sk + NW * BKT - 1) / (NW * BKT);
-  const int w = blockIdx.x;
-  const int bg = w % (a.B * a.Hkv);
-  const int kblk = w / (a.B * a.Hkv);
+  const int total = n_kb * a.B * a.Hkv;
+  const int per_xcd = (total + 7) / 8;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (w >= total) return;
+  const int bg = w / n_kb;
+  const int kblk = w - bg * n_kb;
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  if (kblk >= n_kb) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_index();
   const int half = lane >> 5, col = lane & 31;
@@ -146,14 +153,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int qb_hi = r_hi >= r_lo ? r_hi / TQ : qb_lo - 1;
 
   // staging: the block's 32 Q rows and dO rows (G*D contiguous per token),
-  // one 16-byte chunk per thread and step, plus LSE*log2e and D per row
+  // one 16-byte chunk per thread and step, plus LSE*log2e and D per row.
+  // Loads run PF blocks ahead of their use (PF register slots, block m in
+  // slot m % PF) so that enough bytes are in flight to cover the memory
+  // latency with one workgroup per CU; LDS holds two blocks (the one being
+  // computed and the next, stored after the compute and before the barrier).
   constexpr int CPR = D / 8;                   // chunks per row
   constexpr int IT = Gm::CH / 256;
-  u32x4 qpre[IT], opre[IT];
-  float lpre = 0.0f, dpre = 0.0f;
+  u32x4 qpre[PF][IT], opre[PF][IT];
+  float lpre[PF], dpre[PF];
   const long qbase_b = (long)b * a.Sq * q_tok;
   const long rbase_b = (long)b * a.Sq * a.Hq;
-  auto load_block = [&](int qb) {
+  auto load_block = [&](int qb, int slot) {
     const int t0 = qb * TQ;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
@@ -162,84 +173,99 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const int tok = t0 + m / G;
       if (tok < a.Sq) {
         const long off = qbase_b + qrow_off(t0, m, G, g, q_tok, D) + ch * 8;
-        qpre[i] = *(const u32x4*)(a.q + off);
-        opre[i] = *(const u32x4*)(a.dout + off);
+        qpre[slot][i] = *(const u32x4*)(a.q + off);
+        opre[slot][i] = *(const u32x4*)(a.dout + off);
       } else {
-        qpre[i] = u32x4{0, 0, 0, 0};
-        opre[i] = u32x4{0, 0, 0, 0};
+        qpre[slot][i] = u32x4{0, 0, 0, 0};
+        opre[slot][i] = u32x4{0, 0, 0, 0};
       }
     }
     if (tid < BKT) {
       const int tok = t0 + tid / G;
       const long row = rbase_b + (long)tok * a.Hq + g * G + tid % G;
-      lpre = tok < a.Sq ? a.lse[row] * kLog2e : __builtin_inff();
-      dpre = tok < a.Sq ? a.delta[row] : 0.0f;
+      lpre[slot] = tok < a.Sq ? a.lse[row] * kLog2e : __builtin_inff();
+      dpre[slot] = tok < a.Sq ? a.delta[row] : 0.0f;
     }
   };
-  auto store_block = [&](int buf) {
+  auto store_block = [&](int buf, int slot) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int c = tid + i * 256;
       const int m = c / CPR, ch = c % CPR;
-      *(u32x4*)&q_lds[buf][Tile::off(m, ch * 8)] = qpre[i];
-      *(u32x4*)&o_lds[buf][Tile::off(m, ch * 8)] = opre[i];
+      *(u32x4*)&q_lds[buf][Tile::off(m, ch * 8)] = qpre[slot][i];
+      *(u32x4*)&o_lds[buf][Tile::off(m, ch * 8)] = opre[slot][i];
     }
     if (tid < BKT) {
-      lse_lds[buf][tid] = lpre;
-      del_lds[buf][tid] = dpre;
+      lse_lds[buf][tid] = lpre[slot];
+      del_lds[buf][tid] = dpre[slot];
     }
   };
 
-  if (qb_lo <= qb_hi) {
-    load_block(qb_lo);
-    store_block(0);
-  }
-  __syncthreads();
   const float c2 = a.scale_log2;
   const uint32_t ko = Tile::k_lane_off(lane), vo = Tile::vt_lane_off(lane);
-  for (int qb = qb_lo; qb <= qb_hi; ++qb) {
-    const int buf = (qb - qb_lo) & 1;
-    if (qb < qb_hi) load_block(qb + 1);
+  auto compute_block = [&](int qb, int buf) {
     // does this wave's key tile meet the block's queries?
     const int t0 = qb * TQ;
     const int i_lo = a.q_offset + t0, i_hi = a.q_offset + min(t0 + TQ, a.Sq) - 1;
     const bool need = kb < a.Sk && kb <= i_hi && (W <= 0 || kb + BKT - 1 > i_lo - W);
-    if (need) {
-      const lds_u16* qa = lane_base(lds_addr(q_lds[buf]), ko);
-      const lds_u16* oa = lane_base(lds_addr(o_lds[buf]), ko);
-      // S = Q K^T and dP = dO V^T: lane (col = key), rows = queries c_row(v, half)
-      f32x16 s = {}, dp = {};
+    if (!need) return;
+    const lds_u16* qa = lane_base(lds_addr(q_lds[buf]), ko);
+    const lds_u16* oa = lane_base(lds_addr(o_lds[buf]), ko);
+    // S = Q K^T and dP = dO V^T: lane (col = key), rows = queries c_row(v, half)
+    f32x16 s = {}, dp = {};
 #pragma unroll
-      for (int c = 0; c < Gm::NC; ++c) s = mfma32(Tile::k_operand(qa, c), kop[c], s);
-#pragma unroll
-      for (int c = 0; c < Gm::NC; ++c) dp = mfma32(Tile::k_operand(oa, c), vop[c], dp);
-      // P, dS (masked entries exactly zero), rounded to bf16 B operands
-      const bool edge = !(kb + BKT - 1 <= i_lo && (W <= 0 || kb > i_hi - W)) || i_hi < a.q_offset + t0 + TQ - 1;
-      bf16x8 pb[2], sb[2];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = c_row(v, half);
-        float p = exp2_fast(fmaf(s[v], c2, -lse_lds[buf][m]));
-        if (edge) {
-          const int i = a.q_offset + t0 + m / G;
-          if (!visible(i, key, W) || key >= a.Sk) p = 0.0f;
-        }
-        const float ds = p * (dp[v] - del_lds[buf][m]);
-        pb[v >> 3][v & 7] = (__bf16)p;
-        sb[v >> 3][v & 7] = (__bf16)ds;
-      }
-      const lds_u16* qt = lane_base(lds_addr(q_lds[buf]), vo);
-      const lds_u16* ot = lane_base(lds_addr(o_lds[buf]), vo);
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int db = 0; db < Gm::ND; ++db) {
-          dv[db] = mfma32(Tile::vt_operand(ot, db, kc), pb[kc], dv[db]);
-          dk[db] = mfma32(Tile::vt_operand(qt, db, kc), sb[kc], dk[db]);
-        }
+    for (int c = 0; c < Gm::NC; ++c) {
+      s = mfma32(Tile::k_operand(qa, c), kop[c], s);
+      dp = mfma32(Tile::k_operand(oa, c), vop[c], dp);
     }
-    if (qb < qb_hi) store_block(buf ^ 1);
-    __syncthreads();
+    // P, dS (masked entries exactly zero), rounded to bf16 B operands
+    const bool edge = !(kb + BKT - 1 <= i_lo && (W <= 0 || kb > i_hi - W)) || i_hi < a.q_offset + t0 + TQ - 1;
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = c_row(v, half);
+      float p = exp2_fast(fmaf(s[v], c2, -lse_lds[buf][m]));
+      if (edge) {
+        const int i = a.q_offset + t0 + m / G;
+        if (!visible(i, key, W) || key >= a.Sk) p = 0.0f;
+      }
+      const float ds = p * (dp[v] - del_lds[buf][m]);
+      pb[v >> 3][v & 7] = (__bf16)p;
+      sb[v >> 3][v & 7] = (__bf16)ds;
+    }
+    const lds_u16* qt = lane_base(lds_addr(q_lds[buf]), vo);
+    const lds_u16* ot = lane_base(lds_addr(o_lds[buf]), vo);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db) {
+        dv[db] = mfma32(Tile::vt_operand(ot, db, kc), pb[kc], dv[db]);
+        dk[db] = mfma32(Tile::vt_operand(qt, db, kc), sb[kc], dk[db]);
+      }
+  };
+
+  const int nblk = qb_hi - qb_lo + 1;
+  if (nblk > 0) {
+    load_block(qb_lo, 0);
+    store_block(0, 0);
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      if (1 + u < nblk) load_block(qb_lo + 1 + u, (1 + u) % PF);
+  }
+  __syncthreads();
+  for (int n0 = 0; n0 < nblk; n0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int n = n0 + u;
+      if (n < nblk) {
+        compute_block(qb_lo + n, n & 1);
+        // block n + 1 (slot (u + 1) % PF) into the other LDS buffer, then
+        // the load of block n + 1 + PF into the slot it frees
+        if (n + 1 < nblk) store_block((n + 1) & 1, (u + 1) % PF);
+        if (n + 1 + PF < nblk) load_block(qb_lo + n + 1 + PF, (u + 1) % PF);
+        __syncthreads();
+      }
+    }
   }
 
   // dK = scale * dK^T, dV = dV^T, transposed back: lane col is key kb + col,
@@ -261,23 +287,28 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dQ
-template <int D, int G>
-__global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
+template <int D, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
   using Gm = BwdGeom<D>;
   using KT_ = typename Gm::Tile;     // K tile: row-major reads and transposed reads
   using VT_ = KTile<D>;              // V tile: row-major reads only
-  constexpr int NW = 8;
+  constexpr int NT = NW * 64;
   constexpr int TQ = BKT / G;        // tokens per wave
   constexpr int TB = TQ * NW;        // tokens per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT_::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][VT_::ELEMS];
 
+  // XCD-aware work item, as in the dK/dV kernel: consecutive token blocks of
+  // one (b, g) on one XCD share their K / V tiles through its L2; latest
+  // (longest, for global attention) blocks first
   const int n_tb = (a.Sq + TB - 1) / TB;
-  const int w = blockIdx.x;
-  const int bg = w % (a.B * a.Hkv);
-  const int tb = n_tb - 1 - w / (a.B * a.Hkv);   // latest (longest) blocks first
+  const int total = n_tb * a.B * a.Hkv;
+  const int per_xcd = (total + 7) / 8;
+  const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (w >= total) return;
+  const int bg = w / n_tb;
+  const int tb = n_tb - 1 - (w - bg * n_tb);
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  if (tb < 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_index();
   const int half = lane >> 5, col = lane & 31;
@@ -325,7 +356,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   const bool wave_live = tw0 < a.Sq;
 
   constexpr int CPR = D / 8;
-  constexpr int IT = (Gm::CH + 511) / 512;
+  constexpr int IT = (Gm::CH + NT - 1) / NT;
   u32x4 kpre[IT], vpre[IT];
   const long kvb = (long)b * a.Sk * kv_tok + (long)g * D;
   auto load_tile = [&](int kt) {
@@ -334,7 +365,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     const rsrc_t rv = make_rsrc(a.v + kvb + (long)kb * kv_tok, (uint32_t)(((min(BKT, a.Sk - kb) - 1) * kv_tok + D) * 2));
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const int c = tid + i * 512;
+      const int c = tid + i * NT;
       if (c < Gm::CH) {
         const uint32_t off = (uint32_t)(((c / CPR) * kv_tok + (c % CPR) * 8) * 2);
         kpre[i] = buf_load16(rk, off, 0);
@@ -345,7 +376,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const int c = tid + i * 512;
+      const int c = tid + i * NT;
       if (c < Gm::CH) {
         *(u32x4*)&k_lds[buf][KT_::off(c / CPR, (c % CPR) * 8)] = kpre[i];
         *(u32x4*)&v_lds[buf][VT_::off(c / CPR, (c % CPR) * 8)] = vpre[i];
@@ -415,11 +446,12 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
 template <int D, int G>
 hipError_t launch_bwd_dg(BwdArgs a, hipStream_t s) {
   // dQ first: it also leaves D = <dO, O> for dK/dV and the dsink partials
-  const int TB = (BKT / G) * 8;
+  const int TB = (BKT / G) * kDqWaves;
   const int n_tb = (a.Sq + TB - 1) / TB;
   a.n_sink_parts = a.B * n_tb;
   if (n_tb > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(n_tb * a.B * a.Hkv), dim3(512), 0, s, a);
+    const int total = n_tb * a.B * a.Hkv;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, G, kDqWaves>), dim3(8 * ((total + 7) / 8)), dim3(kDqWaves * 64), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -434,7 +466,8 @@ hipError_t launch_bwd_dg(BwdArgs a, hipStream_t s) {
   }
   const int n_kb = (a.Sk + 4 * BKT - 1) / (4 * BKT);
   if (n_kb > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(n_kb * a.B * a.Hkv), dim3(256), 0, s, a);
+    const int total = n_kb * a.B * a.Hkv;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, G, kDkdvPrefetch>), dim3(8 * ((total + 7) / 8)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;
