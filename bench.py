@@ -10,7 +10,12 @@ with inputs resident in HBM.  The same run also times the q_len=4 MTP verify
 on 64 requests (global-layer cache with contexts U[4096, 65536] and a
 128-slot SWA ring) and reports its HBM GB/s from algorithmic bytes (every
 K/V row the windows need read once, plus Q, the new rows and O), and the
-same for a plain q_len=1 decode step on the same shapes.
+same for a plain q_len=1 decode step on the same shapes.  Further sections
+(context for the same run, not the headline): the 48-layer self-speculative
+MTP step (verify of 39 SWA and 9 global layers, greedy acceptance over a
+152064-token vocabulary, append, advance) against the q_len=1 decode step;
+the partial rotary embedding, standalone and fused into the SWA prefill;
+and the SWA 32K training forward (saved log-sum-exp) and backward.
 
 Prints ONE JSON line.  Inputs are seeded synthetic N(0,1) tensors rounded to
 bf16 (random numbers, no dataset).  --gpus above 1 is refused: this build
