@@ -309,7 +309,7 @@ struct QState {
                                             int half) const {
     const float lt = halves_sum(l_run);
     const int tok = tw0 + col / G;
-    if (half == 0 && tok < Sq) lse_b[(long)tok * Hq + g * G + col % G] = (m_run + log2f(lt)) * kLn2;
+    if (half == 0 && tok < Sq) lse_b[(long)tok * Hq + g * G + col % G] = (m_run + __builtin_amdgcn_logf(lt)) * kLn2;
   }
 
   // O = acc / l in bf16, one 8-byte store per 4 consecutive d.
@@ -483,11 +483,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
 // converts between that layout and the MFMA register layout.
 constexpr int kRingTiles = 6;
 
+constexpr int kStripPlain = 0, kStripRope = 1, kStripLse = 2;
 constexpr double kRopeTwoPi = 6.283185307179586476925286766559;
 constexpr double kRopeInvTwoPi = 0.15915494309189533576888376337251;
 
-template <int D, int G, bool ROPE>
+// MODE: kStripPlain, kStripRope (rotate the queries as they are staged) or
+// kStripLse (also save each row's log-sum-exp); separate instantiations keep
+// the plain kernel's registers to itself.
+template <int D, int G, int MODE>
 __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p) {
+  constexpr bool ROPE = MODE == kStripRope;
   using Gm = TileGeom<D>;
   constexpr int NW = G;
   constexpr int NT = NW * 64;
@@ -723,7 +728,7 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
                                    tile_mask(kt + 1), W, half, lane);
       st.template fold<false>(s, p.scale_log2, v_ring[wk1 % NR], nullptr, 0, 0, W, half, lane);
       store_o_rows(tw0);
-      if (p.lse) st.store_lse(p.lse + (long)b * p.Sq * p.Hq, p.Hq, tw0, G, g, p.Sq, col, half);
+      if constexpr (MODE == kStripLse) st.store_lse(p.lse + (long)b * p.Sq * p.Hq, p.Hq, tw0, G, g, p.Sq, col, half);
     }
     // the new tile's slot held tile new_kt - NR, older than this block's window
     if (have_new) {
@@ -750,7 +755,6 @@ static hipError_t launch_generic(const PrefillArgs& a0, hipStream_t stream) {
 
 template <int D, int G>
 static hipError_t launch_strip(const PrefillArgs& a0, int num_cu, hipStream_t stream) {
-  // prefill_swa_strip_kernel<D, G, true> also rotates the queries
   PrefillArgs a = a0;
   a.n_tb = (a.Sq + 31) / 32;
   const int bgs = a.B * a.Hkv;
@@ -760,9 +764,11 @@ static hipError_t launch_strip(const PrefillArgs& a0, int num_cu, hipStream_t st
   a.per_xcd = spb;
   a.total = bgs * spb;
   if (a.rope_hr > 0)
-    hipLaunchKernelGGL((prefill_swa_strip_kernel<D, G, true>), dim3(a.total), dim3(G * 64), 0, stream, a);
+    hipLaunchKernelGGL((prefill_swa_strip_kernel<D, G, kStripRope>), dim3(a.total), dim3(G * 64), 0, stream, a);
+  else if (a.lse)
+    hipLaunchKernelGGL((prefill_swa_strip_kernel<D, G, kStripLse>), dim3(a.total), dim3(G * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_swa_strip_kernel<D, G, false>), dim3(a.total), dim3(G * 64), 0, stream, a);
+    hipLaunchKernelGGL((prefill_swa_strip_kernel<D, G, kStripPlain>), dim3(a.total), dim3(G * 64), 0, stream, a);
   return hipGetLastError();
 }
 
