@@ -57,6 +57,26 @@ __device__ __forceinline__ long qrow_off(int t0, int m, int G, int g, long q_tok
   return (long)(t0 + m / G) * q_tok + (long)(g * G + m % G) * D;
 }
 
+// <x, y> of bf16 vectors in fp32, two products per v_dot2_f32_bf16.
+__device__ __forceinline__ float dot_bf16x8(const bf16x8& x, const bf16x8& y, float acc) {
+#define SWA_DOT2_XY(e) \
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, e, e + 1), \
+                                        __builtin_shufflevector(y, y, e, e + 1), acc, false)
+  SWA_DOT2_XY(0);
+  SWA_DOT2_XY(2);
+  SWA_DOT2_XY(4);
+  SWA_DOT2_XY(6);
+#undef SWA_DOT2_XY
+  return acc;
+}
+template <int NC>
+__device__ __forceinline__ float dot_bf16(const bf16x8 (&x)[NC], const bf16x8 (&y)[NC]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc = dot_bf16x8(x[c], y[c], acc);
+  return acc;
+}
+
 // Is key j visible from the query at position i?
 __device__ __forceinline__ bool visible(int i, int j, int window) {
   return j <= i && (window <= 0 || j > i - window);
@@ -331,8 +351,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
       qop[c] = tok < a.Sq ? *(const bf16x8*)(a.q + qoff + c * 16) : bf16x8{};
       oop[c] = tok < a.Sq ? *(const bf16x8*)(a.dout + qoff + c * 16) : bf16x8{};
       const bf16x8 ov = tok < a.Sq ? *(const bf16x8*)(a.o + qoff + c * 16) : bf16x8{};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part = fmaf((float)oop[c][e], (float)ov[e], part);
+      part = dot_bf16x8(oop[c], ov, part);
     }
     del = halves_sum(part);
     float term = 0.0f;
@@ -443,17 +462,264 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- dQ, sliding window
+// Persistent over a strip of consecutive TB-token blocks of one (b, g), like
+// the forward's strip kernel: the K/V tiles of the window live in an LDS ring
+// (each tile is loaded once per strip), and while a block is computed the next
+// block's q, dO, O rows and LSE are already loading into a second register
+// set (one wave per SIMD, so the register file holds both).  Per lane the
+// sink-gradient terms of the whole strip are summed, then reduced in a fixed
+// order into one partial per (strip, head).
+constexpr int kDqRing = 7;
+
+template <int D>
+struct DqRows {
+  bf16x8 q[D / 16], o[D / 16], ov[D / 16];  // q, dO, O in B-operand layout
+  float lse;
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
+  using Gm = BwdGeom<D>;
+  using KT_ = typename Gm::Tile;     // K tile: row-major reads and transposed reads
+  using VT_ = KTile<D>;              // V tile: row-major reads only
+  constexpr int NW = 4, NT = 256;
+  constexpr int TQ = BKT / G;        // tokens per wave
+  constexpr int TB = TQ * NW;        // tokens per block
+  constexpr int NR = kDqRing;
+  __shared__ __attribute__((aligned(16))) uint16_t k_ring[NR][KT_::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_ring[NR][VT_::ELEMS];
+  __shared__ float sink_red[NW][32];
+
+  const int n_tb = (a.Sq + TB - 1) / TB;
+  const int spb = a.strips_per_bg;
+  const int strip = blockIdx.x;
+  const int bg = strip / spb, sidx = strip - bg * spb;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int blk0 = (int)((long)sidx * n_tb / spb), blk1 = (int)((long)(sidx + 1) * n_tb / spb);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_index();
+  const int half = lane >> 5, col = lane & 31;
+  const long q_tok = (long)a.Hq * D, kv_tok = (long)a.Hkv * D;
+  const int W = a.window;
+  const int h = g * G + col % G;
+  const float c2 = a.scale_log2;
+  const float sink = a.sinks ? a.sinks[h] : 0.0f;
+
+  auto kt_lo = [&](int blk) { return max(0, a.q_offset + blk * TB - W + 1) / BKT; };
+  auto kt_hi = [&](int blk) { return (a.q_offset + min(blk * TB + TB, a.Sq) - 1) / BKT; };
+
+  // this lane's query row of block blk: token blk*TB + wv*TQ + col/G, head h
+  auto load_rows = [&](DqRows<D>& r, int blk) {
+    const int tok = blk * TB + wv * TQ + col / G;
+    if (tok < a.Sq) {
+      const long off = ((long)b * a.Sq + tok) * q_tok + (long)h * D + half * 8;
+#pragma unroll
+      for (int c = 0; c < Gm::NC; ++c) {
+        r.q[c] = *(const bf16x8*)(a.q + off + c * 16);
+        r.o[c] = *(const bf16x8*)(a.dout + off + c * 16);
+        r.ov[c] = *(const bf16x8*)(a.o + off + c * 16);
+      }
+      r.lse = a.lse[((long)b * a.Sq + tok) * a.Hq + h];
+    } else {
+#pragma unroll
+      for (int c = 0; c < Gm::NC; ++c) {
+        r.q[c] = bf16x8{};
+        r.o[c] = bf16x8{};
+        r.ov[c] = bf16x8{};
+      }
+      r.lse = __builtin_inff();
+    }
+  };
+
+  // K/V tile staging through registers (two 16-byte chunks per thread and
+  // tensor for D = 128); rows at or past Sk read as zeros
+  constexpr int CPR = D / 8;
+  constexpr int IT = (Gm::CH + NT - 1) / NT;
+  u32x4 kpre[IT], vpre[IT];
+  const long kvb = (long)b * a.Sk * kv_tok + (long)g * D;
+  auto load_tile = [&](int kt) {
+    const int kb = kt * BKT;
+    const uint32_t bytes = (uint32_t)(((min(BKT, a.Sk - kb) - 1) * kv_tok + D) * 2);
+    const rsrc_t rk = make_rsrc(a.k + kvb + (long)kb * kv_tok, bytes);
+    const rsrc_t rv = make_rsrc(a.v + kvb + (long)kb * kv_tok, bytes);
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int c = tid + i * NT;
+      if (c < Gm::CH) {
+        const uint32_t off = (uint32_t)(((c / CPR) * kv_tok + (c % CPR) * 8) * 2);
+        kpre[i] = buf_load16(rk, off, 0);
+        vpre[i] = buf_load16(rv, off, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int kt) {
+    uint16_t* kd = k_ring[kt % NR];
+    uint16_t* vd = v_ring[kt % NR];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int c = tid + i * NT;
+      if (c < Gm::CH) {
+        *(u32x4*)&kd[KT_::off(c / CPR, (c % CPR) * 8)] = kpre[i];
+        *(u32x4*)&vd[VT_::off(c / CPR, (c % CPR) * 8)] = vpre[i];
+      }
+    }
+  };
+
+  float sterm = 0.0f;  // this lane's sink-gradient terms over the strip
+  // dQ of one block from the ring, with the rows in r
+  auto block = [&](const DqRows<D>& r, int blk) {
+    const int tw0 = blk * TB + wv * TQ;
+    const int tok = tw0 + col / G;
+    const int qpos = a.q_offset + tok;
+    const float del = halves_sum(dot_bf16(r.o, r.ov));
+    const float lse2 = r.lse * kLog2e;
+    if (tok < a.Sq) {
+      if (half == 0) a.delta[((long)b * a.Sq + tok) * a.Hq + h] = del;
+      if (a.sinks) sterm += __expf(sink - r.lse) * del;
+    }
+    if (tw0 >= a.Sq) return;
+    const int wpos_lo = a.q_offset + tw0, wpos_hi = a.q_offset + min(tw0 + TQ, a.Sq) - 1;
+    const int wk0 = max(0, wpos_lo - W + 1) / BKT, wk1 = wpos_hi / BKT;
+    f32x16 dq[Gm::ND];
+#pragma unroll
+    for (int db = 0; db < Gm::ND; ++db) dq[db] = f32x16{};
+    for (int kt = wk0; kt <= wk1; ++kt) {
+      const int kb = kt * BKT;
+      const uint16_t* kt_t = k_ring[kt % NR];
+      const uint16_t* vt_t = v_ring[kt % NR];
+      const lds_u16* ka = lane_base(lds_addr(kt_t), KT_::k_lane_off(lane));
+      const lds_u16* va = lane_base(lds_addr(vt_t), VT_::k_lane_off(lane));
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int c = 0; c < Gm::NC; ++c) {
+        s = mfma32(KT_::k_operand(ka, c), r.q[c], s);
+        dp = mfma32(VT_::k_operand(va, c), r.o[c], dp);
+      }
+      const bool edge = !(kb + BKT - 1 <= wpos_lo && kb > wpos_hi - W);
+      bf16x8 sb[2];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p = exp2_fast(fmaf(s[v], c2, -lse2));
+        if (edge) {
+          const int j = kb + c_row(v, half);
+          if (!visible(qpos, j, W)) p = 0.0f;
+        }
+        sb[v >> 3][v & 7] = (__bf16)(p * (dp[v] - del));
+      }
+      const lds_u16* kt_op = lane_base(lds_addr(kt_t), KT_::vt_lane_off(lane));
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < Gm::ND; ++db) dq[db] = mfma32(KT_::vt_operand(kt_op, db, kc), sb[kc], dq[db]);
+    }
+    if (tok < a.Sq) {
+      uint16_t* dqp = a.dq + ((long)b * a.Sq + tok) * q_tok + (long)h * D;
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 y = {dq[db][4 * a4] * a.scale, dq[db][4 * a4 + 1] * a.scale, dq[db][4 * a4 + 2] * a.scale,
+                           dq[db][4 * a4 + 3] * a.scale};
+          *(bf16x4*)(dqp + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(y, bf16x4);
+        }
+    }
+  };
+
+  DqRows<D> ra, rb;
+  int loaded_hi = -1;
+  if (blk0 < blk1) {
+    loaded_hi = kt_hi(blk0);
+    for (int kt = kt_lo(blk0); kt <= loaded_hi; ++kt) {
+      load_tile(kt);
+      store_tile(kt);
+    }
+    load_rows(ra, blk0);
+  }
+  __syncthreads();
+  // one block with rows `cur` while `nxt` loads the next block's rows and the
+  // next block's new K/V tile, if any, is staged after the compute
+  auto step = [&](const DqRows<D>& cur, DqRows<D>& nxt, int blk) {
+    const bool more = blk + 1 < blk1;
+    const int new_kt = more ? kt_hi(blk + 1) : -1;
+    const bool have_new = new_kt > loaded_hi;
+    if (more) load_rows(nxt, blk + 1);
+    if (have_new) load_tile(new_kt);
+    block(cur, blk);
+    if (have_new) {
+      store_tile(new_kt);
+      loaded_hi = new_kt;
+    }
+    __syncthreads();
+  };
+  for (int blk = blk0; blk < blk1; blk += 2) {
+    step(ra, rb, blk);
+    if (blk + 1 < blk1) step(rb, ra, blk + 1);
+  }
+
+  // this strip's sink-gradient partial per head, fixed order
+  if (a.sinks) {
+    if (half == 0) sink_red[wv][col] = sterm;
+    __syncthreads();
+    if (tid < G) {
+      float sum = 0.0f;
+      for (int wq = 0; wq < NW; ++wq)
+        for (int c = tid; c < 32; c += G) sum += sink_red[wq][c];
+      a.sink_part[((long)b * spb + sidx) * a.Hq + g * G + tid] = -sum;
+    }
+  }
+}
+
+// Can the strip dQ kernel hold every block's window (plus the next block's
+// new tile) in its ring?  Blocks start at positions q_offset + blk*TB.
+static bool dq_strip_fits(const BwdArgs& a, int G) {
+  if (a.window <= 0 || (G != 4 && G != 8)) return false;
+  const int TB = (BKT / G) * 4;
+  for (int blk = 0; blk < 2 * BKT / TB; ++blk) {
+    const int p0 = a.q_offset + blk * TB;
+    const int lo = max(0, p0 - a.window + 1) / BKT, hi = (p0 + TB - 1) / BKT;
+    // the lowest tile a block can need is floor((p0 - W + 1) / 32) (or 0)
+    const int lo_unclamped = (p0 - a.window + 1) >= 0 ? lo : -((-(p0 - a.window + 1) + BKT - 1) / BKT);
+    if (hi - lo_unclamped + 1 + 1 > kDqRing) return false;
+  }
+  return true;
+}
+
 template <int D, int G>
 hipError_t launch_bwd_dg(BwdArgs a, hipStream_t s) {
   // dQ first: it also leaves D = <dO, O> for dK/dV and the dsink partials
-  const int TB = (BKT / G) * kDqWaves;
-  const int n_tb = (a.Sq + TB - 1) / TB;
-  a.n_sink_parts = a.B * n_tb;
-  if (n_tb > 0) {
-    const int total = n_tb * a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, G, kDqWaves>), dim3(8 * ((total + 7) / 8)), dim3(kDqWaves * 64), 0, s, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  int n_tb = 0;
+  if constexpr (G == 4 || G == 8) {
+    if (dq_strip_fits(a, G)) {
+      const int TB = (BKT / G) * 4;
+      n_tb = (a.Sq + TB - 1) / TB;
+      int dev = 0, num_cu = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || num_cu <= 0)
+        num_cu = 256;
+      const int bgs = a.B * a.Hkv;
+      int spb = num_cu / bgs;
+      if (spb < 1) spb = 1;
+      if (spb > n_tb) spb = n_tb;
+      a.strips_per_bg = spb;
+      a.n_sink_parts = a.B * spb;
+      if (n_tb > 0) {
+        hipLaunchKernelGGL((bwd_dq_strip_kernel<D, G>), dim3(bgs * spb), dim3(256), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    }
+  }
+  if (a.strips_per_bg == 0) {
+    const int TB = (BKT / G) * kDqWaves;
+    n_tb = (a.Sq + TB - 1) / TB;
+    a.n_sink_parts = a.B * n_tb;
+    if (n_tb > 0) {
+      const int total = n_tb * a.B * a.Hkv;
+      hipLaunchKernelGGL((bwd_dq_kernel<D, G, kDqWaves>), dim3(8 * ((total + 7) / 8)), dim3(kDqWaves * 64), 0, s, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (a.dsink) {
     if (a.sinks && n_tb > 0) {

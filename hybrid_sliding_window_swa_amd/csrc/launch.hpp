@@ -77,6 +77,7 @@ struct BwdArgs {
   int window, q_offset;
   float scale, scale_log2;
   int n_sink_parts;       // set by the launcher
+  int strips_per_bg;      // set by the launcher (0: the non-persistent dQ kernel)
 };
 
 struct BwdPlan {
