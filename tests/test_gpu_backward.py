@@ -116,3 +116,24 @@ def test_backward_dsink_deterministic_and_unseen_keys_zero():
     assert not a[1][:, :first_seen].float().abs().sum().item()
     assert not a[2][:, :first_seen].float().abs().sum().item()
     assert a[1][:, first_seen:].float().abs().sum().item() > 0
+
+
+def test_full_size_backward_swa_32k():
+    """The bench's training workload (SWA 32K, 64 query heads, 8 KV heads,
+    D 128, sinks): every element of dq, dk, dv and dsink against the oracle."""
+    from swa_inputs import PREFILL_CONFIGS
+    dev = device()
+    m = swa()
+    cfg = PREFILL_CONFIGS["swa_32k"]
+    print(f"[full-size] {cfg.name} backward: inputs", flush=True)
+    q, k, v, sinks = prefill_inputs(cfg, device=dev)
+    dout = normal(q.shape, derive_seed(cfg.seed, "dout"), dev, torch.bfloat16)
+    o, lse = m.swa_attn_prefill_lse(q, k, v, sinks, cfg.window, cfg.q_offset, cfg.scale)
+    dq, dk, dv, dsink = m.swa_attn_backward(q, k, v, sinks, o, lse, dout, cfg.window, cfg.q_offset, cfg.scale)
+    torch.cuda.synchronize()
+    print(f"[full-size] {cfg.name} backward: oracle", flush=True)
+    rq, rk, rv, rs = oracle.prefill_backward(q, k, v, dout, sinks, cfg.window, cfg.q_offset, cfg.scale)
+    _check_grad(dq, rq, "full dq")
+    _check_grad(dk, rk, "full dk")
+    _check_grad(dv, rv, "full dv")
+    _check_grad(dsink, rs, "full dsink")

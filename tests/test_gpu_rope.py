@@ -170,3 +170,50 @@ def test_prefill_rope_unsupported_configs_raise():
     k2 = torch.zeros((1, 64 + 333, 2, 128), dtype=torch.bfloat16, device=dev)
     with pytest.raises(m.SwaError):
         m.swa_attn_prefill_rope(q, k2, k2, None, 128, 42, 10000.0, q_offset=333)
+
+
+def test_full_size_rope_32k():
+    """The bench's RoPE workload: every rotated element of q [1,32768,64,128]
+    and k [1,32768,8,128] against the oracle, at positions 229376 .. 262143
+    (the 256K stack's last chunk) for q and 0 .. 32767 for k."""
+    from swa_inputs import PREFILL_CONFIGS
+    dev = device()
+    m = swa()
+    cfg = PREFILL_CONFIGS["swa_32k"]
+    q, k, _, _ = prefill_inputs(cfg, device=dev)
+    rot, base = m.rope_dims(cfg.D), 640000.0
+    for name, x, off in (("q", q, 229376), ("k", k, 0)):
+        x0 = x.cpu()
+        m.swa_rope_apply(x, rot, base, None, off)
+        torch.cuda.synchronize()
+        pos = off + np.arange(cfg.S)[None, :]
+        ref = oracle.rope(x0[..., :rot].contiguous(), pos, rot, base)
+        got = x.cpu()
+        _check_rope(got[..., :rot].contiguous(), x0[..., :rot].contiguous(), ref, rot, "bf16", f"full {name}")
+        assert torch.equal(got[..., rot:].view(torch.int16), x0[..., rot:].view(torch.int16))
+
+
+def test_full_size_prefill_rope_32k():
+    """The fused SWA prefill at 32K (queries rotated as staged, keys rotated
+    once) on sampled rows against the oracle."""
+    from swa_inputs import PREFILL_CONFIGS, sample_rows
+    dev = device()
+    m = swa()
+    cfg = PREFILL_CONFIGS["swa_32k"]
+    q, k, v, sinks = prefill_inputs(cfg, device=dev)
+    rot, base = m.rope_dims(cfg.D), 10000.0
+    k_rot = k.clone()
+    m.swa_rope_apply(k_rot, rot, base)
+    o = m.swa_attn_prefill_rope(q, k_rot, v, sinks, cfg.window, rot, base, 0, cfg.scale)
+    torch.cuda.synchronize()
+    S = cfg.S
+    rows = sample_rows(S, 512, cfg.seed + 1, (0, 1, 31, 32, 127, 128, 129, S - 1))
+    rows_d = rows.to(dev)
+    got = o[0].index_select(0, rows_d).cpu()
+    q_rows = oracle.rope(q[0].index_select(0, rows_d).cpu()[None], rows.numpy()[None, :], rot, base)[0]
+    lo = max(0, int(rows.min()) - cfg.window + 1)
+    hi = int(rows.max()) + 1
+    kk = oracle.rope(k[0, lo:hi].cpu()[None], np.arange(lo, hi)[None, :], rot, base)[0]
+    ref = oracle.prefill_rows(q_rows, rows, kk, v[0, lo:hi].cpu(), sinks.cpu(), cfg.window, 0, cfg.scale,
+                              k_base=lo)
+    assert_close(got, ref, BF16_TOL, "full prefill_rope")
