@@ -41,6 +41,7 @@ namespace {
 
 constexpr int BKT = 32;  // keys per tile / rows per query block
 constexpr int kDqWaves = 8;      // waves (32-row query blocks) per dQ workgroup
+constexpr int kDkdvWaves = 2;    // 32-key tiles (waves) per dK/dV workgroup (measured: 2 beats 1 and 4)
 constexpr int kDkdvPrefetch = 1;  // query blocks loaded ahead in the dK/dV kernel (deeper measured slower)
 
 template <int D>
@@ -117,11 +118,11 @@ __device__ __forceinline__ void load_rows_operand(bf16x8 (&x)[D / 16], const uin
   for (int c = 0; c < D / 16; ++c) x[c] = __builtin_bit_cast(bf16x8, buf_load16(r, voff + c * 32, 0));
 }
 
-template <int D, int G, int PF>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+template <int D, int G, int PF, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
   using Gm = BwdGeom<D>;
   using Tile = typename Gm::Tile;
-  constexpr int NW = 4;
+  constexpr int NT = NW * 64;
   constexpr int TQ = BKT / G;                  // tokens per query block
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][Gm::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t o_lds[2][Gm::ELEMS];  // dO
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   // latency with one workgroup per CU; LDS holds two blocks (the one being
   // computed and the next, stored after the compute and before the barrier).
   constexpr int CPR = D / 8;                   // chunks per row
-  constexpr int IT = Gm::CH / 256;
+  constexpr int IT = Gm::CH / NT;
   u32x4 qpre[PF][IT], opre[PF][IT];
   float lpre[PF], dpre[PF];
   const long qbase_b = (long)b * a.Sq * q_tok;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int t0 = qb * TQ;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       const int m = c / CPR, ch = c % CPR;
       const int tok = t0 + m / G;
       if (tok < a.Sq) {
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   auto store_block = [&](int buf, int slot) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       const int m = c / CPR, ch = c % CPR;
       *(u32x4*)&q_lds[buf][Tile::off(m, ch * 8)] = qpre[slot][i];
       *(u32x4*)&o_lds[buf][Tile::off(m, ch * 8)] = opre[slot][i];
@@ -730,10 +731,11 @@ hipError_t launch_bwd_dg(BwdArgs a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int n_kb = (a.Sk + 4 * BKT - 1) / (4 * BKT);
+  const int n_kb = (a.Sk + kDkdvWaves * BKT - 1) / (kDkdvWaves * BKT);
   if (n_kb > 0) {
     const int total = n_kb * a.B * a.Hkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, G, kDkdvPrefetch>), dim3(8 * ((total + 7) / 8)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, G, kDkdvPrefetch, kDkdvWaves>), dim3(8 * ((total + 7) / 8)),
+                       dim3(kDkdvWaves * 64), 0, s, a);
     return hipGetLastError();
   }
   return hipSuccess;
