@@ -185,27 +185,35 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
   float lpre[PF], dpre[PF];
   const long qbase_b = (long)b * a.Sq * q_tok;
   const long rbase_b = (long)b * a.Sq * a.Hq;
+  // Plain buffer loads only (no branch, no arithmetic on the results until
+  // the store to LDS), so the compiler leaves them in flight while a block is
+  // computed; rows at or past Sq read as zeros (zero q and dO rows give zero
+  // dS and zero dV contributions whatever their P).
+  uint32_t ch_voff[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int c = tid + i * NT;
+    const int m = c / CPR, ch = c % CPR;
+    ch_voff[i] = (uint32_t)((((m / G) * q_tok) + (long)(m % G) * D + ch * 8) * 2);
+  }
+  const uint32_t row_voff4 = (uint32_t)((((tid & (BKT - 1)) / G) * a.Hq + (tid & (BKT - 1)) % G) * 4);
   auto load_block = [&](int qb, int slot) {
     const int t0 = qb * TQ;
+    const int ntok = min(TQ, a.Sq - t0);
+    const long base = qbase_b + (long)t0 * q_tok + (long)g * G * D;
+    const uint32_t bytes = (uint32_t)(((ntok - 1) * q_tok + (long)G * D) * 2);
+    const rsrc_t rq = make_rsrc(a.q + base, bytes), ro = make_rsrc(a.dout + base, bytes);
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const int c = tid + i * NT;
-      const int m = c / CPR, ch = c % CPR;
-      const int tok = t0 + m / G;
-      if (tok < a.Sq) {
-        const long off = qbase_b + qrow_off(t0, m, G, g, q_tok, D) + ch * 8;
-        qpre[slot][i] = *(const u32x4*)(a.q + off);
-        opre[slot][i] = *(const u32x4*)(a.dout + off);
-      } else {
-        qpre[slot][i] = u32x4{0, 0, 0, 0};
-        opre[slot][i] = u32x4{0, 0, 0, 0};
-      }
+      qpre[slot][i] = buf_load16(rq, ch_voff[i], 0);
+      opre[slot][i] = buf_load16(ro, ch_voff[i], 0);
     }
     if (tid < BKT) {
-      const int tok = t0 + tid / G;
-      const long row = rbase_b + (long)tok * a.Hq + g * G + tid % G;
-      lpre[slot] = tok < a.Sq ? a.lse[row] * kLog2e : __builtin_inff();
-      dpre[slot] = tok < a.Sq ? a.delta[row] : 0.0f;
+      const long rb0 = rbase_b + (long)t0 * a.Hq + g * G;
+      const uint32_t rbytes = (uint32_t)(((ntok - 1) * a.Hq + G) * 4);
+      const rsrc_t rl = make_rsrc(a.lse + rb0, rbytes), rd = make_rsrc(a.delta + rb0, rbytes);
+      lpre[slot] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)row_voff4, 0, 0));
+      dpre[slot] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rd, (int)row_voff4, 0, 0));
     }
   };
   auto store_block = [&](int buf, int slot) {
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
       *(u32x4*)&o_lds[buf][Tile::off(m, ch * 8)] = opre[slot][i];
     }
     if (tid < BKT) {
-      lse_lds[buf][tid] = lpre[slot];
+      lse_lds[buf][tid] = lpre[slot] * kLog2e;
       del_lds[buf][tid] = dpre[slot];
     }
   };
@@ -510,27 +518,27 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
   auto kt_lo = [&](int blk) { return max(0, a.q_offset + blk * TB - W + 1) / BKT; };
   auto kt_hi = [&](int blk) { return (a.q_offset + min(blk * TB + TB, a.Sq) - 1) / BKT; };
 
-  // this lane's query row of block blk: token blk*TB + wv*TQ + col/G, head h
+  // this lane's query row of block blk: token blk*TB + wv*TQ + col/G, head h.
+  // Plain buffer loads only (no branch, no arithmetic on the results), so the
+  // compiler can leave them in flight across the block that is computed
+  // meanwhile; rows at or past Sq read as zeros, which makes their dS zero.
+  const uint32_t row_voff = (uint32_t)((((wv * TQ + col / G) * q_tok) + (long)h * D + half * 8) * 2);
+  const uint32_t lse_voff = (uint32_t)(((wv * TQ + col / G) * a.Hq + h) * 4);
   auto load_rows = [&](DqRows<D>& r, int blk) {
-    const int tok = blk * TB + wv * TQ + col / G;
-    if (tok < a.Sq) {
-      const long off = ((long)b * a.Sq + tok) * q_tok + (long)h * D + half * 8;
+    const int t0 = blk * TB;
+    const int ntok = min(TB, a.Sq - t0);
+    const long base = ((long)b * a.Sq + t0) * q_tok;
+    const uint32_t bytes = (uint32_t)(((ntok - 1) * q_tok + (long)a.Hq * D) * 2);
+    const rsrc_t rq = make_rsrc(a.q + base, bytes), ro = make_rsrc(a.dout + base, bytes);
+    const rsrc_t rv = make_rsrc(a.o + base, bytes);
 #pragma unroll
-      for (int c = 0; c < Gm::NC; ++c) {
-        r.q[c] = *(const bf16x8*)(a.q + off + c * 16);
-        r.o[c] = *(const bf16x8*)(a.dout + off + c * 16);
-        r.ov[c] = *(const bf16x8*)(a.o + off + c * 16);
-      }
-      r.lse = a.lse[((long)b * a.Sq + tok) * a.Hq + h];
-    } else {
-#pragma unroll
-      for (int c = 0; c < Gm::NC; ++c) {
-        r.q[c] = bf16x8{};
-        r.o[c] = bf16x8{};
-        r.ov[c] = bf16x8{};
-      }
-      r.lse = __builtin_inff();
+    for (int c = 0; c < Gm::NC; ++c) {
+      r.q[c] = __builtin_bit_cast(bf16x8, buf_load16(rq, row_voff + c * 32, 0));
+      r.o[c] = __builtin_bit_cast(bf16x8, buf_load16(ro, row_voff + c * 32, 0));
+      r.ov[c] = __builtin_bit_cast(bf16x8, buf_load16(rv, row_voff + c * 32, 0));
     }
+    const rsrc_t rl = make_rsrc(a.lse + ((long)b * a.Sq + t0) * a.Hq, (uint32_t)(ntok * a.Hq * 4));
+    r.lse = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)lse_voff, 0, 0));
   };
 
   // K/V tile staging through registers (two 16-byte chunks per thread and
@@ -568,17 +576,23 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
   };
 
   float sterm = 0.0f;  // this lane's sink-gradient terms over the strip
-  // dQ of one block from the ring, with the rows in r
-  auto block = [&](const DqRows<D>& r, int blk) {
-    const int tw0 = blk * TB + wv * TQ;
-    const int tok = tw0 + col / G;
-    const int qpos = a.q_offset + tok;
-    const float del = halves_sum(dot_bf16(r.o, r.ov));
-    const float lse2 = r.lse * kLog2e;
+  // Per-row scalars of a block's rows, computed when they are first needed,
+  // at the end of the step that loaded them: D = <dO, O> (also written for
+  // dK/dV), LSE * log2(e), and the row's sink-gradient term.
+  auto prep = [&](const DqRows<D>& r, int blk, float& del, float& lse2) {
+    const int tok = blk * TB + wv * TQ + col / G;
+    del = halves_sum(dot_bf16(r.o, r.ov));
+    lse2 = r.lse * kLog2e;
     if (tok < a.Sq) {
       if (half == 0) a.delta[((long)b * a.Sq + tok) * a.Hq + h] = del;
       if (a.sinks) sterm += __expf(sink - r.lse) * del;
     }
+  };
+  // dQ of one block from the ring, with the rows in r
+  auto block = [&](const DqRows<D>& r, int blk, float del, float lse2) {
+    const int tw0 = blk * TB + wv * TQ;
+    const int tok = tw0 + col / G;
+    const int qpos = a.q_offset + tok;
     if (tw0 >= a.Sq) return;
     const int wpos_lo = a.q_offset + tw0, wpos_hi = a.q_offset + min(tw0 + TQ, a.Sq) - 1;
     const int wk0 = max(0, wpos_lo - W + 1) / BKT, wk1 = wpos_hi / BKT;
@@ -628,6 +642,7 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
   };
 
   DqRows<D> ra, rb;
+  float del_a = 0.0f, lse2_a = 0.0f, del_b = 0.0f, lse2_b = 0.0f;
   int loaded_hi = -1;
   if (blk0 < blk1) {
     loaded_hi = kt_hi(blk0);
@@ -636,26 +651,34 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
       store_tile(kt);
     }
     load_rows(ra, blk0);
+    prep(ra, blk0, del_a, lse2_a);
   }
   __syncthreads();
-  // one block with rows `cur` while `nxt` loads the next block's rows and the
-  // next block's new K/V tile, if any, is staged after the compute
-  auto step = [&](const DqRows<D>& cur, DqRows<D>& nxt, int blk) {
+  // one block with rows `cur` while `nxt` loads the next block's rows (their
+  // per-row scalars are formed after the compute) and the next block's new
+  // K/V tile, if any, is staged after the compute
+  auto step = [&](const DqRows<D>& cur, float del_c, float lse2_c, DqRows<D>& nxt, float& del_n, float& lse2_n,
+                  int blk) {
     const bool more = blk + 1 < blk1;
     const int new_kt = more ? kt_hi(blk + 1) : -1;
     const bool have_new = new_kt > loaded_hi;
     if (more) load_rows(nxt, blk + 1);
     if (have_new) load_tile(new_kt);
-    block(cur, blk);
+    block(cur, blk, del_c, lse2_c);
     if (have_new) {
       store_tile(new_kt);
       loaded_hi = new_kt;
     }
+    if (more) prep(nxt, blk + 1, del_n, lse2_n);
+    // Drain here, a block after the loads were issued: the next step then
+    // starts with nothing in flight, so no wait the compiler derives for the
+    // current rows can land on the prefetch issued at its top.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   for (int blk = blk0; blk < blk1; blk += 2) {
-    step(ra, rb, blk);
-    if (blk + 1 < blk1) step(rb, ra, blk + 1);
+    step(ra, del_a, lse2_a, rb, del_b, lse2_b, blk);
+    if (blk + 1 < blk1) step(rb, del_b, lse2_b, ra, del_a, lse2_a, blk + 1);
   }
 
   // this strip's sink-gradient partial per head, fixed order
