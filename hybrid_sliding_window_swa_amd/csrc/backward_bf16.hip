@@ -281,6 +281,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
     for (int u = 0; u < PF; ++u)
       if (1 + u < nblk) load_block(qb_lo + 1 + u, (1 + u) % PF);
   }
+  // Everything the prologue loaded (the K/V operands, the first blocks) is
+  // drained here, so that inside the loop no wait the compiler derives for
+  // those registers can land on a prefetch.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int n0 = 0; n0 < nblk; n0 += PF) {
 #pragma unroll
