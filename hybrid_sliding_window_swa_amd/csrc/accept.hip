@@ -59,6 +59,9 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
   }
 }
 
+// the logits are read once
+constexpr bool kAcceptNT = false;
+
 __device__ __forceinline__ float widen(float x) { return x; }
 __device__ __forceinline__ float widen(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
@@ -150,13 +153,13 @@ __global__ __launch_bounds__(kAcceptThreads) void argmax_partial_vec_kernel(Acce
   for (; e + (kLoadsInFlight - 1) * step < hi; e += kLoadsInFlight * step) {
     V x[kLoadsInFlight];
 #pragma unroll
-    for (int u = 0; u < kLoadsInFlight; ++u) x[u].x = *(const u32x4*)(lg + e + u * step);
+    for (int u = 0; u < kLoadsInFlight; ++u) x[u].x = load_pol<kAcceptNT>((const u32x4*)(lg + e + u * step));
 #pragma unroll
     for (int u = 0; u < kLoadsInFlight; ++u) consider(x[u], e + u * step);
   }
   for (; e < hi; e += step) {
     V x;
-    x.x = *(const u32x4*)(lg + e);
+    x.x = load_pol<kAcceptNT>((const u32x4*)(lg + e));
     consider(x, e);
   }
   int bi = INT_MAX;

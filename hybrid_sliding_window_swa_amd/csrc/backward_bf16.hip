@@ -41,6 +41,11 @@ namespace {
 
 constexpr int BKT = 32;  // keys per tile / rows per query block
 constexpr int kDqWaves = 8;      // waves (32-row query blocks) per dQ workgroup
+// Cache policies: the strip dQ kernel reads each q, dO and O row once (the
+// dK/dV kernel re-reads q and dO, so those stay cacheable there); dq, dk and
+// dv are written once.
+constexpr int kDqRowPolicy = kCacheDefault;
+constexpr bool kBwdOutNT = false;
 constexpr int kDkdvWaves = 2;    // 32-key tiles (waves) per dK/dV workgroup (measured: 2 beats 1 and 4)
 constexpr int kDkdvPrefetch = 1;  // query blocks loaded ahead in the dK/dV kernel (deeper measured slower)
 
@@ -313,8 +318,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
         const f32x4 yk = {dk[db][4 * a4] * a.scale, dk[db][4 * a4 + 1] * a.scale, dk[db][4 * a4 + 2] * a.scale,
                           dk[db][4 * a4 + 3] * a.scale};
         const f32x4 yv = {dv[db][4 * a4], dv[db][4 * a4 + 1], dv[db][4 * a4 + 2], dv[db][4 * a4 + 3]};
-        *(bf16x4*)(dkp + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(yk, bf16x4);
-        *(bf16x4*)(dvp + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(yv, bf16x4);
+        store_pol<kBwdOutNT>(__builtin_convertvector(yk, bf16x4), (bf16x4*)(dkp + db * 32 + 8 * a4 + 4 * half));
+        store_pol<kBwdOutNT>(__builtin_convertvector(yv, bf16x4), (bf16x4*)(dvp + db * 32 + 8 * a4 + 4 * half));
       }
   }
 }
@@ -537,9 +542,9 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
     const rsrc_t rv = make_rsrc(a.o + base, bytes);
 #pragma unroll
     for (int c = 0; c < Gm::NC; ++c) {
-      r.q[c] = __builtin_bit_cast(bf16x8, buf_load16(rq, row_voff + c * 32, 0));
-      r.o[c] = __builtin_bit_cast(bf16x8, buf_load16(ro, row_voff + c * 32, 0));
-      r.ov[c] = __builtin_bit_cast(bf16x8, buf_load16(rv, row_voff + c * 32, 0));
+      r.q[c] = __builtin_bit_cast(bf16x8, buf_load16<kDqRowPolicy>(rq, row_voff + c * 32, 0));
+      r.o[c] = __builtin_bit_cast(bf16x8, buf_load16<kDqRowPolicy>(ro, row_voff + c * 32, 0));
+      r.ov[c] = __builtin_bit_cast(bf16x8, buf_load16<kDqRowPolicy>(rv, row_voff + c * 32, 0));
     }
     const rsrc_t rl = make_rsrc(a.lse + ((long)b * a.Sq + t0) * a.Hq, (uint32_t)(ntok * a.Hq * 4));
     r.lse = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)lse_voff, 0, 0));
@@ -640,7 +645,7 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
         for (int a4 = 0; a4 < 4; ++a4) {
           const f32x4 y = {dq[db][4 * a4] * a.scale, dq[db][4 * a4 + 1] * a.scale, dq[db][4 * a4 + 2] * a.scale,
                            dq[db][4 * a4 + 3] * a.scale};
-          *(bf16x4*)(dqp + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(y, bf16x4);
+          store_pol<kBwdOutNT>(__builtin_convertvector(y, bf16x4), (bf16x4*)(dqp + db * 32 + 8 * a4 + 4 * half));
         }
     }
   };

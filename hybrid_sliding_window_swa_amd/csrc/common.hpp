@@ -59,11 +59,32 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Cache policy of a vector memory access: kCacheNT marks data that is
+// touched once (streamed rows, outputs) as non-temporal, so it does not
+// displace reused data in the L2 and the Infinity Cache.
+constexpr int kCacheDefault = 0, kCacheNT = 2;
+template <int POLICY = kCacheDefault>
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, POLICY);
 }
+template <int POLICY = kCacheDefault>
 __device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, POLICY);
+}
+
+// Plain global accesses with a cache policy (see kCacheNT).
+template <bool NT, typename T>
+__device__ __forceinline__ T load_pol(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void store_pol(T v, T* p) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
+  }
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.

@@ -6,12 +6,15 @@
 //     16-byte loads in flight per thread, XOR-reduced so nothing is dead code.
 //   * HBM copy: the same grid stride reading one 8 GiB buffer and writing
 //     another (bytes read + bytes written per second).
+//   * Both with default and with non-temporal loads / stores; the faster
+//     policy is the ceiling.
 //   * bf16 MFMA: v_mfma_f32_32x32x16_bf16 on four independent accumulators,
 //     two waves per SIMD, operands in registers (no memory traffic).
 //
 // Every kernel runs untimed for about half a second first, so the clocks
 // are at their sustained-load level, then the mean of several launches is
-// timed with HIP events (the streaming kernels: best of five grid sizes).
+// timed with HIP events (the streaming kernels: best of five grid sizes and
+// two cache policies).
 // One JSON line per measurement on stdout.
 // All accesses are grid-stride loops bounded by the element count.
 #include <hip/hip_runtime.h>
@@ -24,22 +27,39 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// NT: non-temporal loads and stores (the data is touched once)
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ p, long n16, uint32_t* out) {
   u32x4 acc = {0, 0, 0, 0};
   long i = blockIdx.x * 256L + threadIdx.x;
   const long stride = (long)gridDim.x * 256;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    const u32x4 a = ld<NT>(p + i), b = ld<NT>(p + i + stride), c = ld<NT>(p + i + 2 * stride),
+                d = ld<NT>(p + i + 3 * stride);
     acc ^= a ^ b ^ c ^ d;
   }
-  for (; i < n16; i += stride) acc ^= p[i];
+  for (; i < n16; i += stride) acc ^= ld<NT>(p + i);
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) out[0] = 1;
 }
 
+template <bool NT>
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ p, u32x4* __restrict__ q, long n16) {
   long i = blockIdx.x * 256L + threadIdx.x;
   const long stride = (long)gridDim.x * 256;
-  for (; i < n16; i += stride) q[i] = p[i];
+  for (; i < n16; i += stride) {
+    const u32x4 v = ld<NT>(p + i);
+    if constexpr (NT) {
+      __builtin_nontemporal_store(v, q + i);
+    } else {
+      q[i] = v;
+    }
+  }
 }
 
 constexpr int kMfmaIter = 8192;
@@ -114,23 +134,40 @@ int main() {
     return 1;
   if (!ok(hipMemset(a, 1, bytes), "hipMemset") || !ok(hipDeviceSynchronize(), "init")) return 1;
 
-  // streaming kernels: best of several grid sizes (clocks settle on the first)
+  // streaming kernels: best of several grid sizes and both cache policies
+  // (clocks settle on the first)
   float rd = 1e30f, cp = 1e30f;
   int rd_grid = 0, cp_grid = 0;
-  for (int mult : {4, 8, 16, 32, 64}) {
-    const int grid = mult * cus;
-    const float settle = mult == 4 ? 500.0f : 0.0f;
-    const float r = time_ms([&] { hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, 0, a, n16, flag); },
-                            settle, 10);
-    if (r < rd) { rd = r; rd_grid = grid; }
-    const float c = time_ms([&] { hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, 0, a, b, n16); },
-                            settle, 10);
-    if (c < cp) { cp = c; cp_grid = grid; }
+  bool rd_nt = false, cp_nt = false;
+  for (int nt = 0; nt < 2; ++nt) {
+    for (int mult : {4, 8, 16, 32, 64}) {
+      const int grid = mult * cus;
+      const float settle = (mult == 4 && nt == 0) ? 500.0f : 0.0f;
+      const float r = time_ms(
+          [&] {
+            if (nt)
+              hipLaunchKernelGGL(read_kernel<true>, dim3(grid), dim3(256), 0, 0, a, n16, flag);
+            else
+              hipLaunchKernelGGL(read_kernel<false>, dim3(grid), dim3(256), 0, 0, a, n16, flag);
+          },
+          settle, 10);
+      if (r < rd) { rd = r; rd_grid = grid; rd_nt = nt; }
+      const float c = time_ms(
+          [&] {
+            if (nt)
+              hipLaunchKernelGGL(copy_kernel<true>, dim3(grid), dim3(256), 0, 0, a, b, n16);
+            else
+              hipLaunchKernelGGL(copy_kernel<false>, dim3(grid), dim3(256), 0, 0, a, b, n16);
+          },
+          settle, 10);
+      if (c < cp) { cp = c; cp_grid = grid; cp_nt = nt; }
+    }
   }
-  printf("{\"measure\": \"hbm_read\", \"bytes\": %ld, \"grid\": %d, \"ms\": %.4f, \"GB/s\": %.1f}\n", bytes, rd_grid,
-         rd, bytes / (rd * 1e-3) / 1e9);
-  printf("{\"measure\": \"hbm_copy\", \"bytes_read_plus_written\": %ld, \"grid\": %d, \"ms\": %.4f, \"GB/s\": %.1f}\n",
-         2 * bytes, cp_grid, cp, 2.0 * bytes / (cp * 1e-3) / 1e9);
+  printf("{\"measure\": \"hbm_read\", \"bytes\": %ld, \"grid\": %d, \"nontemporal\": %s, \"ms\": %.4f, \"GB/s\": %.1f}\n",
+         bytes, rd_grid, rd_nt ? "true" : "false", rd, bytes / (rd * 1e-3) / 1e9);
+  printf("{\"measure\": \"hbm_copy\", \"bytes_read_plus_written\": %ld, \"grid\": %d, \"nontemporal\": %s, \"ms\": %.4f, "
+         "\"GB/s\": %.1f}\n",
+         2 * bytes, cp_grid, cp_nt ? "true" : "false", cp, 2.0 * bytes / (cp * 1e-3) / 1e9);
   const float mm = time_ms([&] { hipLaunchKernelGGL(mfma_kernel, dim3(mfma_blocks), dim3(512), 0, 0, sink, 0.001f); },
                            500.0f, 10);
   const double flop = (double)mfma_blocks * 8 * kMfmaIter * 4 * 32768.0;

@@ -29,6 +29,8 @@ namespace swa {
 namespace {
 
 constexpr int kRopeThreads = 256;
+// every rotated vector is read and written once
+constexpr bool kRopeNT = false;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeArgs a) {
 
   for (int q = tid; q < nrows * nv; q += kRopeThreads) {
     const int row = q / nv, v = q - row * nv;
-    const u32x4 d = *(const u32x4*)(gbase + row * row_bytes + v * 16);
+    const u32x4 d = load_pol<kRopeNT>((const u32x4*)(gbase + row * row_bytes + v * 16));
     uint32_t* dst = lds + row * pitch + v * 4;
     dst[0] = d[0];
     dst[1] = d[1];
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(RopeArgs a) {
   for (int q = tid; q < nrows * nv; q += kRopeThreads) {
     const int row = q / nv, v = q - row * nv;
     const uint32_t* src = lds + row * pitch + v * 4;
-    *(u32x4*)(gbase + row * row_bytes + v * 16) = u32x4{src[0], src[1], src[2], src[3]};
+    store_pol<kRopeNT>(u32x4{src[0], src[1], src[2], src[3]}, (u32x4*)(gbase + row * row_bytes + v * 16));
   }
 }
 

@@ -223,8 +223,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
     for (int i = 0; i < LD_IT; ++i) {
       const int c = lane + 64 * i;
       const long o = row_off(j, c / CPR) + (c % CPR) * 8;
-      kpre[i] = *(const u32x4*)(kb + o);
-      vpre[i] = *(const u32x4*)(vb + o);
+      // every cache row is read once: non-temporal, so the stream does not
+      // displace reused data in the L2 and the Infinity Cache (measured:
+      // 5.6 -> 6.1 TB/s on the 64-request global cache)
+      kpre[i] = __builtin_nontemporal_load((const u32x4*)(kb + o));
+      vpre[i] = __builtin_nontemporal_load((const u32x4*)(vb + o));
     }
   };
   auto store_tile = [&]() {
@@ -407,38 +410,66 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
 
 // Merge the splits of one (request, KV head): M = max(max_s m_s, sink),
 // l = sum_s l_s 2^(m_s - M) + 2^(sink - M), O = sum_s O_s 2^(m_s - M) / l.
+// Grid (B * Hkv, row groups): one thread per (row, 4 columns).  The splits
+// are taken kCombineBatch at a time with every load of a batch issued before
+// its first use (splits past the request's count alias its last split and get
+// weight zero), the running state rescaled between batches, so the kernel
+// waits on memory once per batch.
+constexpr int kCombineBatch = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void verify_combine_kernel(VerifyArgs p) {
   const int g = blockIdx.x % p.Hkv, b = blockIdx.x / p.Hkv;
-  const int L = p.cache_len[b];
-  const SplitRange sr = split_range(p, L);
   const int G = p.Hq / p.Hkv;
   const int R = G * p.T;
   constexpr int TPR = D / 4;            // threads per row (4 floats each)
-  constexpr int RPP = 256 / TPR;        // rows per pass
+  constexpr int RPP = 256 / TPR;        // rows per workgroup
   const int tid = threadIdx.x;
+  const int m = blockIdx.y * RPP + tid / TPR;
+  if (m >= R) return;
   const int d = (tid % TPR) * 4;
-  for (int m = tid / TPR; m < R; m += RPP) {
-    const int t = m / G, h = g * G + m % G;
-    const long base = ((long)b * p.Hkv + g) * p.nsplit * p.r_pad + m;
-    const float sink2 = p.sinks ? p.sinks[h] * kLog2e : kNegInf;
-    float M = sink2;
-    for (int s = 0; s < sr.ns; ++s) M = fmaxf(M, p.ws_ml[(base + (long)s * p.r_pad) * 2]);
-    float l = sink2 == kNegInf ? 0.0f : exp2_fast(sink2 - M);
-    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s = 0; s < sr.ns; ++s) {
-      const long row = base + (long)s * p.r_pad;
-      const float ms = p.ws_ml[row * 2];
-      if (ms == kNegInf) continue;
-      const float f = exp2_fast(ms - M);
-      l += p.ws_ml[row * 2 + 1] * f;
-      const f32x4 x = *(const f32x4*)(p.ws_o + row * D + d);
-      o += x * f;
+  const int L = p.cache_len[b];
+  const int ns = split_range(p, L).ns;
+  const int t = m / G, h = g * G + m % G;
+  const long base = ((long)b * p.Hkv + g) * p.nsplit * p.r_pad + m;
+  const float sink2 = p.sinks ? p.sinks[h] * kLog2e : kNegInf;
+  float M = kNegInf, l = 0.0f;
+  f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < ns; s0 += kCombineBatch) {
+    float ms[kCombineBatch], ls[kCombineBatch];
+    f32x4 xs[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const long row = base + (long)min(s0 + i, ns - 1) * p.r_pad;
+      const float2 ml = *(const float2*)(p.ws_ml + row * 2);
+      ms[i] = s0 + i < ns ? ml.x : kNegInf;
+      ls[i] = ml.y;
+      xs[i] = *(const f32x4*)(p.ws_o + row * D + d);
     }
-    o *= 1.0f / l;
-    uint16_t* op = p.o + (((long)b * p.T + t) * p.Hq + h) * D + d;
-    *(bf16x4*)op = __builtin_convertvector(o, bf16x4);
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) Mb = fmaxf(Mb, ms[i]);
+    if (Mb == kNegInf) continue;
+    const float fo = M == kNegInf ? 0.0f : exp2_fast(M - Mb);
+    l *= fo;
+    o *= fo;
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const float f = ms[i] == kNegInf ? 0.0f : exp2_fast(ms[i] - Mb);
+      l += ls[i] * f;
+      o += xs[i] * f;
+    }
+    M = Mb;
   }
+  if (sink2 != kNegInf) {
+    const float Mt = fmaxf(M, sink2);
+    const float fo = M == kNegInf ? 0.0f : exp2_fast(M - Mt);
+    l = l * fo + exp2_fast(sink2 - Mt);
+    o *= fo;
+  }
+  o *= 1.0f / l;
+  uint16_t* op = p.o + (((long)b * p.T + t) * p.Hq + h) * D + d;
+  *(bf16x4*)op = __builtin_convertvector(o, bf16x4);
 }
 
 VerifyPlan plan_verify_bf16(int B, int T, int Hq, int Hkv, int D, int slots, int ring, int window) {
@@ -479,7 +510,9 @@ static hipError_t launch_verify_t(VerifyArgs a, const VerifyPlan& pl, hipStream_
   hipLaunchKernelGGL((verify_bf16_kernel<D, NB, NW, false>), grid, block, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_combine_kernel<D>), dim3(a.B * a.Hkv), dim3(256), 0, s, a);
+  constexpr int RPP = 256 / (D / 4);
+  const int R = (a.Hq / a.Hkv) * a.T;
+  hipLaunchKernelGGL((verify_combine_kernel<D>), dim3(a.B * a.Hkv, (R + RPP - 1) / RPP), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
