@@ -597,7 +597,11 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
       if (a.sinks) sterm += __expf(sink - r.lse) * del;
     }
   };
-  // dQ of one block from the ring, with the rows in r
+  // dQ of one block from the ring, with the rows in r.  Software pipelined:
+  // the S^T and dP^T MFMAs of tile kt + 1 are issued between the dS^T
+  // elements of tile kt (a pair of MFMAs, then that chunk's share of the
+  // exponentials), so the matrix core and the vector ALU of the SIMD work at
+  // the same time; then the dQ^T MFMAs of tile kt.
   auto block = [&](const DqRows<D>& r, int blk, float del, float lse2) {
     const int tw0 = blk * TB + wv * TQ;
     const int tok = tw0 + col / G;
@@ -605,37 +609,79 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
     if (tw0 >= a.Sq) return;
     const int wpos_lo = a.q_offset + tw0, wpos_hi = a.q_offset + min(tw0 + TQ, a.Sq) - 1;
     const int wk0 = max(0, wpos_lo - W + 1) / BKT, wk1 = wpos_hi / BKT;
+    constexpr int EPC = 16 / Gm::NC;  // dS elements per MFMA pair
     f32x16 dq[Gm::ND];
 #pragma unroll
     for (int db = 0; db < Gm::ND; ++db) dq[db] = f32x16{};
-    for (int kt = wk0; kt <= wk1; ++kt) {
-      const int kb = kt * BKT;
-      const uint16_t* kt_t = k_ring[kt % NR];
-      const uint16_t* vt_t = v_ring[kt % NR];
-      const lds_u16* ka = lane_base(lds_addr(kt_t), KT_::k_lane_off(lane));
-      const lds_u16* va = lane_base(lds_addr(vt_t), VT_::k_lane_off(lane));
-      f32x16 s = {}, dp = {};
+    auto edge_of = [&](int kb) { return !(kb + BKT - 1 <= wpos_lo && kb > wpos_hi - W); };
+    // dS of elements v, v + 1 of tile kb, packed to bf16
+    auto ds_pair = [&](const f32x16& s, const f32x16& dp, int v, bool edge, int kb) {
+      float p0 = exp2_fast(fmaf(s[v], c2, -lse2));
+      float p1 = exp2_fast(fmaf(s[v + 1], c2, -lse2));
+      if (edge) {
+        if (!visible(qpos, kb + c_row(v, half), W)) p0 = 0.0f;
+        if (!visible(qpos, kb + c_row(v + 1, half), W)) p1 = 0.0f;
+      }
+      const bf16x2 w2 = {(__bf16)(p0 * (dp[v] - del)), (__bf16)(p1 * (dp[v + 1] - del))};
+      return __builtin_bit_cast(uint32_t, w2);
+    };
+    auto dq_acc = [&](int kt, const uint32_t (&pw)[8]) {
+      bf16x8 sb[2];
+      sb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      sb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+      const lds_u16* kt_op = lane_base(lds_addr(k_ring[kt % NR]), KT_::vt_lane_off(lane));
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < Gm::ND; ++db) dq[db] = mfma32(KT_::vt_operand(kt_op, db, kc), sb[kc], dq[db]);
+    };
+    f32x16 s = {}, dp = {};
+    {
+      const lds_u16* ka = lane_base(lds_addr(k_ring[wk0 % NR]), KT_::k_lane_off(lane));
+      const lds_u16* va = lane_base(lds_addr(v_ring[wk0 % NR]), VT_::k_lane_off(lane));
 #pragma unroll
       for (int c = 0; c < Gm::NC; ++c) {
         s = mfma32(KT_::k_operand(ka, c), r.q[c], s);
         dp = mfma32(VT_::k_operand(va, c), r.o[c], dp);
       }
-      const bool edge = !(kb + BKT - 1 <= wpos_lo && kb > wpos_hi - W);
-      bf16x8 sb[2];
+    }
+    for (int kt = wk0; kt < wk1; ++kt) {
+      const int kb = kt * BKT;
+      const bool edge = edge_of(kb);
+      const lds_u16* ka = lane_base(lds_addr(k_ring[(kt + 1) % NR]), KT_::k_lane_off(lane));
+      const lds_u16* va = lane_base(lds_addr(v_ring[(kt + 1) % NR]), VT_::k_lane_off(lane));
+      bf16x8 kop[Gm::NC], vop[Gm::NC];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float p = exp2_fast(fmaf(s[v], c2, -lse2));
-        if (edge) {
-          const int j = kb + c_row(v, half);
-          if (!visible(qpos, j, W)) p = 0.0f;
-        }
-        sb[v >> 3][v & 7] = (__bf16)(p * (dp[v] - del));
+      for (int c = 0; c < Gm::NC; ++c) {
+        kop[c] = KT_::k_operand(ka, c);
+        vop[c] = VT_::k_operand(va, c);
       }
-      const lds_u16* kt_op = lane_base(lds_addr(kt_t), KT_::vt_lane_off(lane));
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 sn = {}, dpn = {};
+      uint32_t pw[8];
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
+      for (int c = 0; c < Gm::NC; ++c) {
+        sn = mfma32(kop[c], r.q[c], sn);
+        dpn = mfma32(vop[c], r.o[c], dpn);
 #pragma unroll
-        for (int db = 0; db < Gm::ND; ++db) dq[db] = mfma32(KT_::vt_operand(kt_op, db, kc), sb[kc], dq[db]);
+        for (int e = 0; e < EPC; e += 2) {
+          uint32_t w = ds_pair(s, dp, c * EPC + e, edge, kb);
+          __asm__ volatile("" : "+v"(w));
+          pw[(c * EPC + e) >> 1] = w;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dq_acc(kt, pw);
+      s = sn;
+      dp = dpn;
+    }
+    {
+      const int kb = wk1 * BKT;
+      const bool edge = edge_of(kb);
+      uint32_t pw[8];
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) pw[v >> 1] = ds_pair(s, dp, v, edge, kb);
+      dq_acc(wk1, pw);
     }
     if (tok < a.Sq) {
       uint16_t* dqp = a.dq + ((long)b * a.Sq + tok) * q_tok + (long)h * D;
