@@ -508,6 +508,15 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k_ring[NR][KT_::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t v_ring[NR][VT_::ELEMS];
   __shared__ float sink_red[NW][32];
+  constexpr int HD = D / 2;           // staging width: half a head
+  constexpr int HC = HD / 8;          // 16-byte chunks per staged row
+  constexpr int SIT = 32 * HC / 64;   // chunks per lane per staged half
+  constexpr int RPI = 64 / HC;        // rows per load instruction
+  static_assert(RPI % G == 0, "a load instruction must cover whole tokens");
+  static_assert(SIT == Gm::NC / 2, "one register per chunk in both layouts");
+  constexpr int TPI = RPI / G;        // tokens per load instruction
+  using Stg = PadTile<HD, HD + 8>;
+  __shared__ __attribute__((aligned(16))) uint16_t stage_lds[NW][Stg::ELEMS];
 
   const int n_tb = (a.Sq + TB - 1) / TB;
   const int spb = a.strips_per_bg;
@@ -527,27 +536,57 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
   auto kt_lo = [&](int blk) { return max(0, a.q_offset + blk * TB - W + 1) / BKT; };
   auto kt_hi = [&](int blk) { return (a.q_offset + min(blk * TB + TB, a.Sq) - 1) / BKT; };
 
-  // this lane's query row of block blk: token blk*TB + wv*TQ + col/G, head h.
-  // Plain buffer loads only (no branch, no arithmetic on the results), so the
-  // compiler can leave them in flight across the block that is computed
-  // meanwhile; rows at or past Sq read as zeros, which makes their dS zero.
-  const uint32_t row_voff = (uint32_t)((((wv * TQ + col / G) * q_tok) + (long)h * D + half * 8) * 2);
+  // A wave's q, dO and O rows of block blk (tokens blk*TB + wv*TQ ..., heads
+  // g*G ...: TQ runs of G*D contiguous elements) are loaded as whole rows,
+  // half a head at a time: load instruction it of half hh covers RPI rows
+  // (TPI tokens), lane l taking row l / HC, 16-byte chunk l % HC, so every
+  // instruction reads whole 128-byte lines.  The raw chunks sit in the
+  // DqRows registers (chunk it of half hh in slot hh*SIT + it) until
+  // to_operand() turns them, through a per-wave LDS tile, into the MFMA
+  // B-operand layout (row col, d = 16c + 8*half).  Plain buffer loads only
+  // (no branch, no arithmetic on the results), so the compiler can leave
+  // them in flight across the block that is computed meanwhile; rows at or
+  // past Sq read as zeros, which makes their dS zero.
+  const uint32_t wrow_voff =
+      (uint32_t)((((lane / HC) / G) * q_tok + ((lane / HC) % G) * D + (lane % HC) * 8) * 2);
   const uint32_t lse_voff = (uint32_t)(((wv * TQ + col / G) * a.Hq + h) * 4);
   auto load_rows = [&](DqRows<D>& r, int blk) {
-    const int t0 = blk * TB;
-    const int ntok = min(TB, a.Sq - t0);
-    const long base = ((long)b * a.Sq + t0) * q_tok;
-    const uint32_t bytes = (uint32_t)(((ntok - 1) * q_tok + (long)a.Hq * D) * 2);
+    const int tw0 = blk * TB + wv * TQ;
+    const int ntok = min(TQ, a.Sq - tw0);
+    const long base = ((long)b * a.Sq + tw0) * q_tok + (long)g * G * D;
+    const uint32_t bytes = ntok > 0 ? (uint32_t)(((ntok - 1) * q_tok + (long)G * D) * 2) : 0u;
     const rsrc_t rq = make_rsrc(a.q + base, bytes), ro = make_rsrc(a.dout + base, bytes);
     const rsrc_t rv = make_rsrc(a.o + base, bytes);
 #pragma unroll
-    for (int c = 0; c < Gm::NC; ++c) {
-      r.q[c] = __builtin_bit_cast(bf16x8, buf_load16<kDqRowPolicy>(rq, row_voff + c * 32, 0));
-      r.o[c] = __builtin_bit_cast(bf16x8, buf_load16<kDqRowPolicy>(ro, row_voff + c * 32, 0));
-      r.ov[c] = __builtin_bit_cast(bf16x8, buf_load16<kDqRowPolicy>(rv, row_voff + c * 32, 0));
-    }
-    const rsrc_t rl = make_rsrc(a.lse + ((long)b * a.Sq + t0) * a.Hq, (uint32_t)(ntok * a.Hq * 4));
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int it = 0; it < SIT; ++it) {
+        const uint32_t off = wrow_voff + (uint32_t)((it * TPI * q_tok + hh * HD) * 2);
+        r.q[hh * SIT + it] = __builtin_bit_cast(bf16x8, buf_load16<kDqRowPolicy>(rq, off, 0));
+        r.o[hh * SIT + it] = __builtin_bit_cast(bf16x8, buf_load16<kDqRowPolicy>(ro, off, 0));
+        r.ov[hh * SIT + it] = __builtin_bit_cast(bf16x8, buf_load16<kDqRowPolicy>(rv, off, 0));
+      }
+    const int t0 = blk * TB;
+    const int ntok_b = min(TB, a.Sq - t0);
+    const rsrc_t rl = make_rsrc(a.lse + ((long)b * a.Sq + t0) * a.Hq, (uint32_t)(ntok_b * a.Hq * 4));
     r.lse = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (int)lse_voff, 0, 0));
+  };
+  // whole-row chunks -> LDS -> B-operand layout, in place, half a head at a time
+  auto to_operand = [&](bf16x8 (&x)[D / 16]) {
+    uint16_t* stg = stage_lds[wv];
+    const lds_u16* sbase = lane_base(lds_addr(stg), Stg::k_lane_off(lane));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int it = 0; it < SIT; ++it) {
+        const int u = it * 64 + lane;
+        *(u32x4*)&stg[Stg::off(u / HC, (u % HC) * 8)] = __builtin_bit_cast(u32x4, x[hh * SIT + it]);
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int c = 0; c < Gm::NC / 2; ++c) x[hh * (Gm::NC / 2) + c] = Stg::k_operand(sbase, c);
+      wave_lds_sync();
+    }
   };
 
   // K/V tile staging through registers (two 16-byte chunks per thread and
@@ -588,7 +627,10 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
   // Per-row scalars of a block's rows, computed when they are first needed,
   // at the end of the step that loaded them: D = <dO, O> (also written for
   // dK/dV), LSE * log2(e), and the row's sink-gradient term.
-  auto prep = [&](const DqRows<D>& r, int blk, float& del, float& lse2) {
+  auto prep = [&](DqRows<D>& r, int blk, float& del, float& lse2) {
+    to_operand(r.q);
+    to_operand(r.o);
+    to_operand(r.ov);
     const int tok = blk * TB + wv * TQ + col / G;
     del = halves_sum(dot_bf16(r.o, r.ov));
     lse2 = r.lse * kLog2e;
