@@ -735,7 +735,16 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
       };
       f32x16 s = st.scores(k_ring[wk0 % NR], lane);
       st.prep(s, wk0 * KT, tile_mask(wk0), W, p.scale_log2, half);
-      for (int kt = wk0; kt < wk1; ++kt)
+      // two folds per trip: the scores alternate between two register
+      // sets, so none is copied back to close the loop
+      int kt = wk0;
+      for (; kt + 1 < wk1; kt += 2) {
+        const f32x16 s1 = st.template fold<true>(s, p.scale_log2, v_ring[kt % NR], k_ring[(kt + 1) % NR],
+                                                 (kt + 1) * KT, tile_mask(kt + 1), W, half, lane);
+        s = st.template fold<true>(s1, p.scale_log2, v_ring[(kt + 1) % NR], k_ring[(kt + 2) % NR], (kt + 2) * KT,
+                                   tile_mask(kt + 2), W, half, lane);
+      }
+      if (kt < wk1)
         s = st.template fold<true>(s, p.scale_log2, v_ring[kt % NR], k_ring[(kt + 1) % NR], (kt + 1) * KT,
                                    tile_mask(kt + 1), W, half, lane);
       st.template fold<false>(s, p.scale_log2, v_ring[wk1 % NR], nullptr, 0, 0, W, half, lane);
