@@ -13,23 +13,28 @@
 // (the sink adds exp(sink) to the denominator and carries no value).
 //
 // Kernels
-//   * bwd_dq (first): besides dQ, D_i = <dO_i, O_i> for its rows (written for
-//     bwd_dkdv) and, per workgroup and head, the partial sum of
-//     exp(sink - LSE) D in a fixed order; bwd_sink_reduce adds the partials
-//     in a fixed order, so dsink is deterministic.
+//   * dQ, launched first.  Besides dQ it writes D_i = <dO_i, O_i> for its
+//     rows (read by the dK/dV kernel) and, per workgroup or strip and head,
+//     the partial sum of exp(sink - LSE) D in a fixed order;
+//     bwd_sink_reduce adds the partials in a fixed order, so dsink is
+//     deterministic.  Q-parallel: a wave owns 32 query rows (32/G tokens x
+//     the G heads of a KV head) with q and dO as MFMA B operands;
+//     S^T = K Q^T and dP^T = V dO^T give a lane one query's column, dS^T is
+//     the B operand of dQ^T += K^T dS^T with K^T read transposed from the K
+//     tile.  Sliding windows with G in {4, 8} use bwd_dq_strip (persistent
+//     strips of 16-token blocks, the window's K/V tiles in an LDS ring, rows
+//     loaded whole and turned into operands through LDS, the tile loop
+//     software-pipelined); other shapes use bwd_dq (one workgroup per block,
+//     the forward's structure).
 //   * bwd_dkdv: KV-parallel.  A wave owns 32 keys of one KV head and keeps
-//     their K and V rows as MFMA B operands in registers; the workgroup's four
-//     waves walk the query blocks (32 rows = 32/G tokens x the G heads of the
-//     KV head) that see any of their keys, staged through a double-buffered
-//     LDS tile.  Scores are computed as S = Q K^T, so a lane holds one key's
-//     column and 16 query rows: P and dS are then already the B operands of
-//     dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read transposed
-//     from the row-major LDS tiles by ds_read_b64_tr_b16 (the forward's V^T
-//     trick, with the query as the contraction index).
-//   * bwd_dq: Q-parallel, the forward's structure, launched first.  A wave owns 32 query rows
-//     with q and dO in registers; S^T = K Q^T and dP^T = V dO^T give a lane
-//     one query's column, dS^T is the B operand of dQ^T += K^T dS^T with K^T
-//     read transposed from the K tile.
+//     their K and V rows as MFMA B operands in registers; the workgroup's
+//     waves walk the query blocks that see any of their keys, staged through
+//     a double-buffered LDS tile.  Scores are computed as S = Q K^T, so a
+//     lane holds one key's column and 16 query rows: P and dS are then
+//     already the B operands of dV^T += dO^T P and dK^T += Q^T dS, with dO^T
+//     and Q^T read transposed from the row-major LDS tiles by
+//     ds_read_b64_tr_b16 (the forward's V^T trick, with the query as the
+//     contraction index).
 // P and dS are rounded to bf16 for the MFMAs, as the forward rounds P; every
 // accumulation is fp32; dQ, dK, dV are rounded to bf16 (nearest even).
 #include "common.hpp"
