@@ -730,16 +730,33 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
       for (int v = 0; v < 16; v += 2) pw[v >> 1] = ds_pair(s, dp, v, edge, kb);
       dq_acc(wk1, pw);
     }
-    if (tok < a.Sq) {
-      uint16_t* dqp = a.dq + ((long)b * a.Sq + tok) * q_tok + (long)h * D;
+    // dQ = scale * dQ^T: MFMA layout -> the wave's LDS tile -> whole rows,
+    // half a head at a time (full 128-byte lines per store; rows past Sq
+    // fall outside the buffer range and are dropped)
+    const int ntok = min(TQ, a.Sq - tw0);
+    const rsrc_t rd = make_rsrc(a.dq + ((long)b * a.Sq + tw0) * q_tok + (long)g * G * D,
+                                (uint32_t)(((ntok - 1) * q_tok + (long)G * D) * 2));
+    uint16_t* stg = stage_lds[wv];
 #pragma unroll
-      for (int db = 0; db < Gm::ND; ++db)
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int db2 = 0; db2 < Gm::ND / 2; ++db2) {
+        const int db = hh * (Gm::ND / 2) + db2;
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const f32x4 y = {dq[db][4 * a4] * a.scale, dq[db][4 * a4 + 1] * a.scale, dq[db][4 * a4 + 2] * a.scale,
                            dq[db][4 * a4 + 3] * a.scale};
-          store_pol<kBwdOutNT>(__builtin_convertvector(y, bf16x4), (bf16x4*)(dqp + db * 32 + 8 * a4 + 4 * half));
+          *(bf16x4*)&stg[Stg::off(col, 32 * db2 + 8 * a4 + 4 * half)] = __builtin_convertvector(y, bf16x4);
         }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int it = 0; it < SIT; ++it) {
+        const int u = it * 64 + lane;
+        buf_store16(*(const u32x4*)&stg[Stg::off(u / HC, (u % HC) * 8)], rd,
+                    wrow_voff + (uint32_t)((it * TPI * q_tok + hh * HD) * 2), 0);
+      }
+      wave_lds_sync();
     }
   };
 
