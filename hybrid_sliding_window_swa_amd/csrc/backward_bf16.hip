@@ -274,13 +274,26 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
     }
     const lds_u16* qt = lane_base(lds_addr(q_lds[buf]), vo);
     const lds_u16* ot = lane_base(lds_addr(o_lds[buf]), vo);
+    // the transposed operands are read two MFMA pairs ahead of their use,
+    // so each pair waits for reads issued long before, not for its own
+    constexpr int NM = 2 * Gm::ND;
+    bf16x8 otop[3], qtop[3];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
+    for (int i = 0; i < 2 && i < NM; ++i) {
+      otop[i] = Tile::vt_operand(ot, i % Gm::ND, i / Gm::ND);
+      qtop[i] = Tile::vt_operand(qt, i % Gm::ND, i / Gm::ND);
+    }
 #pragma unroll
-      for (int db = 0; db < Gm::ND; ++db) {
-        dv[db] = mfma32(Tile::vt_operand(ot, db, kc), pb[kc], dv[db]);
-        dk[db] = mfma32(Tile::vt_operand(qt, db, kc), sb[kc], dk[db]);
+    for (int i = 0; i < NM; ++i) {
+      if (i + 2 < NM) {
+        otop[(i + 2) % 3] = Tile::vt_operand(ot, (i + 2) % Gm::ND, (i + 2) / Gm::ND);
+        qtop[(i + 2) % 3] = Tile::vt_operand(qt, (i + 2) % Gm::ND, (i + 2) / Gm::ND);
       }
+      const int db = i % Gm::ND, kc = i / Gm::ND;
+      dv[db] = mfma32(otop[i % 3], pb[kc], dv[db]);
+      dk[db] = mfma32(qtop[i % 3], sb[kc], dk[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   const int nblk = qb_hi - qb_lo + 1;
