@@ -699,10 +699,22 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
     {
       const lds_u16* ka = lane_base(lds_addr(k_ring[wk0 % NR]), KT_::k_lane_off(lane));
       const lds_u16* va = lane_base(lds_addr(v_ring[wk0 % NR]), VT_::k_lane_off(lane));
+      // operand reads run two chunks ahead of their MFMAs
+      bf16x8 krd[3], vrd[3];
+#pragma unroll
+      for (int c = 0; c < 2 && c < Gm::NC; ++c) {
+        krd[c] = KT_::k_operand(ka, c);
+        vrd[c] = VT_::k_operand(va, c);
+      }
 #pragma unroll
       for (int c = 0; c < Gm::NC; ++c) {
-        s = mfma32(KT_::k_operand(ka, c), r.q[c], s);
-        dp = mfma32(VT_::k_operand(va, c), r.o[c], dp);
+        if (c + 2 < Gm::NC) {
+          krd[(c + 2) % 3] = KT_::k_operand(ka, c + 2);
+          vrd[(c + 2) % 3] = VT_::k_operand(va, c + 2);
+        }
+        s = mfma32(krd[c % 3], r.q[c], s);
+        dp = mfma32(vrd[c % 3], r.o[c], dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     for (int kt = wk0; kt < wk1; ++kt) {
