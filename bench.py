@@ -642,7 +642,20 @@ def cpu_baseline(cfg, q, k, v, sinks, target_s):
         "sample": f"{n} of {cfg.S} query rows x {cfg.Hq} heads of the swa_32k prefill "
                   f"(fp64 C oracle, OpenMP), {dt:.1f} s",
         "seconds": round(dt, 2),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
