@@ -642,6 +642,7 @@ def cpu_baseline(cfg, q, k, v, sinks, target_s):
         "sample": f"{n} of {cfg.S} query rows x {cfg.Hq} heads of the swa_32k prefill "
                   f"(fp64 C oracle, OpenMP), {dt:.1f} s",
         "seconds": round(dt, 2),
+        "rows_per_s": round(n * cfg.Hq / dt, 1),
         "cpu_model": cpu_model(),
     }
 
