@@ -69,6 +69,8 @@ template <int D, int NT, int POL = kCacheDefault>
 struct Stager {
   using Gm = TileGeom<D>;
   static constexpr int IT = (Gm::KCH + NT - 1) / NT;
+  // every thread owns IT chunks (no lane predicate, no exec-mask branch)
+  static constexpr bool kWhole = IT * NT == Gm::KCH;
   u32x4 kpre[IT];
   u32x4 vpre[IT];
   uint32_t voff[IT];  // byte offset of this thread's 16-byte chunks in a tile
@@ -84,17 +86,28 @@ struct Stager {
     const int rows = min(KT, Sk - kb);
     return make_rsrc(g + (long)kb * kv_tok, (uint32_t)(((rows - 1) * kv_tok + D) * 2));
   }
-  __device__ __forceinline__ void load_k(const uint16_t* kg, long kv_tok, int kb, int Sk, int tid) {
-    const rsrc_t r = tile(kg, kv_tok, kb, Sk);
+  // The same range from a first-row pointer the caller advances itself:
+  // rows * row_bytes - pad_bytes = ((rows - 1) * kv_tok + D) * 2 with
+  // row_bytes = 2 kv_tok and pad_bytes = 2 (kv_tok - D), no 64-bit multiply.
+  static __device__ __forceinline__ rsrc_t tile_at(const uint16_t* first_row, int kb, int Sk, uint32_t row_bytes,
+                                                   uint32_t pad_bytes) {
+    return make_rsrc(first_row, (uint32_t)min(KT, Sk - kb) * row_bytes - pad_bytes);
+  }
+  __device__ __forceinline__ void load_k(rsrc_t r, int tid) {
 #pragma unroll
     for (int i = 0; i < IT; ++i)
-      if (tid + i * NT < Gm::KCH) kpre[i] = buf_load16<POL>(r, voff[i], 0);
+      if (kWhole || tid + i * NT < Gm::KCH) kpre[i] = buf_load16<POL>(r, voff[i], 0);
+  }
+  __device__ __forceinline__ void load_v(rsrc_t r, int tid) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+      if (kWhole || tid + i * NT < Gm::KCH) vpre[i] = buf_load16<POL>(r, voff[i], 0);
+  }
+  __device__ __forceinline__ void load_k(const uint16_t* kg, long kv_tok, int kb, int Sk, int tid) {
+    load_k(tile(kg, kv_tok, kb, Sk), tid);
   }
   __device__ __forceinline__ void load_v(const uint16_t* vg, long kv_tok, int kb, int Sk, int tid) {
-    const rsrc_t r = tile(vg, kv_tok, kb, Sk);
-#pragma unroll
-    for (int i = 0; i < IT; ++i)
-      if (tid + i * NT < Gm::KCH) vpre[i] = buf_load16<POL>(r, voff[i], 0);
+    load_v(tile(vg, kv_tok, kb, Sk), tid);
   }
   __device__ __forceinline__ void load(const uint16_t* kg, const uint16_t* vg, long kv_tok, int kb,
                                        int Sk, int tid) {
@@ -107,20 +120,24 @@ struct Stager {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int c = tid + i * NT;
-      if (c < Gm::KCH) *(u32x4*)&k_dst[KTile<D>::off(c / (D / 8), (c % (D / 8)) * 8)] = kpre[i];
+      if (kWhole || c < Gm::KCH) *(u32x4*)&k_dst[KTile<D>::off(c / (D / 8), (c % (D / 8)) * 8)] = kpre[i];
     }
   }
   __device__ __forceinline__ void store_v(uint16_t* v_dst, int tid) const {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int c = tid + i * NT;
-      if (c < Gm::KCH) *(u32x4*)&v_dst[VTile<D>::off(c / (D / 8), (c % (D / 8)) * 8)] = vpre[i];
+      if (kWhole || c < Gm::KCH) *(u32x4*)&v_dst[VTile<D>::off(c / (D / 8), (c % (D / 8)) * 8)] = vpre[i];
     }
   }
   __device__ __forceinline__ void store(uint16_t* k_dst, uint16_t* v_dst, int tid) const {
     store_k(k_dst, tid);
     store_v(v_dst, tid);
   }
+};
+
+struct NoExtra {
+  __device__ __forceinline__ void operator()(int) const {}
 };
 
 // Per-lane state of one 32-query block; row m of the block is (token m / G,
@@ -230,10 +247,12 @@ struct QState {
   // each P V MFMA by a share of the row sums and of the next row max
   // (scheduling fences keep that order), so the matrix core and the vector
   // ALU of the SIMD work at the same time.
-  template <bool NEXT>
+  // `extra(c)` runs right after score MFMA c (work that then issues while
+  // the matrix core is busy, e.g. the next tiles' global loads).
+  template <bool NEXT, typename X = NoExtra>
   __device__ __forceinline__ f32x16 fold(const f32x16& s, float c2, const uint16_t* v_t,
                                          const uint16_t* k_next, int kb_next, int mask_next,
-                                         int window, int half, int lane) {
+                                         int window, int half, int lane, const X& extra = X()) {
     constexpr int EPM = 16 / Gm::NC;  // exponentials per score MFMA
     const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
     f32x16 sn = {};
@@ -261,6 +280,7 @@ struct QState {
           __asm__ volatile("" : "+v"(w));
           pw[v >> 1] = w;
         }
+        extra(c);
         __builtin_amdgcn_sched_barrier(0);
       }
       pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
@@ -352,7 +372,7 @@ __device__ __forceinline__ bool tile_needed(int kb, int wpos_lo, int wpos_hi, in
 // One workgroup per block of TB tokens (global attention and general shapes).
 // K tiles are staged one tile ahead of V tiles, so while a wave
 // exponentiates tile kt it already computes the scores of tile kt + 1.
-template <int D, int G, int NW>
+template <int D, int G, int NW, bool NOWIN>
 __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   using Gm = TileGeom<D>;
   constexpr int NT = NW * 64;
@@ -382,12 +402,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   const uint16_t* kg = p.k + ((long)b * p.Sk * p.Hkv + g) * D;
   const uint16_t* vg = p.v + ((long)b * p.Sk * p.Hkv + g) * D;
   const long qoff = (long)b * p.Sq * q_tok;
-  const int W = p.window;
+  const int W = NOWIN ? 0 : p.window;  // NOWIN is launched only for window 0
   const float c2 = p.scale_log2;
 
   QState<D> st;
   st.load_q(p.q + qoff, q_tok, tw0, G, g, p.Sq, p.q_offset, col, half);
-  st.reset(p.sinks ? p.sinks[g * G + col % G] * kLog2e : kNegInf, half);
 
   const int tlast = min(t0 + TB, p.Sq) - 1;
   const int pos_lo = p.q_offset + t0, pos_hi = p.q_offset + tlast;
@@ -404,77 +423,141 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   Stager<D, NT> s0, s1;
   s0.init(kv_tok, tid);
   s1.init(kv_tok, tid);
-#pragma unroll
-  for (int i = 0; i < 3; ++i)
-    if (kt_begin + i <= kt_end) {
-      s0.load_k(kg, kv_tok, (kt_begin + i) * KT, p.Sk, tid);
-      s0.store_k(k_lds[i], tid);
-    }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    if (kt_begin + i <= kt_end) {
-      s0.load_v(vg, kv_tok, (kt_begin + i) * KT, p.Sk, tid);
-      s0.store_v(v_lds[i], tid);
-    }
+  float sink;
+  {
+    // the first three K tiles and two V tiles: every load is issued before
+    // the first LDS store, so the block start waits for one memory round
+    // trip, not five
+    Stager<D, NT> s2;
+    s2.init(kv_tok, tid);
+    const bool t1 = kt_begin + 1 <= kt_end, t2 = kt_begin + 2 <= kt_end;
+    s0.load(kg, vg, kv_tok, kt_begin * KT, p.Sk, tid);
+    if (t1) s1.load(kg, vg, kv_tok, (kt_begin + 1) * KT, p.Sk, tid);
+    if (t2) s2.load_k(kg, kv_tok, (kt_begin + 2) * KT, p.Sk, tid);
+    sink = p.sinks ? p.sinks[g * G + col % G] : 0.0f;
+    s0.store(k_lds[0], v_lds[0], tid);
+    if (t1) s1.store(k_lds[1], v_lds[1], tid);
+    if (t2) s2.store_k(k_lds[2], tid);
+  }
+  st.reset(p.sinks ? sink * kLog2e : kNegInf, half);
   // Drain the prologue loads (queries, first tiles): inside the loop the only
   // loads in flight are then the prefetches, and no wait for the queries can
   // stall on them.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // One code path per tile: a wave inside its range folds tile kt and
-  // computes the scores of tile kt + 1 (discarded after its last tile); in
-  // the step before its first tile it folds a fully masked tile, which adds
-  // nothing, to get those scores.  The last tile of the workgroup is folded
-  // after the loop.
+  // Each fold of tile kt also computes the scores of tile kt + 1 (discarded
+  // after the last tile); the last tile of the workgroup is folded after the
+  // loop.  With a window, a wave folds only the tiles of its own range, and
+  // in the step before its first tile it folds a fully masked tile, which
+  // adds nothing, to get those scores.
   auto tile_mask = [&](int kt) {  // kMaskAll before this wave's first tile
     int mask;
     tile_needed(kt * KT, wpos_lo, wpos_hi, W, mask);
-    return kt < wk0 ? kMaskAll : mask;
+    return !NOWIN && kt < wk0 ? kMaskAll : mask;
   };
   f32x16 s = {};
-  if (wk0 == kt_begin && wk1 >= 0) {
+  int kt = kt_begin;
+  if constexpr (NOWIN) {
+    // No window: every wave's range starts at the workgroup's first tile, and
+    // a tile past a wave's last query is masked whole by the causal bound, so
+    // every wave folds every tile with no per-wave condition, two folds per
+    // loop trip: the scores alternate between two register sets and no copy
+    // closes the loop.
     s = st.scores(k_lds[0], lane);
     st.prep(s, kt_begin * KT, tile_mask(kt_begin), W, c2, half);
-  }
-  auto fold_step = [&](int kt) {
-    if (kt + 1 >= wk0 && kt <= wk1) {
-      const int r = kt - kt_begin;
-      if (kt + 1 == wk0) st.prep(s, kt * KT, kMaskAll, W, c2, half);
-      s = st.template fold<true>(s, c2, v_lds[r & 3], k_lds[(r + 1) & 3], (kt + 1) * KT, tile_mask(kt + 1), W,
-                                 half, lane);
+    if ((kt_end - kt_begin) & 1) {  // a single step first, so that pairs remain
+      if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, p.Sk, tid);
+      if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, p.Sk, tid);
+      s = st.template fold<true>(s, c2, v_lds[0], k_lds[1], (kt + 1) * KT, tile_mask(kt + 1), W, half, lane);
+      if (kt + 3 <= kt_end) s0.store_k(k_lds[3], tid);
+      if (kt + 2 <= kt_end) s0.store_v(v_lds[2], tid);
+      __syncthreads();
+      ++kt;
     }
-  };
-  int kt = kt_begin;
-  if ((kt_end - kt_begin) & 1) {  // a single step first, so that pairs remain
-    if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, p.Sk, tid);
-    if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, p.Sk, tid);
-    fold_step(kt);
-    if (kt + 3 <= kt_end) s0.store_k(k_lds[3], tid);
-    if (kt + 2 <= kt_end) s0.store_v(v_lds[2], tid);
-    __syncthreads();
-    ++kt;
-  }
-  // The second wave of each SIMD pair runs at a raised priority: otherwise
-  // the older wave wins every issue tie, finishes its tiles first and idles
-  // at the barrier while the younger one runs alone (measured: about 1%).
-  if (wv >= NW / 2) __builtin_amdgcn_s_setprio(1);
-  for (; kt < kt_end; kt += 2) {
-    const int r = kt - kt_begin;
-    if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, p.Sk, tid);
-    if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, p.Sk, tid);
-    if (kt + 4 <= kt_end) s1.load_k(kg, kv_tok, (kt + 4) * KT, p.Sk, tid);
-    if (kt + 3 <= kt_end) s1.load_v(vg, kv_tok, (kt + 3) * KT, p.Sk, tid);
-    fold_step(kt);
-    fold_step(kt + 1);
-    if (kt + 3 <= kt_end) s0.store_k(k_lds[(r + 3) & 3], tid);
-    if (kt + 2 <= kt_end) s0.store_v(v_lds[(r + 2) & 3], tid);
-    if (kt + 4 <= kt_end) s1.store_k(k_lds[r & 3], tid);
-    if (kt + 3 <= kt_end) s1.store_v(v_lds[(r + 3) & 3], tid);
-    __syncthreads();
-  }
-  if (kt_end >= wk0 && kt_end <= wk1)
+    if (wv >= NW / 2) __builtin_amdgcn_s_setprio(1);
+    // first rows of K tile kt + 3 and V tile kt + 2, advanced by two tiles a
+    // step (an add instead of a 64-bit multiply per tile)
+    const long tstride = (long)KT * kv_tok;
+    const uint32_t row_b = (uint32_t)(2 * kv_tok), pad_b = (uint32_t)(2 * (kv_tok - D));
+    const uint16_t* kp = kg + (kt + 3) * tstride;
+    const uint16_t* vp = vg + (kt + 2) * tstride;
+    for (; kt < kt_end; kt += 2, kp += 2 * tstride, vp += 2 * tstride) {
+      const int r = kt - kt_begin;
+      using Stg = Stager<D, NT>;
+      // this step's loads issue one per score MFMA of the first fold (MFMAs
+      // c0 .. c0 + 3 of the D / 16), while the matrix core is busy, instead
+      // of ahead of it
+      static_assert(Gm::NC >= 4, "four loads and four stores per fold");
+      constexpr int c0 = Gm::NC > 4 ? 1 : 0;
+      auto loads = [&](int c) {
+        if (c == c0 && kt + 3 <= kt_end) s0.load_k(Stg::tile_at(kp, (kt + 3) * KT, p.Sk, row_b, pad_b), tid);
+        if (c == c0 + 1 && kt + 2 <= kt_end)
+          s0.load_v(Stg::tile_at(vp, (kt + 2) * KT, p.Sk, row_b, pad_b), tid);
+        if (c == c0 + 2 && kt + 4 <= kt_end)
+          s1.load_k(Stg::tile_at(kp + tstride, (kt + 4) * KT, p.Sk, row_b, pad_b), tid);
+        if (c == c0 + 3 && kt + 3 <= kt_end)
+          s1.load_v(Stg::tile_at(vp + tstride, (kt + 3) * KT, p.Sk, row_b, pad_b), tid);
+      };
+      const f32x16 s_mid = st.template fold<true>(s, c2, v_lds[r & 3], k_lds[(r + 1) & 3], (kt + 1) * KT,
+                                                  tile_mask(kt + 1), W, half, lane, loads);
+      // and their LDS stores, one per score MFMA of the last four of the
+      // second fold: the slots they fill were last read in the previous step
+      constexpr int c1 = Gm::NC - 4;
+      auto stores = [&](int c) {
+        if (c == c1 && kt + 3 <= kt_end) s0.store_k(k_lds[(r + 3) & 3], tid);
+        if (c == c1 + 1 && kt + 2 <= kt_end) s0.store_v(v_lds[(r + 2) & 3], tid);
+        if (c == c1 + 2 && kt + 4 <= kt_end) s1.store_k(k_lds[r & 3], tid);
+        if (c == c1 + 3 && kt + 3 <= kt_end) s1.store_v(v_lds[(r + 3) & 3], tid);
+      };
+      s = st.template fold<true>(s_mid, c2, v_lds[(r + 1) & 3], k_lds[(r + 2) & 3], (kt + 2) * KT,
+                                 tile_mask(kt + 2), W, half, lane, stores);
+      __syncthreads();
+    }
     st.template fold<false>(s, c2, v_lds[(kt_end - kt_begin) & 3], nullptr, 0, 0, W, half, lane);
+  } else {
+    if (wk0 == kt_begin && wk1 >= 0) {
+      s = st.scores(k_lds[0], lane);
+      st.prep(s, kt_begin * KT, tile_mask(kt_begin), W, c2, half);
+    }
+    auto fold_step = [&](int kt) {
+      if (kt + 1 >= wk0 && kt <= wk1) {
+        const int r = kt - kt_begin;
+        if (kt + 1 == wk0) st.prep(s, kt * KT, kMaskAll, W, c2, half);
+        s = st.template fold<true>(s, c2, v_lds[r & 3], k_lds[(r + 1) & 3], (kt + 1) * KT, tile_mask(kt + 1), W,
+                                   half, lane);
+      }
+    };
+    if ((kt_end - kt_begin) & 1) {  // a single step first, so that pairs remain
+      if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, p.Sk, tid);
+      if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, p.Sk, tid);
+      fold_step(kt);
+      if (kt + 3 <= kt_end) s0.store_k(k_lds[3], tid);
+      if (kt + 2 <= kt_end) s0.store_v(v_lds[2], tid);
+      __syncthreads();
+      ++kt;
+    }
+    // The second wave of each SIMD pair runs at a raised priority: otherwise
+    // the older wave wins every issue tie, finishes its tiles first and idles
+    // at the barrier while the younger one runs alone (measured: about 1%).
+    if (wv >= NW / 2) __builtin_amdgcn_s_setprio(1);
+    for (; kt < kt_end; kt += 2) {
+      const int r = kt - kt_begin;
+      if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, p.Sk, tid);
+      if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, p.Sk, tid);
+      if (kt + 4 <= kt_end) s1.load_k(kg, kv_tok, (kt + 4) * KT, p.Sk, tid);
+      if (kt + 3 <= kt_end) s1.load_v(vg, kv_tok, (kt + 3) * KT, p.Sk, tid);
+      fold_step(kt);
+      fold_step(kt + 1);
+      if (kt + 3 <= kt_end) s0.store_k(k_lds[(r + 3) & 3], tid);
+      if (kt + 2 <= kt_end) s0.store_v(v_lds[(r + 2) & 3], tid);
+      if (kt + 4 <= kt_end) s1.store_k(k_lds[r & 3], tid);
+      if (kt + 3 <= kt_end) s1.store_v(v_lds[(r + 3) & 3], tid);
+      __syncthreads();
+    }
+    if (kt_end >= wk0 && kt_end <= wk1)
+      st.template fold<false>(s, c2, v_lds[(kt_end - kt_begin) & 3], nullptr, 0, 0, W, half, lane);
+  }
   if (wk1 >= 0) {
     st.store_o(p.o + qoff, q_tok, tw0, G, g, p.Sq, col, half);
     if (p.lse) st.store_lse(p.lse + (long)b * p.Sq * p.Hq, p.Hq, tw0, G, g, p.Sq, col, half);
@@ -778,7 +861,10 @@ static hipError_t launch_generic(const PrefillArgs& a0, hipStream_t stream) {
   a.total = a.B * a.Hkv * a.n_tb;
   a.per_xcd = (a.total + 7) / 8;
   dim3 grid(8 * a.per_xcd), block(NW * 64);
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW>), grid, block, 0, stream, a);
+  if (a.window == 0)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -65,6 +65,14 @@ BF16_CASES = [
     _cfg("d64_global", 1, 257, 8, 1, 64, 0, "bf16"),
     _cfg("prefix", 1, 190, 16, 2, 128, 128, "bf16", Sk=450),
     _cfg("prefix_global", 1, 61, 16, 2, 128, 0, "bf16", Sk=300),
+    # the no-window kernel at every group size (waves of one workgroup whose
+    # queries end in different key tiles fold the later tiles fully masked)
+    _cfg("global_g1", 1, 300, 4, 4, 128, 0, "bf16"),
+    _cfg("global_g2_d64", 1, 170, 8, 4, 64, 0, "bf16"),
+    _cfg("global_g4", 1, 300, 8, 2, 128, 0, "bf16"),
+    _cfg("global_g16", 1, 130, 32, 2, 128, 0, "bf16"),
+    _cfg("global_g32", 2, 70, 32, 1, 128, 0, "bf16"),
+    _cfg("prefix_global_g4", 1, 77, 8, 2, 128, 0, "bf16", Sk=301),
     _cfg("one_row", 1, 1, 8, 1, 128, 128, "bf16"),
     _cfg("one_row_offset", 1, 1, 8, 1, 128, 128, "bf16", Sk=1000),
     _cfg("short", 3, 17, 8, 1, 128, 4, "bf16"),
