@@ -248,11 +248,17 @@ struct QState {
   // (scheduling fences keep that order), so the matrix core and the vector
   // ALU of the SIMD work at the same time.
   // `extra(c)` runs right after score MFMA c (work that then issues while
-  // the matrix core is busy, e.g. the next tiles' global loads).
-  template <bool NEXT, typename X = NoExtra>
+  // the matrix core is busy, e.g. the next tiles' global loads).  With
+  // PRE_IN the first KPRE K operands of k_next were read ahead into kpre;
+  // with PRE_OUT this fold reads those of k_after (the tile the next fold
+  // scores) into kpre during its P V MFMAs, so the next fold's first score
+  // MFMAs do not wait for LDS.
+  static constexpr int KPRE = Gm::NC < 4 ? Gm::NC : 4;
+  template <bool NEXT, bool PRE_IN = false, bool PRE_OUT = false, typename X = NoExtra>
   __device__ __forceinline__ f32x16 fold(const f32x16& s, float c2, const uint16_t* v_t,
                                          const uint16_t* k_next, int kb_next, int mask_next,
-                                         int window, int half, int lane, const X& extra = X()) {
+                                         int window, int half, int lane, const X& extra = X(),
+                                         bf16x8* kpre = nullptr, const uint16_t* k_after = nullptr) {
     constexpr int EPM = 16 / Gm::NC;  // exponentials per score MFMA
     const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
     f32x16 sn = {};
@@ -262,7 +268,7 @@ struct QState {
       const lds_u16* kbase = lane_base(lds_addr(k_next), KTile<D>::k_lane_off(lane));
       bf16x8 ka[Gm::NC];
 #pragma unroll
-      for (int c = 0; c < Gm::NC; ++c) ka[c] = KTile<D>::k_operand(kbase, c);
+      for (int c = 0; c < Gm::NC; ++c) ka[c] = (PRE_IN && c < KPRE) ? kpre[c] : KTile<D>::k_operand(kbase, c);
 #pragma unroll
       for (int db = 0; db < Gm::ND; ++db) va[0][db] = VTile<D>::vt_operand(vbase, db, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -297,6 +303,13 @@ struct QState {
       for (int i = 0; i < NPV; ++i) {
         const int kc = i / Gm::ND, db = i % Gm::ND;
         acc[db] = mfma32(va[kc][db], pb[kc], acc[db]);
+        if constexpr (PRE_OUT) {
+          if (i == 1) {
+            const lds_u16* abase = lane_base(lds_addr(k_after), KTile<D>::k_lane_off(lane));
+#pragma unroll
+            for (int c = 0; c < KPRE; ++c) kpre[c] = KTile<D>::k_operand(abase, c);
+          }
+        }
 #pragma unroll
         for (int j = i * 8 / NPV; j < (i + 1) * 8 / NPV; ++j) {
           const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -380,8 +393,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   constexpr int TB = TW * NW;       // tokens per workgroup
   static_assert(32 % G == 0, "a 32-row block must hold whole tokens");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[4][Gm::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[4][Gm::V_ELEMS];
+  // K/V ring: 8 slots without a window (four tiles per barrier), else 4
+  constexpr int NS = NOWIN ? 8 : 4;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NS][Gm::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[NS][Gm::V_ELEMS];
 
   // XCD-aware work item: workgroups on one XCD (blockIdx % 8) take consecutive
   // token blocks of one (b, g), latest (longest) first.
@@ -425,19 +440,26 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   s1.init(kv_tok, tid);
   float sink;
   {
-    // the first three K tiles and two V tiles: every load is issued before
-    // the first LDS store, so the block start waits for one memory round
-    // trip, not five
-    Stager<D, NT> s2;
-    s2.init(kv_tok, tid);
-    const bool t1 = kt_begin + 1 <= kt_end, t2 = kt_begin + 2 <= kt_end;
-    s0.load(kg, vg, kv_tok, kt_begin * KT, p.Sk, tid);
-    if (t1) s1.load(kg, vg, kv_tok, (kt_begin + 1) * KT, p.Sk, tid);
-    if (t2) s2.load_k(kg, kv_tok, (kt_begin + 2) * KT, p.Sk, tid);
+    // the first PK K tiles and PV V tiles the loop expects resident: every
+    // load is issued before the first LDS store, so the block start waits
+    // for one memory round trip
+    constexpr int PK = NOWIN ? 5 : 3, PV = PK - 1;
+    Stager<D, NT> pro[PK];
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+      pro[i].init(kv_tok, tid);
+      if (kt_begin + i <= kt_end) {
+        pro[i].load_k(kg, kv_tok, (kt_begin + i) * KT, p.Sk, tid);
+        if (i < PV) pro[i].load_v(vg, kv_tok, (kt_begin + i) * KT, p.Sk, tid);
+      }
+    }
     sink = p.sinks ? p.sinks[g * G + col % G] : 0.0f;
-    s0.store(k_lds[0], v_lds[0], tid);
-    if (t1) s1.store(k_lds[1], v_lds[1], tid);
-    if (t2) s2.store_k(k_lds[2], tid);
+#pragma unroll
+    for (int i = 0; i < PK; ++i)
+      if (kt_begin + i <= kt_end) {
+        pro[i].store_k(k_lds[i], tid);
+        if (i < PV) pro[i].store_v(v_lds[i], tid);
+      }
   }
   st.reset(p.sinks ? sink * kLog2e : kNegInf, half);
   // Drain the prologue loads (queries, first tiles): inside the loop the only
@@ -461,60 +483,78 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   if constexpr (NOWIN) {
     // No window: every wave's range starts at the workgroup's first tile, and
     // a tile past a wave's last query is masked whole by the causal bound, so
-    // every wave folds every tile with no per-wave condition, two folds per
-    // loop trip: the scores alternate between two register sets and no copy
-    // closes the loop.
+    // every wave folds every tile with no per-wave condition.  Tile t sits in
+    // slot (t - kt_begin) % 8; a step over tiles kt .. kt + 3 reads K(kt + 1
+    // .. kt + 4) and V(kt .. kt + 3) and stages K(kt + 5 .. kt + 8) and V(kt
+    // + 4 .. kt + 7) into the other slots: one barrier per four tiles, and
+    // the scores alternate between two register sets (no copy closes the
+    // loop).
     s = st.scores(k_lds[0], lane);
     st.prep(s, kt_begin * KT, tile_mask(kt_begin), W, c2, half);
-    if ((kt_end - kt_begin) & 1) {  // a single step first, so that pairs remain
-      if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, p.Sk, tid);
-      if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, p.Sk, tid);
-      s = st.template fold<true>(s, c2, v_lds[0], k_lds[1], (kt + 1) * KT, tile_mask(kt + 1), W, half, lane);
-      if (kt + 3 <= kt_end) s0.store_k(k_lds[3], tid);
-      if (kt + 2 <= kt_end) s0.store_v(v_lds[2], tid);
+    // single steps first, so that a multiple of four tiles remains
+    for (const int kt_single = kt_begin + ((kt_end - kt_begin) & 3); kt < kt_single; ++kt) {
+      const int r = kt - kt_begin;
+      if (kt + 5 <= kt_end) s0.load_k(kg, kv_tok, (kt + 5) * KT, p.Sk, tid);
+      if (kt + 4 <= kt_end) s0.load_v(vg, kv_tok, (kt + 4) * KT, p.Sk, tid);
+      s = st.template fold<true>(s, c2, v_lds[r & 7], k_lds[(r + 1) & 7], (kt + 1) * KT, tile_mask(kt + 1), W, half,
+                                 lane);
+      if (kt + 5 <= kt_end) s0.store_k(k_lds[(r + 5) & 7], tid);
+      if (kt + 4 <= kt_end) s0.store_v(v_lds[(r + 4) & 7], tid);
       __syncthreads();
-      ++kt;
     }
     if (wv >= NW / 2) __builtin_amdgcn_s_setprio(1);
-    // first rows of K tile kt + 3 and V tile kt + 2, advanced by two tiles a
+    // first rows of K tile kt + 5 and V tile kt + 4, advanced by four tiles a
     // step (an add instead of a 64-bit multiply per tile)
     const long tstride = (long)KT * kv_tok;
     const uint32_t row_b = (uint32_t)(2 * kv_tok), pad_b = (uint32_t)(2 * (kv_tok - D));
-    const uint16_t* kp = kg + (kt + 3) * tstride;
-    const uint16_t* vp = vg + (kt + 2) * tstride;
-    for (; kt < kt_end; kt += 2, kp += 2 * tstride, vp += 2 * tstride) {
+    const uint16_t* kp = kg + (kt + 5) * tstride;
+    const uint16_t* vp = vg + (kt + 4) * tstride;
+    Stager<D, NT> s2, s3;
+    s2.init(kv_tok, tid);
+    s3.init(kv_tok, tid);
+    // the step's loads issue one per score MFMA of the first two folds
+    // (MFMAs c0 .. c0 + 3 of the D / 16), the LDS stores one per score MFMA
+    // of the last four of the last two folds: the matrix core is busy
+    // meanwhile, and the slots they fill were last read in the previous step
+    static_assert(Gm::NC >= 4, "four loads or stores per fold");
+    constexpr int c0 = Gm::NC > 4 ? 1 : 0, c1 = Gm::NC - 4;
+    using Stg = Stager<D, NT>;
+    for (; kt < kt_end; kt += 4, kp += 4 * tstride, vp += 4 * tstride) {
       const int r = kt - kt_begin;
-      using Stg = Stager<D, NT>;
-      // this step's loads issue one per score MFMA of the first fold (MFMAs
-      // c0 .. c0 + 3 of the D / 16), while the matrix core is busy, instead
-      // of ahead of it
-      static_assert(Gm::NC >= 4, "four loads and four stores per fold");
-      constexpr int c0 = Gm::NC > 4 ? 1 : 0;
-      auto loads = [&](int c) {
-        if (c == c0 && kt + 3 <= kt_end) s0.load_k(Stg::tile_at(kp, (kt + 3) * KT, p.Sk, row_b, pad_b), tid);
-        if (c == c0 + 1 && kt + 2 <= kt_end)
-          s0.load_v(Stg::tile_at(vp, (kt + 2) * KT, p.Sk, row_b, pad_b), tid);
-        if (c == c0 + 2 && kt + 4 <= kt_end)
-          s1.load_k(Stg::tile_at(kp + tstride, (kt + 4) * KT, p.Sk, row_b, pad_b), tid);
-        if (c == c0 + 3 && kt + 3 <= kt_end)
-          s1.load_v(Stg::tile_at(vp + tstride, (kt + 3) * KT, p.Sk, row_b, pad_b), tid);
+      auto load_pair = [&](Stg& a, Stg& b, int i, int c, int cb) {  // K(kt+5+i), V(kt+4+i) into a; i+1 into b
+        if (c == cb && kt + 5 + i <= kt_end)
+          a.load_k(Stg::tile_at(kp + i * tstride, (kt + 5 + i) * KT, p.Sk, row_b, pad_b), tid);
+        if (c == cb + 1 && kt + 4 + i <= kt_end)
+          a.load_v(Stg::tile_at(vp + i * tstride, (kt + 4 + i) * KT, p.Sk, row_b, pad_b), tid);
+        if (c == cb + 2 && kt + 6 + i <= kt_end)
+          b.load_k(Stg::tile_at(kp + (i + 1) * tstride, (kt + 6 + i) * KT, p.Sk, row_b, pad_b), tid);
+        if (c == cb + 3 && kt + 5 + i <= kt_end)
+          b.load_v(Stg::tile_at(vp + (i + 1) * tstride, (kt + 5 + i) * KT, p.Sk, row_b, pad_b), tid);
       };
-      const f32x16 s_mid = st.template fold<true>(s, c2, v_lds[r & 3], k_lds[(r + 1) & 3], (kt + 1) * KT,
-                                                  tile_mask(kt + 1), W, half, lane, loads);
-      // and their LDS stores, one per score MFMA of the last four of the
-      // second fold: the slots they fill were last read in the previous step
-      constexpr int c1 = Gm::NC - 4;
-      auto stores = [&](int c) {
-        if (c == c1 && kt + 3 <= kt_end) s0.store_k(k_lds[(r + 3) & 3], tid);
-        if (c == c1 + 1 && kt + 2 <= kt_end) s0.store_v(v_lds[(r + 2) & 3], tid);
-        if (c == c1 + 2 && kt + 4 <= kt_end) s1.store_k(k_lds[r & 3], tid);
-        if (c == c1 + 3 && kt + 3 <= kt_end) s1.store_v(v_lds[(r + 3) & 3], tid);
+      auto store_pair = [&](const Stg& a, const Stg& b, int i, int c, int cb) {
+        if (c == cb && kt + 5 + i <= kt_end) a.store_k(k_lds[(r + 5 + i) & 7], tid);
+        if (c == cb + 1 && kt + 4 + i <= kt_end) a.store_v(v_lds[(r + 4 + i) & 7], tid);
+        if (c == cb + 2 && kt + 6 + i <= kt_end) b.store_k(k_lds[(r + 6 + i) & 7], tid);
+        if (c == cb + 3 && kt + 5 + i <= kt_end) b.store_v(v_lds[(r + 5 + i) & 7], tid);
       };
-      s = st.template fold<true>(s_mid, c2, v_lds[(r + 1) & 3], k_lds[(r + 2) & 3], (kt + 2) * KT,
-                                 tile_mask(kt + 2), W, half, lane, stores);
+      // within the step each fold reads the first K operands of the next
+      // fold's tile ahead (all four tiles are resident since the barrier)
+      bf16x8 kpre[QState<D>::KPRE];
+      const f32x16 sa = st.template fold<true, false, true>(
+          s, c2, v_lds[r & 7], k_lds[(r + 1) & 7], (kt + 1) * KT, tile_mask(kt + 1), W, half, lane,
+          [&](int c) { load_pair(s0, s1, 0, c, c0); }, kpre, k_lds[(r + 2) & 7]);
+      const f32x16 sb = st.template fold<true, true, true>(
+          sa, c2, v_lds[(r + 1) & 7], k_lds[(r + 2) & 7], (kt + 2) * KT, tile_mask(kt + 2), W, half, lane,
+          [&](int c) { load_pair(s2, s3, 2, c, c0); }, kpre, k_lds[(r + 3) & 7]);
+      const f32x16 sc = st.template fold<true, true, true>(
+          sb, c2, v_lds[(r + 2) & 7], k_lds[(r + 3) & 7], (kt + 3) * KT, tile_mask(kt + 3), W, half, lane,
+          [&](int c) { store_pair(s0, s1, 0, c, c1); }, kpre, k_lds[(r + 4) & 7]);
+      s = st.template fold<true, true, false>(sc, c2, v_lds[(r + 3) & 7], k_lds[(r + 4) & 7], (kt + 4) * KT,
+                                              tile_mask(kt + 4), W, half, lane,
+                                              [&](int c) { store_pair(s2, s3, 2, c, c1); }, kpre);
       __syncthreads();
     }
-    st.template fold<false>(s, c2, v_lds[(kt_end - kt_begin) & 3], nullptr, 0, 0, W, half, lane);
+    st.template fold<false>(s, c2, v_lds[(kt_end - kt_begin) & 7], nullptr, 0, 0, W, half, lane);
   } else {
     if (wk0 == kt_begin && wk1 >= 0) {
       s = st.scores(k_lds[0], lane);
