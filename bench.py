@@ -15,7 +15,9 @@ same for a plain q_len=1 decode step on the same shapes.  Further sections
 MTP step (verify of 39 SWA and 9 global layers, greedy acceptance over a
 152064-token vocabulary, append, advance) against the q_len=1 decode step;
 the partial rotary embedding, standalone and fused into the SWA prefill;
-and the SWA 32K training forward (saved log-sum-exp) and backward.
+the SWA 32K training forward (saved log-sum-exp) and backward; and the 256K
+long-context block (chunked SWA prefill of 262144 tokens on 5 layers, then
+a B=1 global q_len=4 verify against the 262144-token cache).
 
 Prints ONE JSON line.  Inputs are seeded synthetic N(0,1) tensors rounded to
 bf16 (random numbers, no dataset).  --gpus above 1 is refused: this build
@@ -55,7 +57,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="time the SWA prefill only")
-    ap.add_argument("--only", choices=["prefill", "ga", "verify", "mtp", "rope", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "ga", "verify", "mtp", "rope", "backward", "stack"], default=None,
                     help="run one workload only (for profiler runs); prints its own JSON line")
     ap.add_argument("--settle-seconds", type=float, default=0.5,
                     help="untimed repetition of each step before its warmup, so the clocks are at "
@@ -283,6 +285,65 @@ def run_verify(args, swa, torch, dev, stream, names=("verify_ga_b64", "verify_sw
             "frac": ga["frac_of_hbm_peak"],
             "traffic": read_traffic("verify_bf16_ga_b64_hbm_counters.txt", VERIFY_KERNEL_SRC),
         },
+    }
+
+
+def run_stack_256k(args, swa, torch, dev, stream):
+    """The 256K long-context block: the chunked SWA prefill of a 262144-token
+    sequence (8 chunks of 32768 queries over the whole K/V) on each of 5
+    sliding-window layers, then the q_len=4 verify of one global layer
+    against the full 262144-token cache (B = 1, so the split-KV partitioning
+    is the only parallelism).  Every layer reuses the same synthetic tensors:
+    the work per layer is identical."""
+    from swa_inputs import PREFILL_CONFIGS, VERIFY_CONFIGS, prefill_inputs, verify_inputs
+    cfg = PREFILL_CONFIGS["swa_256k"]
+    q, k, v, sinks = prefill_inputs(cfg, device=dev)
+    o = torch.empty_like(q)
+    chunk = cfg.chunk
+
+    def swa_layer():
+        for c0 in range(0, cfg.S, chunk):
+            swa.swa_attn_prefill(q[:, c0:c0 + chunk], k, v, sinks, cfg.window, c0, cfg.scale,
+                                 out=o[:, c0:c0 + chunk])
+
+    vc = VERIFY_CONFIGS["verify_ga_256k"]
+    inp = verify_inputs(vc, device=dev)
+    cl = inp["cache_len"].to(torch.int32).to(dev)
+    need = swa.swa_attn_verify_workspace_bytes(vc.B, vc.T, vc.Hq, vc.Hkv, vc.D, vc.slots, vc.ring, vc.window)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ov = torch.empty_like(inp["q"])
+    row_b = vc.Hkv * vc.D * 2
+    L = int(inp["cache_len"].to(torch.int64).sum())
+    vbytes = 2 * L * row_b + 2 * vc.B * vc.T * row_b + 2 * vc.B * vc.T * vc.Hq * vc.D * 2
+
+    def verify():
+        swa.swa_attn_verify(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], cl,
+                            inp["sinks"], vc.window, vc.ring, vc.scale, workspace=ws, out=ov)
+
+    def block():
+        for _ in range(5):
+            swa_layer()
+        verify()
+
+    settle(block, args.settle_seconds)
+    for _ in range(max(1, args.warmup)):
+        block()
+    n = max(3, min(args.steps, 10))
+    layer_ms = time_launches(swa_layer, n, stream)
+    verify_ms = time_launches(verify, n, stream)
+    block_ms = time_launches(block, n, stream)
+    flop = 4.0 * cfg.D * swa_pairs(cfg.S, cfg.window) * cfg.Hq * cfg.B
+    del q, k, v, o, inp, ws, ov
+    torch.cuda.empty_cache()
+    return {
+        "workload": "stack_256k: 5 SWA layers (chunked prefill, 8 x 32768 of 262144 tokens) + 1 global "
+                    "q_len=4 verify at L=262144, B=1",
+        "ms_swa_layer": round(layer_ms, 4),
+        "swa_TFLOP/s": round(flop / (layer_ms * 1e-3) / 1e12, 2),
+        "ms_global_verify": round(verify_ms, 4),
+        "verify_algorithmic_bytes": vbytes,
+        "verify_GB/s": round(vbytes / (verify_ms * 1e-3) / 1e9, 1),
+        "ms_block": round(block_ms, 4),
     }
 
 
@@ -554,6 +615,9 @@ def main():
     if args.only == "mtp":
         print(json.dumps({"mtp_step": run_mtp(args, swa, torch, dev, stream)}), flush=True)
         return
+    if args.only == "stack":
+        print(json.dumps({"stack_256k": run_stack_256k(args, swa, torch, dev, stream)}), flush=True)
+        return
     if args.only == "backward":
         print(json.dumps({"backward": run_backward(args, swa, torch, dev, stream, PREFILL_CONFIGS["swa_32k"])}),
               flush=True)
@@ -589,6 +653,7 @@ def main():
         result["mtp_step"] = run_mtp(args, swa, torch, dev, stream)
         result["rope"] = run_rope(args, swa, torch, dev, stream, cfg, pres["roofline"]["kernel_ms"])
         result["backward"] = run_backward(args, swa, torch, dev, stream, cfg)
+        result["stack_256k"] = run_stack_256k(args, swa, torch, dev, stream)
     peaks = read_peaks()
     if peaks is not None:
         # fractions of the ceilings measured on this GPU: the SWA prefill moves
