@@ -107,6 +107,34 @@ def read_traffic(name: str, src: str):
         return None
 
 
+def read_mfma_busy(section: str):
+    """Matrix-core busy fraction of one prefill kernel from the committed
+    rocprofv3 counter summary (profiles/prefill_bf16_mfma_counters.txt,
+    section "[prefill]" or "[ga]"), or None when absent or taken on other
+    kernel sources."""
+    path = os.path.join(PROFILE_DIR, "prefill_bf16_mfma_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    start = text.find(f"[{section}]")
+    if start < 0:
+        return None
+    end = text.find("\n[", start + 1)
+    block = text[start:end if end > 0 else len(text)]
+    busy, src = None, None
+    for line in block.splitlines():
+        if line.startswith("derived: matrix-core busy fraction"):
+            busy = line.split()[-1]
+        elif line.startswith("kernel_source_sha256_16:"):
+            src = line.split()[-1]
+    if busy is None or src != source_hash(PREFILL_KERNEL_SRC):
+        return None
+    try:
+        return float(busy)
+    except ValueError:
+        return None
+
+
 def time_launches(fn, steps, stream, before=None):
     """Average duration (ms) of fn() over `steps` launches, measured with HIP
     events recorded on the stream the kernels run on."""
@@ -197,6 +225,7 @@ def run_prefill(args, swa, torch, dev, stream, cfg):
             "kernel_ms": round(ms_kernel, 5),
             "mfma_tflops": round(flop / (ms_kernel * 1e-3) / 1e12, 2),
             "mfma_frac_of_bf16_peak": round(flop / (ms_kernel * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "matrix_core_busy_by_counters": read_mfma_busy("prefill"),
             "roofline_tflops": round(min(MFMA_BF16_PEAK_TFLOPS, flop / p_bytes * HBM_PEAK_GBS / 1e3), 1),
         },
     }
@@ -225,6 +254,10 @@ def run_ga(args, swa, torch, dev, stream):
         "algorithmic_flop": gflop, "ms": round(gms, 4),
         "TFLOP/s": round(gflop / (gms * 1e-3) / 1e12, 2),
         "frac_of_bf16_mfma_peak": round(gflop / (gms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        # rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over the active cycles of the
+        # 1024 SIMDs (profiles/prefill_bf16_mfma_counters.txt); the chip runs
+        # this kernel below the 2.4 GHz the datasheet peak assumes
+        "matrix_core_busy_by_counters": read_mfma_busy("ga"),
     }
 
 
