@@ -275,19 +275,33 @@ struct QState {
       // the packed weights pass through an empty asm so that the
       // exponentials stay next to their MFMA instead of sinking to the use
       uint32_t pw[8];
+      // each group converts the previous group's exponentials after its
+      // MFMA, so no conversion waits on the exponential just issued
+      float ex[EPM];
 #pragma unroll
       for (int c = 0; c < Gm::NC; ++c) {
         sn = mfma32(ka[c], q[c], sn);
+        if (c > 0) {
 #pragma unroll
-        for (int e = 0; e < EPM; e += 2) {
-          const int v = c * EPM + e;
-          const bf16x2 w2 = {(__bf16)exp2_fast(fmaf(s[v], c2, -mu)), (__bf16)exp2_fast(fmaf(s[v + 1], c2, -mu))};
-          uint32_t w = __builtin_bit_cast(uint32_t, w2);
-          __asm__ volatile("" : "+v"(w));
-          pw[v >> 1] = w;
+          for (int e = 0; e < EPM; e += 2) {
+            const bf16x2 w2 = {(__bf16)ex[e], (__bf16)ex[e + 1]};
+            uint32_t w = __builtin_bit_cast(uint32_t, w2);
+            __asm__ volatile("" : "+v"(w));
+            pw[((c - 1) * EPM + e) >> 1] = w;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < EPM; ++e) {
+          ex[e] = exp2_fast(fmaf(s[c * EPM + e], c2, -mu));
+          __asm__ volatile("" : "+v"(ex[e]));
         }
         extra(c);
         __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int e = 0; e < EPM; e += 2) {
+        const bf16x2 w2 = {(__bf16)ex[e], (__bf16)ex[e + 1]};
+        pw[((Gm::NC - 1) * EPM + e) >> 1] = __builtin_bit_cast(uint32_t, w2);
       }
       pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
       pb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
