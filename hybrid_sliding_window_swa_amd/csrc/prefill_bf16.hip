@@ -64,7 +64,8 @@ struct TileGeom {
 // Global -> register half of staging 32-key tiles of K and of V (possibly of
 // different tiles), through raw buffer loads: the tile's first row is a
 // scalar base, each thread's offset inside the tile is fixed, and rows at or
-// past Sk read as zeros (always masked out).
+// past the given key end (the last key any query of the workgroup can see,
+// plus one) read as zeros, whatever the caller's buffer holds there.
 template <int D, int NT, int POL = kCacheDefault>
 struct Stager {
   using Gm = TileGeom<D>;
@@ -113,6 +114,20 @@ struct Stager {
                                        int Sk, int tid) {
     load_k(kg, kv_tok, kb, Sk, tid);
     load_v(vg, kv_tok, kb, Sk, tid);
+  }
+
+  // Zero the loaded rows of the tile below tile-relative row r0: keys that no
+  // query of the workgroup can see.  Such rows only get exact-zero weights,
+  // but a zero weight times a non-finite value is still NaN inside P V, so
+  // they must not carry whatever the caller's buffer holds there.
+  __device__ __forceinline__ void zero_below(int r0, int tid) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      if ((tid + i * NT) / (D / 8) < r0) {
+        kpre[i] = u32x4{0u, 0u, 0u, 0u};
+        vpre[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
   }
 
   // Register -> LDS half: row-major tiles with padded pitches.
@@ -439,7 +454,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
 
   const int tlast = min(t0 + TB, p.Sq) - 1;
   const int pos_lo = p.q_offset + t0, pos_hi = p.q_offset + tlast;
-  const int kt_begin = (W > 0 ? max(0, pos_lo - W + 1) : 0) / KT, kt_end = pos_hi / KT;
+  // keys [key_lo, key_end) are the ones the workgroup's queries can see:
+  // tile rows outside read as (or are set to) zeros
+  const int key_lo = W > 0 ? max(0, pos_lo - W + 1) : 0, key_end = pos_hi + 1;
+  const int kt_begin = key_lo / KT, kt_end = pos_hi / KT;
   // this wave's tiles: [wk0, wk1] (empty when its tokens are all past Sq)
   const int wpos_lo = p.q_offset + tw0;
   const int wpos_hi = p.q_offset + min(tw0 + TW, p.Sq) - 1;
@@ -463,11 +481,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
     for (int i = 0; i < PK; ++i) {
       pro[i].init(kv_tok, tid);
       if (kt_begin + i <= kt_end) {
-        pro[i].load_k(kg, kv_tok, (kt_begin + i) * KT, p.Sk, tid);
-        if (i < PV) pro[i].load_v(vg, kv_tok, (kt_begin + i) * KT, p.Sk, tid);
+        pro[i].load_k(kg, kv_tok, (kt_begin + i) * KT, key_end, tid);
+        if (i < PV) pro[i].load_v(vg, kv_tok, (kt_begin + i) * KT, key_end, tid);
       }
     }
     sink = p.sinks ? p.sinks[g * G + col % G] : 0.0f;
+    if (!NOWIN) pro[0].zero_below(key_lo - kt_begin * KT, tid);
 #pragma unroll
     for (int i = 0; i < PK; ++i)
       if (kt_begin + i <= kt_end) {
@@ -508,8 +527,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
     // single steps first, so that a multiple of four tiles remains
     for (const int kt_single = kt_begin + ((kt_end - kt_begin) & 3); kt < kt_single; ++kt) {
       const int r = kt - kt_begin;
-      if (kt + 5 <= kt_end) s0.load_k(kg, kv_tok, (kt + 5) * KT, p.Sk, tid);
-      if (kt + 4 <= kt_end) s0.load_v(vg, kv_tok, (kt + 4) * KT, p.Sk, tid);
+      if (kt + 5 <= kt_end) s0.load_k(kg, kv_tok, (kt + 5) * KT, key_end, tid);
+      if (kt + 4 <= kt_end) s0.load_v(vg, kv_tok, (kt + 4) * KT, key_end, tid);
       s = st.template fold<true>(s, c2, v_lds[r & 7], k_lds[(r + 1) & 7], (kt + 1) * KT, tile_mask(kt + 1), W, half,
                                  lane);
       if (kt + 5 <= kt_end) s0.store_k(k_lds[(r + 5) & 7], tid);
@@ -537,13 +556,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
       const int r = kt - kt_begin;
       auto load_pair = [&](Stg& a, Stg& b, int i, int c, int cb) {  // K(kt+5+i), V(kt+4+i) into a; i+1 into b
         if (c == cb && kt + 5 + i <= kt_end)
-          a.load_k(Stg::tile_at(kp + i * tstride, (kt + 5 + i) * KT, p.Sk, row_b, pad_b), tid);
+          a.load_k(Stg::tile_at(kp + i * tstride, (kt + 5 + i) * KT, key_end, row_b, pad_b), tid);
         if (c == cb + 1 && kt + 4 + i <= kt_end)
-          a.load_v(Stg::tile_at(vp + i * tstride, (kt + 4 + i) * KT, p.Sk, row_b, pad_b), tid);
+          a.load_v(Stg::tile_at(vp + i * tstride, (kt + 4 + i) * KT, key_end, row_b, pad_b), tid);
         if (c == cb + 2 && kt + 6 + i <= kt_end)
-          b.load_k(Stg::tile_at(kp + (i + 1) * tstride, (kt + 6 + i) * KT, p.Sk, row_b, pad_b), tid);
+          b.load_k(Stg::tile_at(kp + (i + 1) * tstride, (kt + 6 + i) * KT, key_end, row_b, pad_b), tid);
         if (c == cb + 3 && kt + 5 + i <= kt_end)
-          b.load_v(Stg::tile_at(vp + (i + 1) * tstride, (kt + 5 + i) * KT, p.Sk, row_b, pad_b), tid);
+          b.load_v(Stg::tile_at(vp + (i + 1) * tstride, (kt + 5 + i) * KT, key_end, row_b, pad_b), tid);
       };
       auto store_pair = [&](const Stg& a, const Stg& b, int i, int c, int cb) {
         if (c == cb && kt + 5 + i <= kt_end) a.store_k(k_lds[(r + 5 + i) & 7], tid);
@@ -583,8 +602,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
       }
     };
     if ((kt_end - kt_begin) & 1) {  // a single step first, so that pairs remain
-      if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, p.Sk, tid);
-      if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, p.Sk, tid);
+      if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, key_end, tid);
+      if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, key_end, tid);
       fold_step(kt);
       if (kt + 3 <= kt_end) s0.store_k(k_lds[3], tid);
       if (kt + 2 <= kt_end) s0.store_v(v_lds[2], tid);
@@ -597,10 +616,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
     if (wv >= NW / 2) __builtin_amdgcn_s_setprio(1);
     for (; kt < kt_end; kt += 2) {
       const int r = kt - kt_begin;
-      if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, p.Sk, tid);
-      if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, p.Sk, tid);
-      if (kt + 4 <= kt_end) s1.load_k(kg, kv_tok, (kt + 4) * KT, p.Sk, tid);
-      if (kt + 3 <= kt_end) s1.load_v(vg, kv_tok, (kt + 3) * KT, p.Sk, tid);
+      if (kt + 3 <= kt_end) s0.load_k(kg, kv_tok, (kt + 3) * KT, key_end, tid);
+      if (kt + 2 <= kt_end) s0.load_v(vg, kv_tok, (kt + 2) * KT, key_end, tid);
+      if (kt + 4 <= kt_end) s1.load_k(kg, kv_tok, (kt + 4) * KT, key_end, tid);
+      if (kt + 3 <= kt_end) s1.load_v(vg, kv_tok, (kt + 3) * KT, key_end, tid);
       fold_step(kt);
       fold_step(kt + 1);
       if (kt + 3 <= kt_end) s0.store_k(k_lds[(r + 3) & 3], tid);
@@ -832,12 +851,17 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
   Stager<D, NT, kStripKvPolicy> sg;
   sg.init(kv_tok, tid);
   const float sink2 = p.sinks ? p.sinks[g * G + col % G] * kLog2e : kNegInf;
+  // keys [key_lo, key_end) are the ones the strip's queries can see: tile
+  // rows outside read as (or are set to) zeros
+  const int key_lo = max(0, p.q_offset + blk0 * TB - W + 1);
+  const int key_end = p.q_offset + min(blk1 * TB, p.Sq);
 
   // prologue: the first block's queries and its whole window
   load_q_rows(blk0 * TB + wv * TW);
   int loaded_hi = kt_hi(blk0);
   for (int kt = kt_lo(blk0); kt <= loaded_hi; ++kt) {
-    sg.load(kg, vg, kv_tok, kt * KT, p.Sk, tid);
+    sg.load(kg, vg, kv_tok, kt * KT, key_end, tid);
+    sg.zero_below(key_lo - kt * KT, tid);
     sg.store(k_ring[kt % NR], v_ring[kt % NR], tid);
   }
   if constexpr (ROPE) {
@@ -857,7 +881,7 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
     const int new_kt = nxt ? kt_hi(blk + 1) : -1;
     const bool have_new = new_kt > loaded_hi;
     if (nxt) load_q_rows(tw0 + TB);
-    if (have_new) sg.load(kg, vg, kv_tok, new_kt * KT, p.Sk, tid);
+    if (have_new) sg.load(kg, vg, kv_tok, new_kt * KT, key_end, tid);
 
     // compute this block from the ring; the second wave of each SIMD pair
     // at a raised priority while the tiles are folded (see the

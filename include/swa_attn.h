@@ -92,8 +92,13 @@ SWA_API const char *swa_status_string(swa_status_t status);
  *          k / v and q_offset = c0 (only keys >= c0 - window + 1 are read).
  *   sm_scale  multiplier of q.k (normally 1/sqrt(D)), finite and > 0; the
  *          sink is not scaled.
- * Rows of k / v inside a loaded 32-key tile but outside the window are read
- * and weighted by exactly zero, so k and v must be finite for all Sk rows.
+ * Rows of k / v that no query of the call can see -- positions below
+ * max(0, q_offset - window + 1) (none for global attention) and at or above
+ * q_offset + Sq -- are never used and may hold anything, NaN included (e.g.
+ * the unfilled tail of a cache behind a chunk, or stale rows below the
+ * window).  Inside that range a non-finite value can also reach outputs of
+ * nearby queries whose windows exclude it (masked weights are exact zeros,
+ * but they still multiply the loaded value rows of a 32-key tile).
  * B == 0 or Sq == 0 is a valid no-op.
  */
 SWA_API swa_status_t swa_attn_prefill(const void *q, const void *k, const void *v,
@@ -161,7 +166,9 @@ SWA_API size_t swa_attn_backward_workspace_bytes(int B, int Sq, int Hq);
  * Accumulation is fp32; P and dS are rounded to bf16 for the matrix cores;
  * dq, dk, dv are rounded to bf16 (nearest even); dsink is summed in a fixed
  * order (deterministic).  SWA_BF16 only; shape rules as swa_attn_prefill.
- * Calls sharing a workspace must not overlap.
+ * Unlike the forward, the backward reads whole 32-key tiles around each
+ * window and multiplies rows outside it by zero weights, so k and v must be
+ * finite for all Sk rows.  Calls sharing a workspace must not overlap.
  */
 SWA_API swa_status_t swa_attn_backward(const void *q, const void *k, const void *v,
                                const float *sinks, const void *o, const float *lse,

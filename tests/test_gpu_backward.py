@@ -12,14 +12,19 @@ pytestmark = pytest.mark.gpu
 
 # Gradient tolerance.  The kernels see bf16 inputs exactly (the oracle gets
 # the same values), accumulate in fp32, and round P and dS to bf16 (relative
-# 2^-9) before the matrix cores, as the forward rounds P; they also use the
-# forward's bf16 O (for <dO, O>) and its fp32 LSE; dq/dk/dv are rounded to
-# bf16 (2^-9).  Each gradient element is a sum of many terms of both signs,
-# so the error is judged against the gradient's scale: elementwise
-# |gpu - ref| <= GRAD_TOL * (|ref| + rms(ref)) -- about twenty bf16 roundings
-# of the typical term -- and relative L2 < GRAD_L2 (measured 2.3e-3 to
-# 6.5e-3 over the cases below).
-GRAD_TOL = 5e-2
+# 2^-9) before the matrix cores, as the forward rounds P; dq/dk/dv are
+# rounded to bf16 (2^-9).  The largest elementwise errors come from the row
+# term D_i = <dO_i, O_i>, formed (as in any backward that keeps only the
+# forward's output) from the bf16-rounded O: its error, up to 2^-9 of
+# sum_d |dO_id O_id|, enters dS_ij = P_ij (dP_ij - D_i) unreduced where dP_ij
+# and D_i nearly cancel (a query whose weight sits on few keys, e.g. W = 1).
+# Each element is judged against the gradient's scale:
+# |gpu - ref| <= GRAD_TOL * (|ref| + rms(ref)).  Over every case below and the
+# full 32K workload the largest err / (|ref| + rms) measured on the MI355X is
+# 3.8e-2 (dk at W = 1, dq at 32K); GRAD_TOL keeps a 1.2x margin above it.
+# The relative L2 error per tensor is held to the bf16 rtol of 1e-2
+# (measured at most 6.6e-3).
+GRAD_TOL = 4.5e-2
 GRAD_L2 = 1e-2
 # The saved LSE: the forward sums its attention weights after rounding each
 # to bf16 (relative error <= 2^-9, the same rounding that enters P V), and
@@ -53,7 +58,9 @@ def _check_grad(got, ref, name):
     bound = GRAD_TOL * (np.abs(r) + rms)
     worst = float((err - bound).max()) if r.size else 0.0
     l2 = rel_l2(got, r) if rms > 0 else 0.0
-    print(f"{name}: max abs err {err.max():.3e} rms(ref) {rms:.3e} rel L2 {l2:.3e}")
+    need = float((err / (np.abs(r) + rms)).max()) if rms > 0 else 0.0
+    print(f"{name}: max abs err {err.max():.3e} rms(ref) {rms:.3e} rel L2 {l2:.3e} "
+          f"max err/(|ref|+rms) {need:.3e}", flush=True)
     assert worst <= 0, f"{name}: max excess {worst:.3e}"
     assert l2 < GRAD_L2, f"{name}: relative L2 {l2:.3e}"
 

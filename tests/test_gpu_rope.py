@@ -123,6 +123,9 @@ FUSED_CASES = [
     ("w128_g4_d64_rot32", 1, 161, 193, 8, 2, 64, 128, 32),
     ("w1_g8", 1, 70, 70, 8, 1, 128, 1, 42),
     ("model_heads", 1, 600, 600, 64, 8, 128, 128, 42),
+    # block starts off the 32-key tile grid (q_offset % 32 != 0)
+    ("w96_g8_offset170", 1, 200, 370, 64, 8, 128, 96, 42),
+    ("w96_g4_d64_offset21", 1, 150, 171, 16, 4, 64, 96, 20),
 ]
 
 

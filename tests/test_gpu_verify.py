@@ -43,6 +43,9 @@ CASES = [
     (_vcfg("ring_w2", 10, 4, 64, 8, 128, 2, True, 2, 0, 0), EDGE_LENS),
     (_vcfg("ring_d64", 10, 4, 16, 2, 64, 128, True, 128, 0, 0), EDGE_LENS),
     (_vcfg("ring_t8_g8", 10, 8, 64, 8, 128, 128, True, 128, 0, 0), EDGE_LENS),
+    # the wider window the pages compare W = 128 against, on a 512-slot ring
+    (_vcfg("ring_w512", 10, 4, 64, 8, 128, 512, True, 512, 0, 0),
+     [0, 1, 127, 128, 129, 511, 512, 513, 1000, 5000]),
     # linear global caches (several splits + combine)
     (_vcfg("linear_global_t4", 10, 4, 64, 8, 128, 0, False, 1100, 0, 0), EDGE_LENS),
     (_vcfg("linear_global_t1", 10, 1, 16, 2, 128, 0, False, 1100, 0, 0), EDGE_LENS),
@@ -181,24 +184,23 @@ def _full_verify(cfg: VerifyConfig, check_b):
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
     L = inp["cache_len"]
+    print(f"[full-size] {cfg.name}: oracle on {len(check_b)} requests", flush=True)
     for b in check_b:
         Lb = int(L[b])
         base = int(inp["hist_base"][b])
         n = Lb - base
-        print(f"[full-size] {cfg.name}: oracle on request {b} (L={Lb})", flush=True)
         ref = oracle.verify(inp["q"][b:b + 1].cpu(), inp["k_new"][b:b + 1].cpu(),
                             inp["v_new"][b:b + 1].cpu(), inp["k_hist"][b:b + 1, :n].cpu(),
                             inp["v_hist"][b:b + 1, :n].cpu(), inp["hist_base"][b:b + 1],
                             L[b:b + 1], inp["sinks"].cpu(), cfg.window, cfg.scale)
-        assert_close(o[b:b + 1], ref, BF16_TOL, f"{cfg.name} request {b}")
+        assert_close(o[b:b + 1], ref, BF16_TOL, f"{cfg.name} request {b} (L={Lb})")
+        assert rel_l2(o[b:b + 1], ref) < 1e-2, f"{cfg.name} request {b}: relative L2"
 
 
 def test_full_size_verify_ga_b64():
+    """Every request of the 64-request q_len = 4 verify on the global cache."""
     cfg = VERIFY_CONFIGS["verify_ga_b64"]
-    from swa_inputs import draw_lengths
-    L = draw_lengths(cfg.B, cfg.len_lo, cfg.len_hi, cfg.seed)
-    picks = sorted({int(L.argmin()), int(L.argmax()), 0, 17, 42, cfg.B - 1})
-    _full_verify(cfg, picks)
+    _full_verify(cfg, range(cfg.B))
 
 
 def test_full_size_verify_swa_b64():
@@ -207,12 +209,10 @@ def test_full_size_verify_swa_b64():
 
 
 def test_full_size_decode_ga_b64():
-    """q_len = 1 decode over the 64-request global cache (the verify entry point)."""
+    """Every request of the q_len = 1 decode over the 64-request global cache
+    (the verify entry point)."""
     cfg = VERIFY_CONFIGS["decode_ga_b64"]
-    from swa_inputs import draw_lengths
-    L = draw_lengths(cfg.B, cfg.len_lo, cfg.len_hi, cfg.seed)
-    picks = sorted({int(L.argmin()), int(L.argmax()), 0, 31, cfg.B - 1})
-    _full_verify(cfg, picks)
+    _full_verify(cfg, range(cfg.B))
 
 
 def test_full_size_decode_swa_b64():
@@ -223,3 +223,38 @@ def test_full_size_decode_swa_b64():
 def test_full_size_verify_ga_256k():
     cfg = VERIFY_CONFIGS["verify_ga_256k"]
     _full_verify(cfg, [0])
+
+
+def test_verify_many_requests_split():
+    """More requests than the longest-first split order serves (B > 256):
+    the split workgroups then take the plain grid order.  A few requests are
+    long enough for two 16384-row splits plus the combine; the rest are short
+    or empty.  Every request is checked."""
+    cfg = _vcfg("many_requests", 300, 4, 16, 2, 64, 0, False, 16500, 0, 0)
+    g = torch.Generator()
+    g.manual_seed(derive_seed("many_requests", "lens"))
+    lens = torch.randint(0, 700, (cfg.B,), generator=g)
+    lens[torch.tensor([0, 7, 150, 299])] = torch.tensor([16500, 16385, 16384, 16499])
+    lens[torch.tensor([1, 2])] = 0
+    dev = device()
+    m = swa()
+    assert m.swa_attn_verify_workspace_bytes(cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.D, cfg.slots, False, 0) > 0
+    inp = verify_inputs(cfg, device=dev, cache_len=lens)
+    cl = inp["cache_len"].to(torch.int32).to(dev)
+    o = m.swa_attn_verify(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], cl,
+                          inp["sinks"], cfg.window, cfg.ring, cfg.scale)
+    torch.cuda.synchronize()
+    L = inp["cache_len"]
+    # the short requests in one oracle call over their 700-row histories, the
+    # long ones one at a time
+    short = torch.nonzero(L < 700).flatten()
+    groups = [(short, 700)] + [(torch.tensor([b]), int(L[b])) for b in torch.nonzero(L >= 700).flatten()]
+    for idx, hlen in groups:
+        idx_d = idx.to(dev)
+        sel = lambda t: t.index_select(0, idx_d).cpu()
+        ref = oracle.verify(sel(inp["q"]), sel(inp["k_new"]), sel(inp["v_new"]), sel(inp["k_hist"][:, :hlen]),
+                            sel(inp["v_hist"][:, :hlen]), inp["hist_base"][idx], L[idx], inp["sinks"].cpu(),
+                            cfg.window, cfg.scale)
+        got = o.index_select(0, idx_d)
+        assert_close(got, ref, BF16_TOL, f"{cfg.name} requests {idx.tolist()[:4]}...")
+        assert rel_l2(got, ref) < 1e-2
