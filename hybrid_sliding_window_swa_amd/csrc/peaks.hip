@@ -4,8 +4,10 @@
 //
 //   * HBM streaming read: a grid-stride read of 8 GiB, four independent
 //     16-byte loads in flight per thread, XOR-reduced so nothing is dead code.
-//   * HBM copy: the same grid stride reading one 8 GiB buffer and writing
-//     another (bytes read + bytes written per second).
+//   * HBM copy: reading one 8 GiB buffer and writing another (bytes read +
+//     bytes written per second), best of 1, 2, 4 or 8 independent loads in
+//     flight per thread before their stores, grid-stride or one contiguous
+//     range per workgroup.
 //   * Both with default and with non-temporal loads / stores; the faster
 //     policy is the ceiling.
 //   * bf16 MFMA: v_mfma_f32_32x32x16_bf16 on four independent accumulators,
@@ -14,7 +16,7 @@
 // Every kernel runs untimed for about half a second first, so the clocks
 // are at their sustained-load level, then the mean of several launches is
 // timed with HIP events (the streaming kernels: best of five grid sizes and
-// two cache policies).
+// two cache policies; the copies also of the depths and orders above).
 // One JSON line per measurement on stdout.
 // All accesses are grid-stride loops bounded by the element count.
 #include <hip/hip_runtime.h>
@@ -49,17 +51,38 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ p, 
 }
 
 template <bool NT>
-__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ p, u32x4* __restrict__ q, long n16) {
-  long i = blockIdx.x * 256L + threadIdx.x;
-  const long stride = (long)gridDim.x * 256;
-  for (; i < n16; i += stride) {
-    const u32x4 v = ld<NT>(p + i);
-    if constexpr (NT) {
-      __builtin_nontemporal_store(v, q + i);
-    } else {
-      q[i] = v;
-    }
+__device__ __forceinline__ void st(u32x4 v, u32x4* p) {
+  if constexpr (NT) {
+    __builtin_nontemporal_store(v, p);
+  } else {
+    *p = v;
   }
+}
+
+// DEPTH independent 16-byte loads in flight per thread, then their DEPTH
+// stores.  BLOCKED: workgroup b copies one contiguous range (a stream per
+// workgroup, like a strip of the attention kernels); otherwise grid-stride.
+template <bool NT, int DEPTH, bool BLOCKED>
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ p, u32x4* __restrict__ q, long n16) {
+  long i, end, stride;
+  if constexpr (BLOCKED) {
+    const long per = ((n16 + gridDim.x - 1) / gridDim.x + 256L * DEPTH - 1) / (256L * DEPTH) * (256L * DEPTH);
+    i = blockIdx.x * per + threadIdx.x;
+    end = blockIdx.x * per + per < n16 ? blockIdx.x * per + per : n16;
+    stride = 256;
+  } else {
+    i = blockIdx.x * 256L + threadIdx.x;
+    end = n16;
+    stride = (long)gridDim.x * 256;
+  }
+  for (; i + (DEPTH - 1) * stride < end; i += DEPTH * stride) {
+    u32x4 v[DEPTH];
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) v[j] = ld<NT>(p + i + j * stride);
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) st<NT>(v[j], q + i + j * stride);
+  }
+  for (; i < end; i += stride) st<NT>(ld<NT>(p + i), q + i);
 }
 
 constexpr int kMfmaIter = 8192;
@@ -135,10 +158,11 @@ int main() {
   if (!ok(hipMemset(a, 1, bytes), "hipMemset") || !ok(hipDeviceSynchronize(), "init")) return 1;
 
   // streaming kernels: best of several grid sizes and both cache policies
-  // (clocks settle on the first)
+  // (clocks settle on the first); copies also over 1, 2, 4 or 8 loads in
+  // flight per thread, grid-stride or one contiguous range per workgroup
   float rd = 1e30f, cp = 1e30f;
-  int rd_grid = 0, cp_grid = 0;
-  bool rd_nt = false, cp_nt = false;
+  int rd_grid = 0, cp_grid = 0, cp_depth = 0;
+  bool rd_nt = false, cp_nt = false, cp_blocked = false;
   for (int nt = 0; nt < 2; ++nt) {
     for (int mult : {4, 8, 16, 32, 64}) {
       const int grid = mult * cus;
@@ -152,22 +176,37 @@ int main() {
           },
           settle, 10);
       if (r < rd) { rd = r; rd_grid = grid; rd_nt = nt; }
-      const float c = time_ms(
-          [&] {
-            if (nt)
-              hipLaunchKernelGGL(copy_kernel<true>, dim3(grid), dim3(256), 0, 0, a, b, n16);
-            else
-              hipLaunchKernelGGL(copy_kernel<false>, dim3(grid), dim3(256), 0, 0, a, b, n16);
-          },
-          settle, 10);
-      if (c < cp) { cp = c; cp_grid = grid; cp_nt = nt; }
+      for (int blocked = 0; blocked < 2; ++blocked) {
+        for (int depth : {1, 2, 4, 8}) {
+          const float c = time_ms(
+              [&] {
+#define SWA_COPY(NTV, DV, BV) hipLaunchKernelGGL((copy_kernel<NTV, DV, BV>), dim3(grid), dim3(256), 0, 0, a, b, n16)
+#define SWA_COPY_D(NTV, BV)       \
+  switch (depth) {                \
+    case 1: SWA_COPY(NTV, 1, BV); break; \
+    case 2: SWA_COPY(NTV, 2, BV); break; \
+    case 4: SWA_COPY(NTV, 4, BV); break; \
+    default: SWA_COPY(NTV, 8, BV); break; \
+  }
+                if (nt && blocked) { SWA_COPY_D(true, true) }
+                else if (nt) { SWA_COPY_D(true, false) }
+                else if (blocked) { SWA_COPY_D(false, true) }
+                else { SWA_COPY_D(false, false) }
+#undef SWA_COPY_D
+#undef SWA_COPY
+              },
+              0.0f, 10);
+          if (c < cp) { cp = c; cp_grid = grid; cp_nt = nt; cp_depth = depth; cp_blocked = blocked; }
+        }
+      }
     }
   }
   printf("{\"measure\": \"hbm_read\", \"bytes\": %ld, \"grid\": %d, \"nontemporal\": %s, \"ms\": %.4f, \"GB/s\": %.1f}\n",
          bytes, rd_grid, rd_nt ? "true" : "false", rd, bytes / (rd * 1e-3) / 1e9);
-  printf("{\"measure\": \"hbm_copy\", \"bytes_read_plus_written\": %ld, \"grid\": %d, \"nontemporal\": %s, \"ms\": %.4f, "
-         "\"GB/s\": %.1f}\n",
-         2 * bytes, cp_grid, cp_nt ? "true" : "false", cp, 2.0 * bytes / (cp * 1e-3) / 1e9);
+  printf("{\"measure\": \"hbm_copy\", \"bytes_read_plus_written\": %ld, \"grid\": %d, \"nontemporal\": %s, "
+         "\"loads_in_flight\": %d, \"contiguous_per_workgroup\": %s, \"ms\": %.4f, \"GB/s\": %.1f}\n",
+         2 * bytes, cp_grid, cp_nt ? "true" : "false", cp_depth, cp_blocked ? "true" : "false", cp,
+         2.0 * bytes / (cp * 1e-3) / 1e9);
   const float mm = time_ms([&] { hipLaunchKernelGGL(mfma_kernel, dim3(mfma_blocks), dim3(512), 0, 0, sink, 0.001f); },
                            500.0f, 10);
   const double flop = (double)mfma_blocks * 8 * kMfmaIter * 4 * 32768.0;
