@@ -6,6 +6,7 @@ declared in ``include/swa_attn.h``).  The functions carry the C names:
     swa_attn_prefill(q, k, v, sinks, window, q_offset=0, sm_scale=None, out=None)
     swa_attn_verify_workspace_bytes(...)
     swa_attn_verify(q, k_new, v_new, k_cache, v_cache, cache_len, sinks, window, ring, ...)
+    swa_attn_verify_noalloc(q, k_new, v_new, k_cache, v_cache, cache_len, sinks, window, ring, ...)
     kv_ring_append(k_cache, v_cache, k_new, v_new, cache_len, n_append, ring)
     swa_mtp_accept_workspace_bytes(B, q_len, vocab)
     swa_mtp_greedy_accept(logits, draft, ...) -> (target, n_append)
@@ -30,7 +31,7 @@ import torch
 
 __all__ = [
     "SwaError", "library_path", "load_library", "swa_attn_prefill",
-    "swa_attn_verify_workspace_bytes", "swa_attn_verify", "kv_ring_append",
+    "swa_attn_verify_workspace_bytes", "swa_attn_verify", "swa_attn_verify_noalloc", "kv_ring_append",
     "swa_mtp_accept_workspace_bytes", "swa_mtp_greedy_accept", "swa_cache_advance",
     "swa_rope_apply", "rope_dims", "swa_attn_prefill_rope", "swa_attn_prefill_lse",
     "swa_attn_backward_workspace_bytes", "swa_attn_backward", "EXPORTED_SYMBOLS",
@@ -45,7 +46,7 @@ EXPORTED_SYMBOLS = ("swa_status_string", "swa_attn_prefill", "swa_attn_verify_wo
                     "swa_attn_verify", "kv_ring_append", "swa_mtp_accept_workspace_bytes",
                     "swa_mtp_greedy_accept", "swa_cache_advance", "swa_rope_apply",
                     "swa_attn_prefill_rope", "swa_attn_prefill_lse", "swa_attn_backward_workspace_bytes",
-                    "swa_attn_backward")
+                    "swa_attn_backward", "swa_attn_verify_noalloc")
 
 
 class SwaError(RuntimeError):
@@ -76,6 +77,8 @@ def load_library():
     lib.swa_attn_verify_workspace_bytes.restype = sz
     lib.swa_attn_verify.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, p, sz, p]
     lib.swa_attn_verify.restype = i
+    lib.swa_attn_verify_noalloc.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f, i, p]
+    lib.swa_attn_verify_noalloc.restype = i
     lib.kv_ring_append.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, i, p]
     lib.kv_ring_append.restype = i
     i64 = ctypes.c_int64
@@ -248,6 +251,44 @@ def swa_attn_verify(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                              int(bool(ring)), int(window), float(sm_scale), _dtype_code(q),
                              _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "swa_attn_verify")
+    return out
+
+
+def swa_attn_verify_noalloc(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            k_cache: torch.Tensor, v_cache: torch.Tensor, cache_len: torch.Tensor,
+                            sinks: Optional[torch.Tensor], window: int, ring: bool,
+                            sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """swa_attn_verify with the split partials in the library's fixed
+    per-GPU scratch (no workspace; calls on one GPU must not overlap).  With
+    ``out`` given, the call allocates nothing."""
+    lib = load_library()
+    _dev(q, "q", ndim=4)
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, name, q.dtype, 4)
+    _dev(cache_len, "cache_len", torch.int32, 1)
+    _dev(sinks, "sinks", torch.float32, 1)
+    B, T, Hq, D = q.shape
+    _, slots, Hkv, _ = k_cache.shape
+    if k_new.shape != (B, T, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, q_len, Hkv, D]")
+    if v_cache.shape != k_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shape mismatch")
+    if cache_len.shape[0] != B:
+        raise ValueError("cache_len must have B entries")
+    if sm_scale is None:
+        sm_scale = 1.0 / (D ** 0.5)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, "out", q.dtype, 4)
+        if out.shape != q.shape:
+            raise ValueError("out shape mismatch")
+    st = lib.swa_attn_verify_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(cache_len), _ptr(sinks), _ptr(out), B, T, Hq, Hkv, D, slots,
+                                     int(bool(ring)), int(window), float(sm_scale), _dtype_code(q),
+                                     _stream(stream))
+    _check(st, "swa_attn_verify_noalloc")
     return out
 
 

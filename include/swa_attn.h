@@ -218,6 +218,34 @@ SWA_API swa_status_t swa_attn_verify(const void *q, const void *k_new, const voi
                              void *stream);
 
 /*
+ * swa_attn_verify without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid allocation.  Same arguments (minus workspace and
+ * workspace_bytes), validation, kernels and results as swa_attn_verify.  The
+ * split partials live in a fixed device array inside the library, one copy
+ * per GPU, allocated when the library's code is loaded on that GPU and held
+ * until the process ends; the call itself allocates nothing.
+ *   Maximum: swa_attn_verify_workspace_bytes(...) of the same arguments must
+ *   not exceed SWA_VERIFY_NOALLOC_SCRATCH_BYTES (64 MiB, e.g. 64 requests x 8
+ *   KV heads over 65536-slot global caches need 34 MB, one request over
+ *   262144 slots 4.3 MB); larger sizes return SWA_ERR_WORKSPACE with nothing
+ *   enqueued.
+ *   All calls on one GPU share that GPU's array, so calls that overlap on
+ *   one GPU (other streams, other host threads) race and must be ordered by
+ *   the caller.  Nothing in the array has to start at zero.
+ *   The first call on each GPU looks up the array's device address (no
+ *   allocation); make it once outside capture if the runtime forbids that
+ *   lookup during capture.
+ */
+#define SWA_VERIFY_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+SWA_API swa_status_t swa_attn_verify_noalloc(const void *q, const void *k_new, const void *v_new,
+                                     const void *k_cache, const void *v_cache,
+                                     const int32_t *cache_len, const float *sinks, void *o,
+                                     int B, int q_len, int Hq, int Hkv, int D,
+                                     int cache_slots, int ring, int window, float sm_scale,
+                                     swa_dtype_t dtype, void *stream);
+
+/*
  * Commit accepted tokens after a verify step.  For every request b and every
  * t < n_append[b], row t of k_new / v_new [B, q_len, Hkv, D] is copied to the
  * slot of position cache_len[b] + t: slot (cache_len[b] + t) % cache_slots

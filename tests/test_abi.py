@@ -105,6 +105,29 @@ def test_verify_validation(lib):
     assert _verify(lib, B=0, ptr=0) == OK
 
 
+def _verify_noalloc(lib, ptr=1, B=2, T=4, Hq=64, Hkv=8, D=128, slots=128, ring=1, W=128, dt=BF16,
+                    scale=0.1):
+    P = lambda x: ctypes.c_void_p(x) if x else None
+    return lib.swa_attn_verify_noalloc(P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), P(ptr), None, P(ptr),
+                                       B, T, Hq, Hkv, D, slots, ring, W, scale, dt, None)
+
+
+def test_verify_noalloc_validation(lib):
+    """The allocation-free verify rejects what swa_attn_verify rejects, and
+    sizes whose split partials exceed its fixed scratch, before any HIP call."""
+    assert _verify_noalloc(lib, ptr=0) == NULL
+    assert _verify_noalloc(lib, T=17) == SHAPE
+    assert _verify_noalloc(lib, slots=127) == SHAPE
+    assert _verify_noalloc(lib, D=32) == UNSUP
+    assert _verify_noalloc(lib, scale=float("nan")) == UNSUP
+    assert _verify_noalloc(lib, B=0, ptr=0) == OK
+    limit = 64 << 20
+    # 128 requests over 65536-slot global caches: 68 MB of partials > 64 MiB
+    assert lib.swa_attn_verify_workspace_bytes(128, 4, 64, 8, 128, 65536, 0, 0, BF16) > limit
+    assert _verify_noalloc(lib, B=128, ring=0, W=0, slots=65536) == WS
+    assert lib.swa_attn_verify_workspace_bytes(64, 4, 64, 8, 128, 65536, 0, 0, BF16) <= limit
+
+
 def test_workspace_sizes(lib):
     ws = lambda *a: lib.swa_attn_verify_workspace_bytes(*a)
     # ring of 128 slots: one split, the kernel writes O directly
