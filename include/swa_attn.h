@@ -31,7 +31,9 @@
  *   - Tensors are dense, row-major, token-major: [B, S, H, D] (the last index
  *     is contiguous).  Every data pointer is a DEVICE pointer (hipMalloc'd or
  *     from a framework allocator) owned by the caller.  The library allocates
- *     no memory and keeps no state between calls.
+ *     no memory and keeps no state between calls (the one exception is the
+ *     fixed per-GPU array of swa_attn_verify_noalloc, part of the library's
+ *     device code; see there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work on it and return without synchronising.
  *   - Host-visible arguments are validated before anything is launched; on a
