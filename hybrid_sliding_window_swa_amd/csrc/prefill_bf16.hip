@@ -151,6 +151,47 @@ struct Stager {
   }
 };
 
+// Direct-to-LDS staging of a 32-key tile in the padded layouts of KTile and
+// VTile (pitch D + 8 and D + 32): gfx950's buffer_load_dwordx4 ... lds writes
+// the 16 bytes of lane l of a wave to LDS byte M0 + 16 l, so one load fills a
+// 1 KiB window of 64 16-byte slots.  Window j of a tile covers slots 64 j ..
+// 64 j + 63 (slot P = row * pitch16 + chunk); a slot in a row's padding, or
+// past the tile's last row, gets an out-of-range offset and reads as zeros
+// (no memory access).  NK / NV windows cover a K / V tile.
+template <int D>
+struct DmaTile {
+  static constexpr int CPR = D / 8;                  // 16-byte chunks of a row
+  static constexpr int KP = CPR + 1, VP = CPR + 4;   // pitches in 16-byte slots
+  static constexpr int NK = (32 * KP + 63) / 64, NV = (32 * VP + 63) / 64;
+  static constexpr int NPT = NK + NV;                // windows per K + V tile pair
+  static constexpr uint32_t kOut = 0xFFFFFFF0u;      // an offset past any range
+  // byte offset in global memory of lane `lane`'s 16 bytes of window j of a
+  // K (is_k) or V tile whose rows are row_bytes apart
+  static __device__ __forceinline__ uint32_t voff(bool is_k, int j, int lane, uint32_t row_bytes) {
+    const int pitch = is_k ? KP : VP;
+    const int P = 64 * j + lane;
+    const int row = P / pitch, ch = P - row * pitch;
+    return (ch < CPR && row < 32) ? (uint32_t)row * row_bytes + (uint32_t)ch * 16u : kOut;
+  }
+  // One wave-wide load into the 1 KiB LDS window at byte address lds_byte.
+  // Written as asm so that the compiler's wait-count pass, which cannot tell
+  // one ring slot from another, does not make every later LDS read of the
+  // step wait for these loads: the loop waits for them itself, once, before
+  // the barrier that publishes the slots.  (vmcnt retires in order, so loads
+  // the compiler does not count only make its own waits stricter.)  The
+  // buffer descriptor is base, stride 0, num_records, and the flags word of
+  // make_rsrc; the voffset register is read at issue and stays live.
+  static __device__ __forceinline__ void load(const uint16_t* first_row, uint32_t num_records, uint32_t lds_byte,
+                                              uint32_t voffset) {
+    const uint64_t base = (uint64_t)(uintptr_t)first_row;
+    const u32x4 desc = {(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, num_records, 0x00020000u};
+    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(lds_byte), "v"(voffset), "s"(desc)
+                     : "m0");
+  }
+};
+
 struct NoExtra {
   __device__ __forceinline__ void operator()(int) const {}
 };
@@ -422,10 +463,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   constexpr int TB = TW * NW;       // tokens per workgroup
   static_assert(32 % G == 0, "a 32-row block must hold whole tokens");
 
-  // K/V ring: 8 slots without a window (four tiles per barrier), else 4
+  // K/V ring: 8 slots without a window (four tiles per barrier), else 4.
+  // Without a window the main loop fills the slots with direct-to-LDS loads
+  // in whole 1 KiB windows (one wave-wide 16-byte load each), so each slot
+  // is rounded up to whole windows; the tile layout inside is the same.
   constexpr int NS = NOWIN ? 8 : 4;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NS][Gm::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[NS][Gm::V_ELEMS];
+  using Dma = DmaTile<D>;
+  constexpr int KSLOT = NOWIN ? Dma::NK * 512 : Gm::K_ELEMS;
+  constexpr int VSLOT = NOWIN ? Dma::NV * 512 : Gm::V_ELEMS;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NS][KSLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[NS][VSLOT];
 
   // XCD-aware work item: workgroups on one XCD (blockIdx % 8) take consecutive
   // token blocks of one (b, g), latest (longest) first.
@@ -542,49 +589,64 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
     const uint32_t row_b = (uint32_t)(2 * kv_tok), pad_b = (uint32_t)(2 * (kv_tok - D));
     const uint16_t* kp = kg + (kt + 5) * tstride;
     const uint16_t* vp = vg + (kt + 4) * tstride;
-    Stager<D, NT> s2, s3;
-    s2.init(kv_tok, tid);
-    s3.init(kv_tok, tid);
-    // the step's loads issue one per score MFMA of the first two folds
-    // (MFMAs c0 .. c0 + 3 of the D / 16), the LDS stores one per score MFMA
-    // of the last four of the last two folds: the matrix core is busy
-    // meanwhile, and the slots they fill were last read in the previous step
-    static_assert(Gm::NC >= 4, "four loads or stores per fold");
-    constexpr int c0 = Gm::NC > 4 ? 1 : 0, c1 = Gm::NC - 4;
     using Stg = Stager<D, NT>;
+    // The step's K/V tiles for the next step, K(kt + 5 .. kt + 8) and V(kt +
+    // 4 .. kt + 7), go straight from memory into their LDS slots (last read
+    // in the previous step).  A K + V tile pair is NPT 1 KiB windows; wave
+    // wv fills windows wv, wv + NW, ... of every pair (the same windows each
+    // step, so its per-lane offsets are fixed), tile i's loads issued during
+    // fold i, one per score MFMA.  Nothing stages through registers and the
+    // only wait is at the step's end, a whole step after the loads issue.
+    constexpr int WPW = (Dma::NPT + NW - 1) / NW;   // windows per wave and tile pair (at most)
+    static_assert(WPW + 1 <= Gm::NC, "one load per score MFMA of a fold");
+    uint32_t dma_off[WPW], dma_lds[WPW];
+    bool dma_k[WPW], dma_on[WPW];
+#pragma unroll
+    for (int k = 0; k < WPW; ++k) {
+      const int rr = wv + NW * k;
+      dma_on[k] = rr < Dma::NPT;
+      dma_k[k] = rr < Dma::NK;
+      const int win = dma_k[k] ? rr : rr - Dma::NK;
+      dma_off[k] = dma_on[k] ? Dma::voff(dma_k[k], win, lane, row_b) : 0u;
+      dma_lds[k] = 1024u * (uint32_t)win;
+    }
+    const uint32_t k_ring0 = lds_addr(k_lds[0]), v_ring0 = lds_addr(v_lds[0]);
+    const uint32_t full_rec = (uint32_t)KT * row_b - pad_b;
     for (; kt < kt_end; kt += 4, kp += 4 * tstride, vp += 4 * tstride) {
       const int r = kt - kt_begin;
-      auto load_pair = [&](Stg& a, Stg& b, int i, int c, int cb) {  // K(kt+5+i), V(kt+4+i) into a; i+1 into b
-        if (c == cb && kt + 5 + i <= kt_end)
-          a.load_k(Stg::tile_at(kp + i * tstride, (kt + 5 + i) * KT, key_end, row_b, pad_b), tid);
-        if (c == cb + 1 && kt + 4 + i <= kt_end)
-          a.load_v(Stg::tile_at(vp + i * tstride, (kt + 4 + i) * KT, key_end, row_b, pad_b), tid);
-        if (c == cb + 2 && kt + 6 + i <= kt_end)
-          b.load_k(Stg::tile_at(kp + (i + 1) * tstride, (kt + 6 + i) * KT, key_end, row_b, pad_b), tid);
-        if (c == cb + 3 && kt + 5 + i <= kt_end)
-          b.load_v(Stg::tile_at(vp + (i + 1) * tstride, (kt + 5 + i) * KT, key_end, row_b, pad_b), tid);
+      // window k of tile pair i: K(kt + 5 + i) or V(kt + 4 + i)
+      auto dma = [&](int i, int k) {
+        if (!dma_on[k]) return;
+        const int t = kt + (dma_k[k] ? 5 : 4) + i;
+        if (t > kt_end) return;
+        const uint16_t* first = (dma_k[k] ? kp : vp) + i * tstride;
+        const uint32_t nrec = t * KT + KT <= key_end ? full_rec : (uint32_t)(key_end - t * KT) * row_b - pad_b;
+        const uint32_t slot = (uint32_t)((t - kt_begin) & 7);
+        const uint32_t lds = (dma_k[k] ? k_ring0 + slot * (uint32_t)(2 * KSLOT) : v_ring0 + slot * (uint32_t)(2 * VSLOT)) +
+                             dma_lds[k];
+        Dma::load(first, nrec, lds, dma_off[k]);
       };
-      auto store_pair = [&](const Stg& a, const Stg& b, int i, int c, int cb) {
-        if (c == cb && kt + 5 + i <= kt_end) a.store_k(k_lds[(r + 5 + i) & 7], tid);
-        if (c == cb + 1 && kt + 4 + i <= kt_end) a.store_v(v_lds[(r + 4 + i) & 7], tid);
-        if (c == cb + 2 && kt + 6 + i <= kt_end) b.store_k(k_lds[(r + 6 + i) & 7], tid);
-        if (c == cb + 3 && kt + 5 + i <= kt_end) b.store_v(v_lds[(r + 5 + i) & 7], tid);
+      auto issue = [&](int f, int c) {
+        if (c >= 1 && c <= WPW) dma(f, c - 1);
       };
       // within the step each fold reads the first K operands of the next
       // fold's tile ahead (all four tiles are resident since the barrier)
       bf16x8 kpre[QState<D>::KPRE];
       const f32x16 sa = st.template fold<true, false, true>(
           s, c2, v_lds[r & 7], k_lds[(r + 1) & 7], (kt + 1) * KT, tile_mask(kt + 1), W, half, lane,
-          [&](int c) { load_pair(s0, s1, 0, c, c0); }, kpre, k_lds[(r + 2) & 7]);
+          [&](int c) { issue(0, c); }, kpre, k_lds[(r + 2) & 7]);
       const f32x16 sb = st.template fold<true, true, true>(
           sa, c2, v_lds[(r + 1) & 7], k_lds[(r + 2) & 7], (kt + 2) * KT, tile_mask(kt + 2), W, half, lane,
-          [&](int c) { load_pair(s2, s3, 2, c, c0); }, kpre, k_lds[(r + 3) & 7]);
+          [&](int c) { issue(1, c); }, kpre, k_lds[(r + 3) & 7]);
       const f32x16 sc = st.template fold<true, true, true>(
           sb, c2, v_lds[(r + 2) & 7], k_lds[(r + 3) & 7], (kt + 3) * KT, tile_mask(kt + 3), W, half, lane,
-          [&](int c) { store_pair(s0, s1, 0, c, c1); }, kpre, k_lds[(r + 4) & 7]);
+          [&](int c) { issue(2, c); }, kpre, k_lds[(r + 4) & 7]);
       s = st.template fold<true, true, false>(sc, c2, v_lds[(r + 3) & 7], k_lds[(r + 4) & 7], (kt + 4) * KT,
-                                              tile_mask(kt + 4), W, half, lane,
-                                              [&](int c) { store_pair(s2, s3, 2, c, c1); }, kpre);
+                                              tile_mask(kt + 4), W, half, lane, [&](int c) { issue(3, c); },
+                                              kpre);
+      // every direct-to-LDS load of this wave has landed before the barrier
+      // that hands the slots to the other waves
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
     st.template fold<false>(s, c2, v_lds[(kt_end - kt_begin) & 7], nullptr, 0, 0, W, half, lane);
