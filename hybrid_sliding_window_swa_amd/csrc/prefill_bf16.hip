@@ -408,6 +408,139 @@ struct QState {
     return sn;
   }
 
+  // Fold of one tile whose rescale need is decided by its weights' sum (the
+  // no-window loop): P = exp2(s*c2 - mu) with the current shift, rounded to
+  // bf16, then this lane's sum of its 16 rounded weights.  A weight above
+  // 2^kRescaleTau forces that sum above it, so when no lane's sum exceeds it
+  // every weight is bounded as under the max-based rule, and no row max is
+  // needed: the check is one compare per lane before P V.  Otherwise (rare:
+  // a score well above the running shift) the tile's true row max is taken,
+  // the accumulator rescaled and the weights recomputed.  With NEXT the
+  // score MFMAs of the K tile k_next run between the exponentials, the next
+  // tile's mask is applied to them, and they are returned (raw).  `extra`,
+  // kpre and k_after as in fold.
+  template <bool NEXT, bool PRE_IN = false, bool PRE_OUT = false, typename X = NoExtra>
+  __device__ __forceinline__ f32x16 fold_sum(f32x16 s, float c2, const uint16_t* v_t, const uint16_t* k_next,
+                                             int kb_next, int mask_next, int window, int half, int lane,
+                                             const X& extra = X(), bf16x8* kpre = nullptr,
+                                             const uint16_t* k_after = nullptr) {
+    constexpr int EPM = 16 / Gm::NC;  // exponentials per score MFMA
+    constexpr int NPAIR = 8;          // packed weight pairs per tile
+    const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    f32x16 sn = {};
+    uint32_t pw[NPAIR];
+    float tsum = 0.0f;
+    bf16x8 va[2][Gm::ND];
+    if constexpr (NEXT) {
+      const lds_u16* kbase = lane_base(lds_addr(k_next), KTile<D>::k_lane_off(lane));
+      bf16x8 ka[Gm::NC];
+#pragma unroll
+      for (int c = 0; c < Gm::NC; ++c) ka[c] = (PRE_IN && c < KPRE) ? kpre[c] : KTile<D>::k_operand(kbase, c);
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db) va[0][db] = VTile<D>::vt_operand(vbase, db, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // group c: score MFMA c; pack the previous group's weights; add the
+      // pair packed one group earlier to the sum; this group's exponentials
+      float ex[EPM];
+#pragma unroll
+      for (int c = 0; c < Gm::NC; ++c) {
+        sn = mfma32(ka[c], q[c], sn);
+        if (c > 0) {
+#pragma unroll
+          for (int e = 0; e < EPM; e += 2) {
+            const bf16x2 w2 = {(__bf16)ex[e], (__bf16)ex[e + 1]};
+            uint32_t w = __builtin_bit_cast(uint32_t, w2);
+            __asm__ volatile("" : "+v"(w));
+            pw[((c - 1) * EPM + e) >> 1] = w;
+          }
+          if (c > 1) {
+#pragma unroll
+            for (int e = 0; e < EPM; e += 2) {
+              tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[((c - 2) * EPM + e) >> 1]), one,
+                                                     tsum, false);
+              __asm__ volatile("" : "+v"(tsum));
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < EPM; ++e) {
+          ex[e] = exp2_fast(fmaf(s[c * EPM + e], c2, -mu));
+          __asm__ volatile("" : "+v"(ex[e]));
+        }
+        extra(c);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int e = 0; e < EPM; e += 2) {
+        const bf16x2 w2 = {(__bf16)ex[e], (__bf16)ex[e + 1]};
+        pw[((Gm::NC - 1) * EPM + e) >> 1] = __builtin_bit_cast(uint32_t, w2);
+      }
+#pragma unroll
+      for (int c = Gm::NC - 2; c < Gm::NC; ++c)
+#pragma unroll
+        for (int e = 0; e < EPM; e += 2)
+          tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[(c * EPM + e) >> 1]), one, tsum, false);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < Gm::ND; ++db) va[kc][db] = VTile<D>::vt_operand(vbase, db, kc);
+#pragma unroll
+      for (int j = 0; j < NPAIR; ++j) {
+        const bf16x2 w2 = {(__bf16)exp2_fast(fmaf(s[2 * j], c2, -mu)), (__bf16)exp2_fast(fmaf(s[2 * j + 1], c2, -mu))};
+        pw[j] = __builtin_bit_cast(uint32_t, w2);
+        tsum = __builtin_amdgcn_fdot2_f32_bf16(w2, one, tsum, false);
+      }
+    }
+    if (wave_any(!(tsum <= exp2_fast(kRescaleTau)))) {
+      // a weight may exceed 2^tau (or be non-finite): shift by the tile's row max
+      float mx = kNegInf;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = __builtin_elementwise_maximum(mx, s[v]);
+      const float m_new = __builtin_elementwise_maximum(m_run, halves_max(mx) * c2);
+      const float alpha = m_run == kNegInf ? 0.0f : exp2_fast(m_run - m_new);
+      if (m_new > m_run) {
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < Gm::ND; ++db) acc[db] *= alpha;
+      }
+      mu = m_run == kNegInf ? 0.0f : m_run;
+      tsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NPAIR; ++j) {
+        const bf16x2 w2 = {(__bf16)exp2_fast(fmaf(s[2 * j], c2, -mu)), (__bf16)exp2_fast(fmaf(s[2 * j + 1], c2, -mu))};
+        pw[j] = __builtin_bit_cast(uint32_t, w2);
+        tsum = __builtin_amdgcn_fdot2_f32_bf16(w2, one, tsum, false);
+      }
+    }
+    l_run += tsum;
+    bf16x8 pb[2];
+    pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    pb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+    if constexpr (NEXT) {
+      apply_mask(sn, kb_next, mask_next, window, half);
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db) va[1][db] = VTile<D>::vt_operand(vbase, db, 1);
+    }
+    constexpr int NPV = 2 * Gm::ND;
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int kc = i / Gm::ND, db = i % Gm::ND;
+      acc[db] = mfma32(va[kc][db], pb[kc], acc[db]);
+      if constexpr (NEXT && PRE_OUT) {
+        if (i == 1) {
+          const lds_u16* abase = lane_base(lds_addr(k_after), KTile<D>::k_lane_off(lane));
+#pragma unroll
+          for (int c = 0; c < KPRE; ++c) kpre[c] = KTile<D>::k_operand(abase, c);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return sn;
+  }
+
   // Natural-log softmax denominator of each row, sink included, for the
   // backward: lse = (m + log2 l) * ln 2 (m and l share the lazy shift, so the
   // sum is exact whatever the shift).  lse_b points at [b][0][0] of [B, Sq, Hq].
@@ -576,8 +709,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
       const int r = kt - kt_begin;
       if (kt + 5 <= kt_end) s0.load_k(kg, kv_tok, (kt + 5) * KT, key_end, tid);
       if (kt + 4 <= kt_end) s0.load_v(vg, kv_tok, (kt + 4) * KT, key_end, tid);
-      s = st.template fold<true>(s, c2, v_lds[r & 7], k_lds[(r + 1) & 7], (kt + 1) * KT, tile_mask(kt + 1), W, half,
-                                 lane);
+      s = st.template fold_sum<true>(s, c2, v_lds[r & 7], k_lds[(r + 1) & 7], (kt + 1) * KT, tile_mask(kt + 1), W,
+                                     half, lane);
       if (kt + 5 <= kt_end) s0.store_k(k_lds[(r + 5) & 7], tid);
       if (kt + 4 <= kt_end) s0.store_v(v_lds[(r + 4) & 7], tid);
       __syncthreads();
@@ -632,16 +765,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
       // within the step each fold reads the first K operands of the next
       // fold's tile ahead (all four tiles are resident since the barrier)
       bf16x8 kpre[QState<D>::KPRE];
-      const f32x16 sa = st.template fold<true, false, true>(
+      const f32x16 sa = st.template fold_sum<true, false, true>(
           s, c2, v_lds[r & 7], k_lds[(r + 1) & 7], (kt + 1) * KT, tile_mask(kt + 1), W, half, lane,
           [&](int c) { issue(0, c); }, kpre, k_lds[(r + 2) & 7]);
-      const f32x16 sb = st.template fold<true, true, true>(
+      const f32x16 sb = st.template fold_sum<true, true, true>(
           sa, c2, v_lds[(r + 1) & 7], k_lds[(r + 2) & 7], (kt + 2) * KT, tile_mask(kt + 2), W, half, lane,
           [&](int c) { issue(1, c); }, kpre, k_lds[(r + 3) & 7]);
-      const f32x16 sc = st.template fold<true, true, true>(
+      const f32x16 sc = st.template fold_sum<true, true, true>(
           sb, c2, v_lds[(r + 2) & 7], k_lds[(r + 3) & 7], (kt + 3) * KT, tile_mask(kt + 3), W, half, lane,
           [&](int c) { issue(2, c); }, kpre, k_lds[(r + 4) & 7]);
-      s = st.template fold<true, true, false>(sc, c2, v_lds[(r + 3) & 7], k_lds[(r + 4) & 7], (kt + 4) * KT,
+      s = st.template fold_sum<true, true, false>(sc, c2, v_lds[(r + 3) & 7], k_lds[(r + 4) & 7], (kt + 4) * KT,
                                               tile_mask(kt + 4), W, half, lane, [&](int c) { issue(3, c); },
                                               kpre);
       // every direct-to-LDS load of this wave has landed before the barrier
@@ -649,7 +782,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    st.template fold<false>(s, c2, v_lds[(kt_end - kt_begin) & 7], nullptr, 0, 0, W, half, lane);
+    st.template fold_sum<false>(s, c2, v_lds[(kt_end - kt_begin) & 7], nullptr, 0, 0, W, half, lane);
   } else {
     if (wk0 == kt_begin && wk1 >= 0) {
       s = st.scores(k_lds[0], lane);
