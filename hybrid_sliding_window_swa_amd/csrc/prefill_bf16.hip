@@ -226,6 +226,7 @@ struct QState {
   // in the lower half of the wave).  sink2 = sink * log2(e), or -inf for none.
   __device__ __forceinline__ void reset(float sink2, int half) {
     m_run = sink2;
+    mu = sink2 == kNegInf ? 0.0f : sink2;
     l_run = (sink2 != kNegInf && half == 0) ? 1.0f : 0.0f;
 #pragma unroll
     for (int db = 0; db < Gm::ND; ++db) acc[db] = f32x16{};
@@ -495,18 +496,18 @@ struct QState {
     }
     if (wave_any(!(tsum <= exp2_fast(kRescaleTau)))) {
       // a weight may exceed 2^tau (or be non-finite): shift by the tile's row max
+      // (mu is the shift the accumulator and the sum are kept at: the
+      // running max, or 0 while that is still -inf)
       float mx = kNegInf;
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = __builtin_elementwise_maximum(mx, s[v]);
-      const float m_new = __builtin_elementwise_maximum(m_run, halves_max(mx) * c2);
-      const float alpha = m_run == kNegInf ? 0.0f : exp2_fast(m_run - m_new);
-      if (m_new > m_run) {
-        m_run = m_new;
-        l_run *= alpha;
+      // (alpha is exactly 1 where the shift does not move)
+      const float m_new = __builtin_elementwise_maximum(mu, halves_max(mx) * c2);
+      const float alpha = exp2_fast(mu - m_new);
+      l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < Gm::ND; ++db) acc[db] *= alpha;
-      }
-      mu = m_run == kNegInf ? 0.0f : m_run;
+      for (int db = 0; db < Gm::ND; ++db) acc[db] *= alpha;
+      mu = m_new;
       tsum = 0.0f;
 #pragma unroll
       for (int j = 0; j < NPAIR; ++j) {
@@ -542,13 +543,14 @@ struct QState {
   }
 
   // Natural-log softmax denominator of each row, sink included, for the
-  // backward: lse = (m + log2 l) * ln 2 (m and l share the lazy shift, so the
-  // sum is exact whatever the shift).  lse_b points at [b][0][0] of [B, Sq, Hq].
+  // backward: lse = (mu + log2 l) * ln 2, mu being the shift the accumulator
+  // and l are kept at (the running max, or 0 while that is -inf), so the sum
+  // is exact whatever the shift.  lse_b points at [b][0][0] of [B, Sq, Hq].
   __device__ __forceinline__ void store_lse(float* lse_b, int Hq, int tw0, int G, int g, int Sq, int col,
                                             int half) const {
     const float lt = halves_sum(l_run);
     const int tok = tw0 + col / G;
-    if (half == 0 && tok < Sq) lse_b[(long)tok * Hq + g * G + col % G] = (m_run + __builtin_amdgcn_logf(lt)) * kLn2;
+    if (half == 0 && tok < Sq) lse_b[(long)tok * Hq + g * G + col % G] = (mu + __builtin_amdgcn_logf(lt)) * kLn2;
   }
 
   // O = acc / l in bf16, one 8-byte store per 4 consecutive d.

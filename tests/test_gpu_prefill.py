@@ -99,6 +99,30 @@ def test_prefill_bf16_sink_modes(mode):
     assert_close(o, ref, BF16_TOL, cfg.name)
 
 
+@pytest.mark.parametrize("W,G,with_sink", [(128, 8, False), (128, 8, True), (96, 4, False), (512, 8, False),
+                                           (0, 8, False), (0, 8, True), (0, 2, False)])
+def test_prefill_bf16_large_scores(W, G, with_sink):
+    """Queries scaled by 8 (exact in bf16): scores far above the running
+    shift keep arriving, so the kernels' rescale path (raising the shift,
+    rescaling the accumulator, recomputing the tile's weights) runs often,
+    also while no sink has fixed the shift yet.  Output and saved LSE
+    against the oracle."""
+    dev = device()
+    m = swa()
+    cfg = _cfg(f"large_scores_w{W}_g{G}_{int(with_sink)}", 1, 300, 16, 16 // G, 128, W, "bf16", Sk=332)
+    q, k, v, sinks = prefill_inputs(cfg)
+    q = q * 8
+    sinks = sinks if with_sink else None
+    sd = None if sinks is None else sinks.to(dev)
+    o = m.swa_attn_prefill(q.to(dev), k.to(dev), v.to(dev), sd, W, cfg.q_offset, cfg.scale)
+    o2, lse = m.swa_attn_prefill_lse(q.to(dev), k.to(dev), v.to(dev), sd, W, cfg.q_offset, cfg.scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q, k, v, sinks, W, cfg.q_offset, cfg.scale, want_lse=True)
+    assert_close(o, ref["o"], BF16_TOL, cfg.name)
+    assert_close(o2, ref["o"], BF16_TOL, cfg.name + " (lse variant)")
+    assert np.abs(lse.cpu().numpy() - ref["lse"]).max() <= 2 * 2.0 ** -9
+
+
 def test_prefill_chunked_equals_oracle():
     """Chunked prefill (queries [c0, c0 + C) over the full K/V with q_offset = c0)."""
     dev = device()
