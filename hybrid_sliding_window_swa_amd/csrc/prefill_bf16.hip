@@ -873,8 +873,12 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
   constexpr int SIT = 32 * HC / 64;  // 16-byte chunks per lane per staged half
   using Stg = PadTile<HD, HD + 8>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_ring[NR][Gm::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_ring[NR][Gm::V_ELEMS];
+  // ring slots rounded up to whole 1 KiB windows of direct-to-LDS loads
+  // (each block's new tile arrives that way); the tile layout inside is
+  // that of KTile / VTile
+  using Dma = DmaTile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t k_ring[NR][Dma::NK * 512];
+  __shared__ __attribute__((aligned(16))) uint16_t v_ring[NR][Dma::NV * 512];
   __shared__ __attribute__((aligned(16))) uint16_t stage_lds[NW][Stg::ELEMS];
   // rotary embedding of the queries: cos / sin of (token, pair) for a wave's
   // TW tokens (entry tok * 32 + i), and of the turn by one block (TB tokens)
@@ -1071,14 +1075,44 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  // The next block's (at most one) new K/V tile goes straight from memory
+  // into its ring slot: a K + V tile pair is NPT 1 KiB windows, wave wv
+  // filling windows wv, wv + NW, ... (per-lane offsets fixed per wave).  The
+  // slot held tile new_kt - NR, older than this block's window and the last
+  // block's (read before the last barrier).
+  constexpr int WPW = (Dma::NPT + NW - 1) / NW;
+  const uint32_t row_b = (uint32_t)(2 * kv_tok), pad_b = (uint32_t)(2 * (kv_tok - D));
+  uint32_t dma_off[WPW];
+#pragma unroll
+  for (int k = 0; k < WPW; ++k) {
+    const int rr = wv + NW * k;
+    dma_off[k] = rr < Dma::NPT ? Dma::voff(rr < Dma::NK, rr < Dma::NK ? rr : rr - Dma::NK, lane, row_b) : 0u;
+  }
+  auto dma_tile = [&](int t) {
+    const uint16_t* kfirst = kg + (long)t * KT * kv_tok;
+    const uint16_t* vfirst = vg + (long)t * KT * kv_tok;
+    const uint32_t nrec = (uint32_t)min(KT, key_end - t * KT) * row_b - pad_b;
+#pragma unroll
+    for (int k = 0; k < WPW; ++k) {
+      const int rr = wv + NW * k;
+      if (rr < Dma::NK)
+        Dma::load(kfirst, nrec, lds_addr(k_ring[t % NR]) + 1024u * rr, dma_off[k]);
+      else if (rr < Dma::NPT)
+        Dma::load(vfirst, nrec, lds_addr(v_ring[t % NR]) + 1024u * (rr - Dma::NK), dma_off[k]);
+    }
+  };
+
   for (int blk = blk0; blk < blk1; ++blk) {
     const int tw0 = blk * TB + wv * TW;
     const bool nxt = blk + 1 < blk1;
-    // prefetch: next block's queries and (at most one) new K/V tile
+    // prefetch: (at most one) new K/V tile, then the next block's queries.
+    // The tile's loads are older than the query loads, and vmcnt retires in
+    // order, so the wait for the queries before they are staged (at the
+    // block's end, before the barrier) also covers the tile.
     const int new_kt = nxt ? kt_hi(blk + 1) : -1;
     const bool have_new = new_kt > loaded_hi;
+    if (have_new) dma_tile(new_kt);
     if (nxt) load_q_rows(tw0 + TB);
-    if (have_new) sg.load(kg, vg, kv_tok, new_kt * KT, key_end, tid);
 
     // compute this block from the ring; the second wave of each SIMD pair
     // at a raised priority while the tiles are folded (see the
@@ -1104,25 +1138,29 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
       // sets, so none is copied back to close the loop
       int kt = wk0;
       for (; kt + 1 < wk1; kt += 2) {
-        const f32x16 s1 = st.template fold<true>(s, p.scale_log2, v_ring[kt % NR], k_ring[(kt + 1) % NR],
-                                                 (kt + 1) * KT, tile_mask(kt + 1), W, half, lane);
-        s = st.template fold<true>(s1, p.scale_log2, v_ring[(kt + 1) % NR], k_ring[(kt + 2) % NR], (kt + 2) * KT,
-                                   tile_mask(kt + 2), W, half, lane);
+        const f32x16 s1 = st.template fold_sum<true>(s, p.scale_log2, v_ring[kt % NR], k_ring[(kt + 1) % NR],
+                                                     (kt + 1) * KT, tile_mask(kt + 1), W, half, lane);
+        s = st.template fold_sum<true>(s1, p.scale_log2, v_ring[(kt + 1) % NR], k_ring[(kt + 2) % NR],
+                                       (kt + 2) * KT, tile_mask(kt + 2), W, half, lane);
       }
       if (kt < wk1)
-        s = st.template fold<true>(s, p.scale_log2, v_ring[kt % NR], k_ring[(kt + 1) % NR], (kt + 1) * KT,
-                                   tile_mask(kt + 1), W, half, lane);
-      st.template fold<false>(s, p.scale_log2, v_ring[wk1 % NR], nullptr, 0, 0, W, half, lane);
+        s = st.template fold_sum<true>(s, p.scale_log2, v_ring[kt % NR], k_ring[(kt + 1) % NR], (kt + 1) * KT,
+                                       tile_mask(kt + 1), W, half, lane);
+      st.template fold_sum<false>(s, p.scale_log2, v_ring[wk1 % NR], nullptr, 0, 0, W, half, lane);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (have_new) loaded_hi = new_kt;
+    // the next block's queries into their operand registers first (their
+    // wait then covers only loads: no output store has been issued yet),
+    // then this block's output, through the same staging tile
+    if (nxt) stage_q(tw0 + TB, ((blk + 1 - blk0) & 7) == 0);
+    if (wave_active) {
       store_o_rows(tw0);
       if constexpr (MODE == kStripLse) st.store_lse(p.lse + (long)b * p.Sq * p.Hq, p.Hq, tw0, G, g, p.Sq, col, half);
     }
-    __builtin_amdgcn_s_setprio(0);
-    // the new tile's slot held tile new_kt - NR, older than this block's window
-    if (have_new) {
-      sg.store(k_ring[new_kt % NR], v_ring[new_kt % NR], tid);
-      loaded_hi = new_kt;
-    }
-    if (nxt) stage_q(tw0 + TB, ((blk + 1 - blk0) & 7) == 0);
+    // When a new tile was loaded, the query loads came after it and were
+    // waited for before staging, so the tile has landed in every wave's
+    // share by this barrier.
     __syncthreads();
   }
 }
