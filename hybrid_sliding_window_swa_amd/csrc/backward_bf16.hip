@@ -117,17 +117,6 @@ __global__ __launch_bounds__(256) void bwd_sink_reduce_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-// Per-lane MFMA operand of a 32-row, row-major global tile: lane (col, half)
-// gets row col, d in [16c + 8 half, +8); rows past `rows` read as zeros.
-template <int D>
-__device__ __forceinline__ void load_rows_operand(bf16x8 (&x)[D / 16], const uint16_t* base, long row_stride,
-                                                  int rows, int col, int half) {
-  const rsrc_t r = make_rsrc(base, rows > 0 ? (uint32_t)(((rows - 1) * row_stride + D) * 2) : 0u);
-  const uint32_t voff = (uint32_t)((col * row_stride + half * 8) * 2);
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) x[c] = __builtin_bit_cast(bf16x8, buf_load16(r, voff + c * 32, 0));
-}
-
 template <int D, int G, int PF, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
   using Gm = BwdGeom<D>;
@@ -138,6 +127,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t o_lds[2][Gm::ELEMS];  // dO
   __shared__ float lse_lds[2][BKT];
   __shared__ float del_lds[2][BKT];
+  // each wave's 32 K and V rows, read as MFMA B operands for every query
+  // block (held in LDS rather than in 64 registers, which the allocator
+  // otherwise shuttles through accumulation registers every block)
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[NW][2][KTile<D>::ELEMS];
 
   // work item: (b, g, block of NW key tiles).  Workgroups are dealt to the 8
   // XCDs in turn; each XCD takes a contiguous range of work items, i.e.
@@ -160,14 +153,25 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
   const int kb = kb0 + wv * BKT;              // first key of this wave
   const int key = kb + col;                   // this lane's key column
 
-  // this wave's K and V rows as B operands
-  bf16x8 kop[Gm::NC], vop[Gm::NC];
+  // this wave's K and V rows into its LDS tiles (whole rows; rows past Sk
+  // read as zeros), read back as B operands in every query block
   {
     const long kvbase = ((long)b * a.Sk + kb) * kv_tok + (long)g * D;
-    const int rows = min(BKT, a.Sk - kb);
-    load_rows_operand<D>(kop, a.k + kvbase, kv_tok, rows, col, half);
-    load_rows_operand<D>(vop, a.v + kvbase, kv_tok, rows, col, half);
+    const int rows = kb < a.Sk ? min(BKT, a.Sk - kb) : 0;
+    const uint32_t bytes = rows > 0 ? (uint32_t)(((rows - 1) * kv_tok + D) * 2) : 0u;
+    const rsrc_t rk = make_rsrc(a.k + kvbase, bytes), rv = make_rsrc(a.v + kvbase, bytes);
+    constexpr int CPR_ = D / 8, IT_ = BKT * CPR_ / 64;
+#pragma unroll
+    for (int i = 0; i < IT_; ++i) {
+      const int c = lane + 64 * i;
+      const uint32_t off = (uint32_t)(((c / CPR_) * kv_tok + (c % CPR_) * 8) * 2);
+      const u32x4 kx = buf_load16(rk, off, 0), vx = buf_load16(rv, off, 0);
+      *(u32x4*)&kv_lds[wv][0][KTile<D>::off(c / CPR_, (c % CPR_) * 8)] = kx;
+      *(u32x4*)&kv_lds[wv][1][KTile<D>::off(c / CPR_, (c % CPR_) * 8)] = vx;
+    }
   }
+  const lds_u16* kop_base = lane_base(lds_addr(kv_lds[wv][0]), KTile<D>::k_lane_off(lane));
+  const lds_u16* vop_base = lane_base(lds_addr(kv_lds[wv][1]), KTile<D>::k_lane_off(lane));
   f32x16 dk[Gm::ND], dv[Gm::ND];
 #pragma unroll
   for (int db = 0; db < Gm::ND; ++db) {
@@ -254,8 +258,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int c = 0; c < Gm::NC; ++c) {
-      s = mfma32(Tile::k_operand(qa, c), kop[c], s);
-      dp = mfma32(Tile::k_operand(oa, c), vop[c], dp);
+      s = mfma32(Tile::k_operand(qa, c), KTile<D>::k_operand(kop_base, c), s);
+      dp = mfma32(Tile::k_operand(oa, c), KTile<D>::k_operand(vop_base, c), dp);
     }
     // P, dS (masked entries exactly zero), rounded to bf16 B operands
     const bool edge = !(kb + BKT - 1 <= i_lo && (W <= 0 || kb > i_hi - W)) || i_hi < a.q_offset + t0 + TQ - 1;
