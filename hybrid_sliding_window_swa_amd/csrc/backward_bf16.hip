@@ -58,7 +58,11 @@ template <int D>
 struct BwdGeom {
   static constexpr int NC = D / 16;   // 16-wide chunks of a D contraction
   static constexpr int ND = D / 32;   // 32-row blocks of d in a D x 32 result
-  using Tile = VTile<D>;              // pitch D + 32: transposed reads conflict-free
+  // Tiles read both ways (16-byte row reads as MFMA operands, and
+  // ds_read_b64_tr_b16): pitch D + 24, an odd number of 16-byte slots, keeps
+  // the row reads conflict-free (D + 32 puts rows 0, 4, 8, 12 on one bank
+  // group) at two-way conflicts on some transposed reads; measured faster.
+  using Tile = PadTile<D, D + 24>;
   static constexpr int ELEMS = Tile::ELEMS;
   static constexpr int CH = BKT * D / 8;  // 16-byte chunks of a 32-row tile
 };
