@@ -132,6 +132,8 @@ swa_status_t swa_attn_backward(const void* q, const void* k, const void* v, cons
   a.dsink = dsink;
   a.delta = (float*)workspace;
   a.sink_part = (float*)((char*)workspace + plan.delta_bytes);
+  a.part = plan.part_bytes ? (float*)((char*)workspace + plan.part_offset) : nullptr;
+  a.part_bytes = plan.part_bytes;
   a.B = B;
   a.Sq = Sq;
   a.Sk = Sk;

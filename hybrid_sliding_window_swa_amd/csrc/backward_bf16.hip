@@ -13,6 +13,11 @@
 // (the sink adds exp(sink) to the denominator and carries no value).
 //
 // Kernels
+//   * bwd_fused_swa (sliding windows, D = 128, G in {4, 8}, q_offset a
+//     multiple of 32 / G): dQ, dK, dV and the dsink partials in one pass per
+//     query strip, see its section below; bwd_fuse_fixup adds the two
+//     strips' partials of shared key tiles.  Other shapes use the split
+//     kernels:
 //   * dQ, launched first.  Besides dQ it writes D_i = <dO_i, O_i> for its
 //     rows (read by the dK/dV kernel) and, per workgroup or strip and head,
 //     the partial sum of exp(sink - LSE) D in a fixed order;
@@ -26,8 +31,8 @@
 //     loaded whole and turned into operands through LDS, the tile loop
 //     software-pipelined); other shapes use bwd_dq (one workgroup per block,
 //     the forward's structure).
-//   * bwd_dkdv: KV-parallel.  A wave owns 32 keys of one KV head and keeps
-//     their K and V rows as MFMA B operands in registers; the workgroup's
+//   * bwd_dkdv: KV-parallel.  A wave owns 32 keys of one KV head and reads
+//     their K and V rows as MFMA B operands from its LDS tile; the workgroup's
 //     waves walk the query blocks that see any of their keys, staged through
 //     a double-buffered LDS tile.  Scores are computed as S = Q K^T, so a
 //     lane holds one key's column and 16 query rows: P and dS are then
@@ -846,6 +851,532 @@ __global__ __launch_bounds__(256) void bwd_dq_strip_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- fused, sliding window
+// dQ, dK, dV and the sink gradient of a sliding window in one pass over a
+// strip of query blocks (the split kernels above read q and dO twice and
+// compute S and dP twice).  One workgroup per (b, g, strip) of 8 waves:
+//   * key waves 0..4: 32-key tile t belongs to wave t % 5 while it is live
+//     (some query of the current block sees it); the wave keeps the tile's
+//     dK^T and dV^T in its accumulators and, per block, computes S = Q K^T,
+//     P, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS (the dK/dV kernel's
+//     scheme) and leaves dS^T in LDS.  A window of W <= ~130 keys plus a
+//     block of 32/G tokens meets at most five tiles, so every live tile has
+//     its wave.  When a tile stops being live its dK, dV are written: in
+//     bf16 when no other strip's queries see it, else as an fp32 partial
+//     that bwd_fuse_fixup adds to the neighbouring strip's (fixed order).
+//   * waves 5..7, one block behind: dQ^T = sum over the block's tiles of
+//     K^T dS^T (D blocks 0 | 1 | 2, 3), with K^T and dS^T read transposed
+//     from LDS; waves 5, 6 also stage the next block's q and dO rows into
+//     LDS (direct-to-LDS loads) and form its D_i = <dO_i, O_i> and LSE from
+//     global memory, wave 7 stages arriving K/V tiles.
+// LDS: K tiles in six slots (the live tiles of the block computed, of the
+// block whose dQ is formed, and the arriving one), V tiles likewise, q and
+// dO double-buffered, dS^T per key wave double-buffered.  The 32 x 128 K,
+// q and dO tiles are unpadded with XOR-swizzled 16-byte chunks (SwzTile),
+// which keeps both their row reads and their transposed reads
+// conflict-free within the 160 KiB.
+constexpr int kFuseKeyWaves = 5;
+constexpr int kFuseWaves = 8;
+constexpr int kFuseSlots = 6;
+constexpr int kFuseMinStrip = 512;         // tokens per strip at least
+constexpr int kFuseMaxBoundaries = 256;    // strip boundaries per launch at most
+constexpr int kFuseMaxBoundaryTiles = 5;   // tiles two strips share at most
+
+// 32 rows x 128 bf16, rows of 256 bytes, 16-byte chunk c of row r stored at
+// chunk c ^ swz(r), swz(r) = 4 (r % 4) + (r / 4) % 4.  A 16-byte operand read
+// (16 consecutive rows, one chunk per clock group) meets 16 distinct chunks;
+// a ds_read_b64_tr_b16 (4 consecutive rows x 64 bytes per 32 lanes) meets
+// four distinct 64-byte bank groups.  Tile bases are 256-byte aligned, so a
+// per-lane part can be XORed with compile-time chunk offsets.
+struct SwzTile {
+  static constexpr int BYTES = 32 * 256;
+  static __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+  // 16-byte operand read of chunk pair c (d in [16c + 8 half, +8)) by lane
+  // (row lane % 32, half lane / 32): tile + (kop(lane) ^ 32 c)
+  static __device__ __forceinline__ uint32_t kop(int lane) {
+    const int r = lane & 31, h = lane >> 5;
+    return (uint32_t)(r * 256 + 16 * (h ^ swz(r)));
+  }
+  // transposed read (PadTile::vt_operand's lane pattern) of rows
+  // 16 kc + 8 hh + ..., output block db: tile + (tro(lane, hh) ^ 64 db) + 4096 kc
+  static __device__ __forceinline__ uint32_t tro(int lane, int hh) {
+    const int s = lane & 15, g4 = (lane >> 4) & 1, h = lane >> 5;
+    const int row = 8 * hh + 4 * h + (s >> 2);
+    const int unit = (2 * g4 + ((s & 3) >> 1)) ^ (2 * hh + h);
+    return (uint32_t)(row * 256 + 64 * (s >> 2) + 16 * unit + 8 * (s & 1));
+  }
+  // global byte offset of the 16 bytes that DMA window i (rows 4i .. 4i+3)
+  // delivers to lane `lane`, for rows row_off(r) bytes into the source
+  static __device__ __forceinline__ int dma_chunk(int i, int lane) {
+    return (lane & 15) ^ (((lane >> 4) << 2) | (i & 3));
+  }
+};
+
+// dS^T tile per key wave: 32 keys x 32 queries bf16, rows of 64 bytes whose
+// 8-byte units u sit at u ^ ((key / 4) % 8): the key waves' 8-byte row writes
+// and the dQ waves' transposed reads are both conflict-free.
+struct DsTile {
+  static constexpr int BYTES = 32 * 64;
+  // byte offset of the four queries 8 j + 4 half .. +3 of key row `key`
+  static __device__ __forceinline__ uint32_t wr(int key, int half, int j) {
+    return (uint32_t)(key * 64 + 8 * ((2 * j + half) ^ ((key >> 2) & 7)));
+  }
+  // transposed read of key rows 16 kc + 8 hh + ...: tile + ((tro(lane, hh) ^ 32 kc) + 1024 kc)
+  static __device__ __forceinline__ uint32_t tro(int lane, int hh) {
+    const int s = lane & 15, g4 = (lane >> 4) & 1, h = lane >> 5;
+    const int row = 8 * hh + 4 * h + (s >> 2);
+    return (uint32_t)(row * 64 + 8 * ((4 * g4 + (s & 3)) ^ (2 * hh + h)));
+  }
+};
+
+__device__ __forceinline__ bf16x8 lds_rd16(uint32_t addr) { return *(const lds_bf16x8*)(uintptr_t)addr; }
+__device__ __forceinline__ bf16x8 lds_tr16(uint32_t lo, uint32_t hi) {
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)lo);
+  const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)hi);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Block n of the strip holds query tokens n*TQ .. n*TQ + TQ - 1 (q_offset is
+// a multiple of TQ, so blocks are aligned in position).  Its live key tiles:
+__device__ __forceinline__ int fuse_lo(const BwdArgs& a, int n, int TQ) {
+  return max(0, a.q_offset + n * TQ - a.window + 1) / BKT;
+}
+__device__ __forceinline__ int fuse_hi(const BwdArgs& a, int n, int TQ) {
+  return min(a.q_offset + n * TQ + TQ - 1, a.Sk - 1) / BKT;
+}
+// first key tile strip boundary j shares, and its position (the first query
+// position of strip j + 1)
+__device__ __forceinline__ int fuse_bpos(const BwdArgs& a, int j, int TQ) {
+  const int nb = (a.Sq + TQ - 1) / TQ;
+  return a.q_offset + (int)((long)(j + 1) * nb / a.fuse_spb) * TQ;
+}
+
+template <int G>
+__global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs a) {
+  constexpr int D = 128;
+  constexpr int TQ = BKT / G;
+  constexpr int NKW = kFuseKeyWaves, NS = kFuseSlots;
+  constexpr int VCH = D / 8 + 1;                   // V rows: pitch D + 8 (17 slots of 16 bytes)
+  constexpr int NVI = (BKT * VCH + 63) / 64;       // direct-to-LDS loads per V tile
+  constexpr uint32_t kOut = 0xFFFFFFF0u;           // an offset past any buffer range
+  using VT = KTile<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[NS][SwzTile::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NS][NVI * 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_lds[2][SwzTile::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t o_lds[2][SwzTile::BYTES];  // dO
+  __shared__ __attribute__((aligned(1024))) uint8_t ds_lds[2][NKW][DsTile::BYTES];
+  __shared__ float lse_lds[2][BKT];   // LSE * log2(e) per block row
+  __shared__ float del_lds[2][BKT];   // D = <dO, O> per block row
+  __shared__ float sink_red[BKT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_index();
+  const int half = lane >> 5, col = lane & 31;
+  const int spb = a.fuse_spb;
+  const int bg = blockIdx.x / spb, sidx = blockIdx.x - bg * spb;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int nb = (a.Sq + TQ - 1) / TQ;
+  const int n0 = (int)((long)sidx * nb / spb), n1 = (int)((long)(sidx + 1) * nb / spb);
+  const long q_tok = (long)a.Hq * D, kv_tok = (long)a.Hkv * D;
+  const int W = a.window;
+  const float c2 = a.scale_log2;
+
+  // keys no query sees: zeros (the first strip below its first tile, the last
+  // strip above its last one)
+  {
+    const int kz_lo = sidx == 0 ? 0 : a.Sk;
+    const int kz_hi = sidx == 0 ? min(a.Sk, BKT * fuse_lo(a, 0, TQ)) : a.Sk;
+    const int kz2 = sidx == spb - 1 ? min(a.Sk, BKT * (fuse_hi(a, nb - 1, TQ) + 1)) : a.Sk;
+    const long kvb = (long)b * a.Sk * kv_tok + (long)g * D;
+    for (int i = tid; i < (kz_hi - kz_lo) * (D / 8); i += kFuseWaves * 64) {
+      const long off = kvb + (long)(kz_lo + i / (D / 8)) * kv_tok + (i % (D / 8)) * 8;
+      *(u32x4*)(a.dk + off) = u32x4{};
+      *(u32x4*)(a.dv + off) = u32x4{};
+    }
+    for (int i = tid; i < (a.Sk - kz2) * (D / 8); i += kFuseWaves * 64) {
+      const long off = kvb + (long)(kz2 + i / (D / 8)) * kv_tok + (i % (D / 8)) * 8;
+      *(u32x4*)(a.dk + off) = u32x4{};
+      *(u32x4*)(a.dv + off) = u32x4{};
+    }
+  }
+  if (n0 >= n1) return;
+
+  // ---- staging (direct-to-LDS loads; the loop's s_waitcnt + barrier publish them)
+  // q or dO rows of block n: row m is (token n*TQ + m / G, head g*G + m % G)
+  auto dma_rows = [&](const uint16_t* src, uint32_t tile, int n) {
+    const int t0 = n * TQ;
+    const int ntok = min(TQ, a.Sq - t0);
+    const uint16_t* first = src + ((long)b * a.Sq + t0) * q_tok + (long)g * G * D;
+    const uint32_t bytes = (uint32_t)(((ntok - 1) * q_tok + (long)G * D) * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const uint32_t voff = (uint32_t)((((r / G) * q_tok + (long)(r % G) * D) * 2) + 16 * SwzTile::dma_chunk(i, lane));
+      lds_dma16(first, bytes, tile + 1024u * i, voff);
+    }
+  };
+  // K and V tile t (8 + NVI windows); this wave issues windows w0, w0 + step, ...
+  auto dma_kv = [&](int t, int w0, int step) {
+    const int kb = t * BKT;
+    const int rows = min(BKT, a.Sk - kb);
+    const long off = ((long)b * a.Sk + kb) * kv_tok + (long)g * D;
+    const uint32_t bytes = (uint32_t)(((rows - 1) * kv_tok + D) * 2);
+    for (int i = w0; i < 8 + NVI; i += step) {
+      if (i < 8) {
+        const int r = 4 * i + (lane >> 4);
+        const uint32_t voff = (uint32_t)(r * kv_tok * 2) + 16u * SwzTile::dma_chunk(i, lane);
+        lds_dma16(a.k + off, bytes, lds_addr(k_lds[t % NS]) + 1024u * i, voff);
+      } else {
+        const int P = 64 * (i - 8) + lane;
+        const int r = P / VCH, ch = P - r * VCH;
+        const uint32_t voff = (ch < D / 8 && r < BKT) ? (uint32_t)(r * kv_tok * 2) + 16u * ch : kOut;
+        lds_dma16(a.v + off, bytes, lds_addr(v_lds[t % NS]) + 1024u * (i - 8), voff);
+      }
+    }
+  };
+
+  // ---- D = <dO, O> and LSE of block n (waves 5, 6: 16 rows each, four lanes per row)
+  const int drow = 16 * (wv - 5) + (lane >> 2), dq4 = lane & 3;
+  const float sink_h = (a.sinks && wv >= 5 && wv < 7) ? a.sinks[g * G + drow % G] : 0.0f;
+  float sterm = 0.0f;
+  struct DRows {
+    u32x4 o[4], d[4];
+    float lse;
+  };
+  auto d_load = [&](DRows& r, int n) {
+    const int t0 = n * TQ;
+    const int ntok = min(TQ, a.Sq - t0);
+    const long base = ((long)b * a.Sq + t0) * q_tok + (long)g * G * D;
+    const uint32_t bytes = (uint32_t)(((ntok - 1) * q_tok + (long)G * D) * 2);
+    const rsrc_t ro = make_rsrc(a.o + base, bytes), rd = make_rsrc(a.dout + base, bytes);
+    const uint32_t off = (uint32_t)((((drow / G) * q_tok + (long)(drow % G) * D) + 32 * dq4) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r.o[i] = buf_load16(ro, off + 16u * i, 0);
+      r.d[i] = buf_load16(rd, off + 16u * i, 0);
+    }
+    const rsrc_t rl = make_rsrc(a.lse + ((long)b * a.Sq + t0) * a.Hq + g * G, (uint32_t)(((ntok - 1) * a.Hq + G) * 4));
+    r.lse = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+        rl, (int)(((drow / G) * a.Hq + drow % G) * 4), 0, 0));
+  };
+  auto d_finish = [&](const DRows& r, int n) {
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      part = dot_bf16x8(__builtin_bit_cast(bf16x8, r.d[i]), __builtin_bit_cast(bf16x8, r.o[i]), part);
+    part += __shfl_xor(part, 1);
+    part += __shfl_xor(part, 2);
+    if (dq4 == 0) {
+      lse_lds[n & 1][drow] = r.lse * kLog2e;
+      del_lds[n & 1][drow] = part;
+      if (a.sinks && n * TQ + drow / G < a.Sq) sterm += __expf(sink_h - r.lse) * part;
+    }
+  };
+
+  // ---- key waves
+  const uint32_t kop = SwzTile::kop(lane);
+  const uint32_t tro0 = SwzTile::tro(lane, 0), tro1 = SwzTile::tro(lane, 1);
+  const uint32_t vop = VT::k_lane_off(lane);
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+  auto key_block = [&](int n, int t) {
+    const int buf = n & 1;
+    const uint32_t qT = lds_addr(q_lds[buf]), oT = lds_addr(o_lds[buf]);
+    const uint32_t qa = qT + kop, oa = oT + kop, ka = lds_addr(k_lds[t % NS]) + kop;
+    const uint32_t va = lds_addr(v_lds[t % NS]) + vop;
+    // S = Q K^T: lane (col = key), registers = query rows c_row(v, half)
+    f32x16 s = {};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s = mfma32(lds_rd16(qa ^ (32u * c)), lds_rd16(ka ^ (32u * c)), s);
+    const int pos0 = a.q_offset + n * TQ;
+    const int kb = t * BKT, key = kb + col;
+    const int i_hi = min(pos0 + TQ, a.q_offset + a.Sq) - 1;
+    const bool edge = !(kb + BKT - 1 <= pos0 && kb > i_hi - W) || i_hi < pos0 + TQ - 1 || kb + BKT > a.Sk;
+    // the LSE and D of rows c_row(v, half): four runs of four rows, one
+    // 16-byte read each
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      l4[j] = ((const lds_f32x4*)lse_lds[buf])[2 * j + half];
+      d4[j] = ((const lds_f32x4*)del_lds[buf])[2 * j + half];
+    }
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[v] = exp2_fast(fmaf(s[v], c2, -l4[v >> 2][v & 3]));
+    if (edge) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = pos0 + c_row(v, half) / G;
+        const bool ok = key <= i && key > i - W && i <= i_hi && key < a.Sk;
+        p[v] = ok ? p[v] : 0.0f;
+      }
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) pb[v >> 3][v & 7] = (__bf16)p[v];
+    // dP = dO V^T, and dV^T += dO^T P
+    f32x16 dp = {};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dp = mfma32(lds_rd16(oa ^ (32u * c)), lds_rd16(va + 32u * c), dp);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        dv[db] = mfma32(lds_tr16(oT + ((tro0 ^ (64u * db)) + 4096u * kc), oT + ((tro1 ^ (64u * db)) + 4096u * kc)),
+                        pb[kc], dv[db]);
+    // dS = P (dP - D), and dS^T into this wave's LDS tile for dQ
+    bf16x8 sb[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sb[v >> 3][v & 7] = (__bf16)(p[v] * (dp[v] - d4[v >> 2][v & 3]));
+    const uint32_t dsT = lds_addr(ds_lds[buf][t % NKW]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 w4 = __builtin_bit_cast(u32x4, sb[j >> 1]);
+      const u32x2 x2 = (j & 1) ? u32x2{w4[2], w4[3]} : u32x2{w4[0], w4[1]};
+      *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(dsT + DsTile::wr(col, half, j)) = x2;
+    }
+    // dK^T += Q^T dS
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        dk[db] = mfma32(lds_tr16(qT + ((tro0 ^ (64u * db)) + 4096u * kc), qT + ((tro1 ^ (64u * db)) + 4096u * kc)),
+                        sb[kc], dk[db]);
+  };
+  // tile t is done: bf16 dK, dV when only this strip sees it, else an fp32
+  // partial for bwd_fuse_fixup (side 0: the earlier strip of the boundary)
+  const int P0 = a.q_offset + n0 * TQ, P1 = a.q_offset + n1 * TQ;
+  auto key_flush = [&](int t) {
+    const int kb = t * BKT, key = kb + col;
+    int side = -1, j = 0;
+    if (sidx > 0 && kb <= P0 - 1) {
+      side = 1;
+      j = sidx - 1;
+    } else if (sidx < spb - 1 && kb + BKT - 1 >= max(0, P1 - W + 1)) {
+      side = 0;
+      j = sidx;
+    }
+    if (side < 0) {
+      if (key < a.Sk) {
+        uint16_t* dkp = a.dk + ((long)b * a.Sk + key) * kv_tok + (long)g * D;
+        uint16_t* dvp = a.dv + ((long)b * a.Sk + key) * kv_tok + (long)g * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const f32x4 yk = {dk[db][4 * a4] * a.scale, dk[db][4 * a4 + 1] * a.scale, dk[db][4 * a4 + 2] * a.scale,
+                              dk[db][4 * a4 + 3] * a.scale};
+            const f32x4 yv = {dv[db][4 * a4], dv[db][4 * a4 + 1], dv[db][4 * a4 + 2], dv[db][4 * a4 + 3]};
+            *(bf16x4*)(dkp + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(yk, bf16x4);
+            *(bf16x4*)(dvp + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(yv, bf16x4);
+          }
+      }
+    } else {
+      const int tb0 = max(0, fuse_bpos(a, j, TQ) - W + 1) / BKT;
+      float* pk = a.part + ((((long)bg * (spb - 1) + j) * a.fuse_nbt + (t - tb0)) * 2 + side) * (2 * BKT * D) +
+                  col * D + 4 * half;
+      float* pv = pk + BKT * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          *(f32x4*)(pk + db * 32 + 8 * a4) = f32x4{dk[db][4 * a4], dk[db][4 * a4 + 1], dk[db][4 * a4 + 2], dk[db][4 * a4 + 3]};
+          *(f32x4*)(pv + db * 32 + 8 * a4) = f32x4{dv[db][4 * a4], dv[db][4 * a4 + 1], dv[db][4 * a4 + 2], dv[db][4 * a4 + 3]};
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      dk[db] = f32x16{};
+      dv[db] = f32x16{};
+    }
+  };
+
+  // ---- dQ waves: dQ^T of block n (D blocks db0, db0 + 1 if two) from the
+  // key waves' dS^T and the K tiles, then dq = scale * dQ
+  const uint32_t dso0 = DsTile::tro(lane, 0), dso1 = DsTile::tro(lane, 1);
+  auto dq_block = [&](int n) {
+    const int buf = n & 1;
+    const int tlo = fuse_lo(a, n, TQ), thi = fuse_hi(a, n, TQ);
+    const int db0 = wv == 7 ? 2 : wv - 5;
+    const bool two = wv == 7;
+    const uint32_t x0 = 64u * db0, x1 = 64u * (db0 + 1);
+    f32x16 acc0 = {}, acc1 = {};
+    for (int t = tlo; t <= thi; ++t) {
+      const uint32_t kT = lds_addr(k_lds[t % NS]);
+      const uint32_t dT = lds_addr(ds_lds[buf][t % NKW]);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const bf16x8 bop = lds_tr16(dT + ((dso0 ^ (32u * kc)) + 1024u * kc), dT + ((dso1 ^ (32u * kc)) + 1024u * kc));
+        acc0 = mfma32(lds_tr16(kT + ((tro0 ^ x0) + 4096u * kc), kT + ((tro1 ^ x0) + 4096u * kc)), bop, acc0);
+        if (two) acc1 = mfma32(lds_tr16(kT + ((tro0 ^ x1) + 4096u * kc), kT + ((tro1 ^ x1) + 4096u * kc)), bop, acc1);
+      }
+    }
+    // dq = scale * dQ^T: lane (query col, half) holds d = 32 db + 8 a4 + 4 half
+    // + 0..3; v_permlane32_swap gives lane half 0 the 8 values of d = 32 db +
+    // 16 pr + 0..7 and lane half 1 those of 16 pr + 8..15, so every lane
+    // stores 16 bytes per pair of a4
+    const int tq = n * TQ + col / G;
+    uint16_t* dqp = a.dq + ((long)b * a.Sq + tq) * q_tok + (long)(g * G + col % G) * D + 8 * half;
+    auto store_db = [&](const f32x16& acc, int db) {
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const f32x4 x = {acc[8 * pr] * a.scale, acc[8 * pr + 1] * a.scale, acc[8 * pr + 2] * a.scale,
+                         acc[8 * pr + 3] * a.scale};
+        const f32x4 y = {acc[8 * pr + 4] * a.scale, acc[8 * pr + 5] * a.scale, acc[8 * pr + 6] * a.scale,
+                         acc[8 * pr + 7] * a.scale};
+        const u32x2 xw = __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));
+        const u32x2 yw = __builtin_bit_cast(u32x2, __builtin_convertvector(y, bf16x4));
+        const auto r0 = __builtin_amdgcn_permlane32_swap(xw[0], yw[0], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(xw[1], yw[1], false, false);
+        if (tq < a.Sq) *(u32x4*)(dqp + 32 * db + 16 * pr) = u32x4{r0[0], r1[0], r0[1], r1[1]};
+      }
+    };
+    store_db(acc0, db0);
+    if (two) store_db(acc1, db0 + 1);
+  };
+
+  // ---- prologue: block n0's tiles, rows, D and LSE
+  for (int t = fuse_lo(a, n0, TQ); t <= fuse_hi(a, n0, TQ); ++t) dma_kv(t, wv, kFuseWaves);
+  if (wv == 5) dma_rows(a.q, lds_addr(q_lds[n0 & 1]), n0);
+  if (wv == 6) dma_rows(a.dout, lds_addr(o_lds[n0 & 1]), n0);
+  if (wv == 5 || wv == 6) {
+    DRows dr;
+    d_load(dr, n0);
+    d_finish(dr, n0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // ---- main loops (the same number of barriers in both roles): iteration n
+  // computes block n's key tiles and block n - 1's dQ while block n + 1 is
+  // staged; iteration n1 only finishes dQ
+  if (wv < NKW) {
+    for (int n = n0; n <= n1; ++n) {
+      if (n < n1) {
+        const int lo = fuse_lo(a, n, TQ), hi = fuse_hi(a, n, TQ);
+        const int t = lo + (wv - lo % NKW + NKW) % NKW;
+        if (t <= hi) {
+          key_block(n, t);
+          if (n + 1 == n1 || fuse_lo(a, n + 1, TQ) > t) key_flush(t);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  } else {
+    for (int n = n0; n <= n1; ++n) {
+      const bool more = n + 1 < n1;
+      DRows dr;
+      if (more) {
+        if (wv == 5) dma_rows(a.q, lds_addr(q_lds[(n + 1) & 1]), n + 1);
+        if (wv == 6) dma_rows(a.dout, lds_addr(o_lds[(n + 1) & 1]), n + 1);
+        if (wv == 7 && fuse_hi(a, n + 1, TQ) > fuse_hi(a, n, TQ)) dma_kv(fuse_hi(a, n + 1, TQ), 0, 1);
+        if (wv < 7) d_load(dr, n + 1);
+      }
+      if (n > n0) dq_block(n - 1);
+      if (more && wv < 7) d_finish(dr, n + 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+  // this strip's sink-gradient partial per head, fixed order
+  if (a.sinks) {
+    if ((wv == 5 || wv == 6) && dq4 == 0) sink_red[drow] = sterm;
+    __syncthreads();
+    if (tid < G) {
+      float sum = 0.0f;
+      for (int m = tid; m < BKT; m += G) sum += sink_red[m];
+      a.sink_part[((long)b * spb + sidx) * a.Hq + g * G + tid] = -sum;
+    }
+  }
+}
+
+// dK, dV of the key tiles two strips share: the two fp32 partials added in a
+// fixed order (earlier strip first), scaled and rounded.  One workgroup per
+// (b, g, boundary, tile).
+__global__ __launch_bounds__(256) void bwd_fuse_fixup_kernel(BwdArgs a, int TQ) {
+  constexpr int D = 128;
+  const int nbt = a.fuse_nbt, nbd = a.fuse_spb - 1;
+  int idx = blockIdx.x;
+  const int i = idx % nbt;
+  idx /= nbt;
+  const int j = idx % nbd, bg = idx / nbd;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int Pj = fuse_bpos(a, j, TQ);
+  const int tb0 = max(0, Pj - a.window + 1) / BKT, tb1 = (Pj - 1) / BKT;
+  const int t = tb0 + i;
+  if (t > tb1) return;
+  const float* p0 = a.part + (((long)bg * nbd + j) * nbt + i) * 2 * (2 * BKT * D);
+  const float* p1 = p0 + 2 * BKT * D;
+  const long kv_tok = (long)a.Hkv * D;
+  for (int e = threadIdx.x * 4; e < 2 * BKT * D; e += 256 * 4) {
+    const int which = e / (BKT * D), r = (e / D) % BKT, d = e % D;
+    const int key = t * BKT + r;
+    if (key >= a.Sk) continue;
+    const f32x4 x = *(const f32x4*)(p0 + e) + *(const f32x4*)(p1 + e);
+    const f32x4 y = which == 0 ? x * a.scale : x;
+    uint16_t* dst = (which == 0 ? a.dk : a.dv) + ((long)b * a.Sk + key) * kv_tok + (long)g * D + d;
+    *(bf16x4*)dst = __builtin_convertvector(y, bf16x4);
+  }
+}
+
+// Does the fused kernel apply, and with how many strips per (b, g)?
+static bool fuse_plan(BwdArgs& a, int G, size_t part_bytes) {
+  if (a.window <= 0 || a.D != 128 || (G != 4 && G != 8) || a.Sq <= 0) return false;
+  const int TQ = BKT / G;
+  if (a.q_offset % TQ != 0) return false;
+  auto fl = [](int x) { return x >= 0 ? x / BKT : -((-x + BKT - 1) / BKT); };
+  auto lo = [&](int p) { return fl(p - a.window + 1); };
+  auto hi = [&](int p) { return fl(p + TQ - 1); };
+  // block start positions repeat modulo 32: at most five live tiles per
+  // block, six over three consecutive blocks (the K/V slots)
+  for (int n = 1; n <= 2 * BKT / TQ + 1; ++n) {
+    const int p = a.q_offset % BKT + n * TQ;
+    if (hi(p) - lo(p) + 1 > kFuseKeyWaves) return false;
+    if (hi(p + TQ) - lo(p - TQ) + 1 > kFuseSlots) return false;
+  }
+  const int nbt = max(1, (a.window - 2 + BKT - 1) / BKT + 1);
+  if (nbt > kFuseMaxBoundaryTiles) return false;
+  const int bgs = a.B * a.Hkv;
+  const int min_len = max(kFuseMinStrip, a.window + 2 * BKT);
+  int spb = min(kFuseMaxBoundaries / max(1, bgs), a.Sq / min_len);
+  if (spb < 1) spb = 1;
+  const size_t need = (size_t)bgs * (spb - 1) * nbt * 2 * 2 * BKT * 128 * 4;
+  if (need > part_bytes) return false;
+  a.fuse_spb = spb;
+  a.fuse_nbt = nbt;
+  return true;
+}
+
+template <int G>
+hipError_t launch_bwd_fused(BwdArgs a, hipStream_t s) {
+  const int TQ = BKT / G;
+  const int spb = a.fuse_spb;
+  a.n_sink_parts = a.B * spb;
+  hipLaunchKernelGGL((bwd_fused_swa_kernel<G>), dim3(a.B * a.Hkv * spb), dim3(kFuseWaves * 64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (spb > 1) {
+    hipLaunchKernelGGL(bwd_fuse_fixup_kernel, dim3(a.B * a.Hkv * (spb - 1) * a.fuse_nbt), dim3(256), 0, s, a, TQ);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.dsink) {
+    if (a.sinks)
+      hipLaunchKernelGGL(bwd_sink_reduce_kernel, dim3(a.Hq), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(bwd_zero_kernel, dim3((a.Hq + 255) / 256), dim3(256), 0, s, a.dsink, a.Hq);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
 // Can the strip dQ kernel hold every block's window (plus the next block's
 // new tile) in its ring?  Blocks start at positions q_offset + blk*TB.
 static bool dq_strip_fits(const BwdArgs& a, int G) {
@@ -863,6 +1394,9 @@ static bool dq_strip_fits(const BwdArgs& a, int G) {
 
 template <int D, int G>
 hipError_t launch_bwd_dg(BwdArgs a, hipStream_t s) {
+  if constexpr (G == 4 || G == 8) {
+    if (a.part && fuse_plan(a, G, a.part_bytes)) return launch_bwd_fused<G>(a, s);
+  }
   // dQ first: it also leaves D = <dO, O> for dK/dV and the dsink partials
   int n_tb = 0;
   if constexpr (G == 4 || G == 8) {
@@ -933,12 +1467,19 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t s) {
 
 BwdPlan plan_backward(int B, int Sq, int Hq) {
   BwdPlan p = {};
-  // partials: one per (request, dQ token block) and head; blocks hold at
-  // least 8 tokens (G <= 32)
+  // sink partials: one per (request, dQ token block or strip) and head;
+  // blocks hold at least 8 tokens (G <= 32)
   const long parts = (long)B * ((Sq + 7) / 8);
   const size_t delta_bytes = ((size_t)B * Sq * Hq * 4 + 255) / 256 * 256;
   p.delta_bytes = delta_bytes;
-  p.ws_bytes = delta_bytes + (size_t)parts * Hq * 4;
+  p.part_offset = delta_bytes + ((size_t)parts * Hq * 4 + 255) / 256 * 256;
+  // the fused kernel's shared-tile partials: at most kFuseMaxBoundaries strip
+  // boundaries (only when a strip pair fits, Sq >= 2 * kFuseMinStrip), each
+  // with kFuseMaxBoundaryTiles tiles x 2 sides x (dK, dV) x 32 keys x 128
+  p.part_bytes = Sq >= 2 * kFuseMinStrip
+                     ? (size_t)kFuseMaxBoundaries * kFuseMaxBoundaryTiles * 2 * 2 * BKT * 128 * 4
+                     : 0;
+  p.ws_bytes = p.part_offset + p.part_bytes;
   return p;
 }
 

@@ -72,6 +72,27 @@ __device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, uint32_t voff, ui
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, POLICY);
 }
 
+// One wave-wide 16-byte-per-lane load from global memory straight into LDS:
+// lane l's 16 bytes (voffset bytes past first_row, checked against
+// num_records; a lane out of range writes zeros) land at LDS byte address
+// lds_byte + 16 l, so one instruction fills a contiguous 1 KiB window.
+// Written as asm so that the compiler's wait-count pass, which cannot tell
+// one LDS buffer from another, does not make every later LDS read wait for
+// these loads: the caller waits for them itself (s_waitcnt vmcnt) before the
+// barrier that publishes the window.  vmcnt retires in order, so loads the
+// compiler does not count only make its own waits stricter.  The buffer
+// descriptor is base, stride 0, num_records and the flags word of make_rsrc;
+// lds_byte and the descriptor must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(const void* first_row, uint32_t num_records, uint32_t lds_byte,
+                                          uint32_t voffset) {
+  const uint64_t base = (uint64_t)(uintptr_t)first_row;
+  const u32x4 desc = {(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, num_records, 0x00020000u};
+  __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(lds_byte), "v"(voffset), "s"(desc)
+                   : "m0");
+}
+
 // Plain global accesses with a cache policy (see kCacheNT).
 template <bool NT, typename T>
 __device__ __forceinline__ T load_pol(const T* p) {

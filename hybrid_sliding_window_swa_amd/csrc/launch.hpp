@@ -78,10 +78,15 @@ struct BwdArgs {
   float scale, scale_log2;
   int n_sink_parts;       // set by the launcher
   int strips_per_bg;      // set by the launcher (0: the non-persistent dQ kernel)
+  float* part;            // workspace: fp32 dK/dV partials of key tiles two strips share
+  size_t part_bytes;
+  int fuse_spb, fuse_nbt; // set by the launcher for the fused sliding-window kernel
 };
 
 struct BwdPlan {
   size_t delta_bytes; // bytes of the delta array (256-byte rounded)
+  size_t part_offset; // byte offset of the fused kernel's partials
+  size_t part_bytes;
   size_t ws_bytes;
 };
 BwdPlan plan_backward(int B, int Sq, int Hq);

@@ -173,22 +173,11 @@ struct DmaTile {
     const int row = P / pitch, ch = P - row * pitch;
     return (ch < CPR && row < 32) ? (uint32_t)row * row_bytes + (uint32_t)ch * 16u : kOut;
   }
-  // One wave-wide load into the 1 KiB LDS window at byte address lds_byte.
-  // Written as asm so that the compiler's wait-count pass, which cannot tell
-  // one ring slot from another, does not make every later LDS read of the
-  // step wait for these loads: the loop waits for them itself, once, before
-  // the barrier that publishes the slots.  (vmcnt retires in order, so loads
-  // the compiler does not count only make its own waits stricter.)  The
-  // buffer descriptor is base, stride 0, num_records, and the flags word of
-  // make_rsrc; the voffset register is read at issue and stays live.
+  // One wave-wide load into the 1 KiB LDS window at byte address lds_byte
+  // (lds_dma16).
   static __device__ __forceinline__ void load(const uint16_t* first_row, uint32_t num_records, uint32_t lds_byte,
                                               uint32_t voffset) {
-    const uint64_t base = (uint64_t)(uintptr_t)first_row;
-    const u32x4 desc = {(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, num_records, 0x00020000u};
-    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :
-                     : "s"(lds_byte), "v"(voffset), "s"(desc)
-                     : "m0");
+    lds_dma16(first_row, num_records, lds_byte, voffset);
   }
 };
 

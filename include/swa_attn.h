@@ -145,8 +145,11 @@ SWA_API swa_status_t swa_attn_prefill_lse(const void *q, const void *k, const vo
                                   int window, int q_offset, float sm_scale,
                                   swa_dtype_t dtype, void *stream);
 
-/* Bytes of device workspace swa_attn_backward needs (per-row <dO, O> and the
- * per-workgroup partial sink gradients).  0 for invalid sizes. */
+/* Bytes of device workspace swa_attn_backward needs: per-row <dO, O>, the
+ * per-workgroup partial sink gradients, and, for Sq >= 1024, a fixed 80 MiB
+ * for the fp32 dK/dV partials of key tiles that two query strips of the
+ * sliding-window kernel share (at most 256 strip boundaries x 5 tiles).
+ * 0 for invalid sizes. */
 SWA_API size_t swa_attn_backward_workspace_bytes(int B, int Sq, int Hq);
 
 /*
@@ -166,8 +169,9 @@ SWA_API size_t swa_attn_backward_workspace_bytes(int B, int Sq, int Hq);
  *                    swa_attn_backward_workspace_bytes(B, Sq, Hq) bytes.
  * Every element of dq, dk and dv is written (keys no query sees get zeros).
  * Accumulation is fp32; P and dS are rounded to bf16 for the matrix cores;
- * dq, dk, dv are rounded to bf16 (nearest even); dsink is summed in a fixed
- * order (deterministic).  SWA_BF16 only; shape rules as swa_attn_prefill.
+ * dq, dk, dv are rounded to bf16 (nearest even); dsink and the dK/dV of key
+ * tiles shared by two query strips are summed in a fixed order
+ * (deterministic).  SWA_BF16 only; shape rules as swa_attn_prefill.
  * Unlike the forward, the backward reads whole 32-key tiles around each
  * window and multiplies rows outside it by zero weights, so k and v must be
  * finite for all Sk rows.  Calls sharing a workspace must not overlap.

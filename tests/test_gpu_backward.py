@@ -19,9 +19,11 @@ pytestmark = pytest.mark.gpu
 # sum_d |dO_id O_id|, enters dS_ij = P_ij (dP_ij - D_i) unreduced where dP_ij
 # and D_i nearly cancel (a query whose weight sits on few keys, e.g. W = 1).
 # Each element is judged against the gradient's scale:
-# |gpu - ref| <= GRAD_TOL * (|ref| + rms(ref)).  Over every case below and the
-# full 32K workload the largest err / (|ref| + rms) measured on the MI355X is
-# 3.8e-2 (dk at W = 1, dq at 32K); GRAD_TOL keeps a 1.2x margin above it.
+# |gpu - ref| <= GRAD_TOL * (|ref| + rms(ref)), plus, at W = 1 where the
+# cancellation is exact, the derived D-term bound of _d_term_bounds.  Over
+# every case below and the full 32K workload the largest err / (|ref| + rms)
+# measured on the MI355X outside W = 1 is 3.6e-2 (dq at 32K); GRAD_TOL keeps
+# a 1.2x margin above it.
 # The relative L2 error per tensor is held to the bf16 rtol of 1e-2
 # (measured at most 6.6e-3).
 GRAD_TOL = 4.5e-2
@@ -46,23 +48,65 @@ CASES = [
     # with D 64) and a window that is not a multiple of the tile
     ("swa_g4_d128", 1, 200, 200, 16, 4, 128, 128, True),
     ("swa_g8_d64_w96", 1, 160, 160, 16, 2, 64, 96, True),
+    # the fused sliding-window kernel (D 128, G 4 or 8, q_offset a multiple
+    # of 32 / G) over several strips per (b, g): key tiles two strips share
+    # (partials added by the fix-up kernel), ragged last blocks, an offset
+    # chunk, two requests, W = 1 and a window that is not a multiple of 32
+    ("strips_g8", 1, 1100, 1100, 16, 2, 128, 128, True),
+    ("strips_many_g8", 1, 2600, 2600, 8, 1, 128, 128, True),
+    ("strips_g4_w100", 1, 1500, 1500, 16, 4, 128, 100, True),
+    ("strips_chunk_g8", 1, 1202, 1402, 16, 2, 128, 128, True),
+    ("strips_b2_nosink", 2, 1100, 1100, 8, 1, 128, 128, False),
+    ("strips_w1_g8", 1, 1030, 1030, 8, 1, 128, 1, True),
 ]
 
 
-def _check_grad(got, ref, name):
+def _check_grad(got, ref, name, extra=None):
+    """|got - ref| <= GRAD_TOL * (|ref| + rms(ref)) + extra elementwise, and
+    the relative L2 error below GRAD_L2 (extra: a derived error term, see
+    _d_term_bounds)."""
     g = got.detach().float().cpu().numpy()
     r = np.asarray(ref, dtype=np.float64)
     assert np.isfinite(g).all(), f"{name}: non-finite"
     rms = float(np.sqrt((r ** 2).mean())) if r.size else 0.0
     err = np.abs(g - r)
     bound = GRAD_TOL * (np.abs(r) + rms)
+    if extra is not None:
+        bound = bound + extra
     worst = float((err - bound).max()) if r.size else 0.0
     l2 = rel_l2(got, r) if rms > 0 else 0.0
     need = float((err / (np.abs(r) + rms)).max()) if rms > 0 else 0.0
     print(f"{name}: max abs err {err.max():.3e} rms(ref) {rms:.3e} rel L2 {l2:.3e} "
-          f"max err/(|ref|+rms) {need:.3e}", flush=True)
+          f"max err/(|ref|+rms) {need:.3e}" + ("" if extra is None else " (+ D term)"), flush=True)
     assert worst <= 0, f"{name}: max excess {worst:.3e}"
     assert l2 < GRAD_L2, f"{name}: relative L2 {l2:.3e}"
+
+
+def _d_term_bounds(q, k, v, dout, sinks, cfg):
+    """Error terms of the gradients that come from the row term D_i = <dO_i, O_i>
+    at W = 1, where it cancels against dP_ii.  The kernels form D_i from the
+    forward's bf16 output; with one key per row that output is the exact one
+    within 2^-8 elementwise (the weight rounded once to bf16 before P V and
+    the normaliser built from the same rounded weight, then O rounded to
+    bf16), so |D_i - D_i(exact)| <= e_i = 2^-8 sum_d |dO_id O_id|, and through
+    dS_ij = P_ij (dP_ij - D_i):
+      |err dq_i| <= scale e_i sum_j P_ij |k_j|,
+      |err dk_j| <= scale sum_i P_ij e_i |q_i|,  and dv does not use D
+    (dsink sums these errors over many rows with random signs and stays within
+    GRAD_TOL without a term of its own).  Returns the (dq, dk) terms from the
+    oracle's weights, or Nones."""
+    if cfg.window != 1:
+        return None, None
+    ref = oracle.prefill(q, k, v, sinks, cfg.window, cfg.q_offset, cfg.scale, want_lse=True, want_weights=True)
+    P = np.asarray(ref["weights"], dtype=np.float64)              # [B, Sq, Hq, Sk]
+    e = 2.0 ** -8 * np.abs(dout.double().numpy() * ref["o"]).sum(-1)  # [B, Sq, Hq]
+    G = cfg.Hq // cfg.Hkv
+    ka = np.repeat(np.abs(k.double().numpy()), G, axis=2)         # [B, Sk, Hq, D]
+    qa = np.abs(q.double().numpy())
+    x_dq = cfg.scale * e[..., None] * np.einsum("bihj,bjhd->bihd", P, ka)
+    x_dk = cfg.scale * np.einsum("bihj,bih,bihd->bjhd", P, e, qa)
+    x_dk = x_dk.reshape(x_dk.shape[0], x_dk.shape[1], cfg.Hkv, G, -1).sum(3)
+    return x_dq, x_dk
 
 
 def _inputs(case):
@@ -101,8 +145,9 @@ def test_backward_matches_oracle(case):
                                             cfg.scale)
     torch.cuda.synchronize()
     rq, rk, rv, rs = oracle.prefill_backward(q, k, v, dout, sinks, cfg.window, cfg.q_offset, cfg.scale)
-    _check_grad(dq, rq, case[0] + " dq")
-    _check_grad(dk, rk, case[0] + " dk")
+    x_dq, x_dk = _d_term_bounds(q, k, v, dout, sinks, cfg)
+    _check_grad(dq, rq, case[0] + " dq", x_dq)
+    _check_grad(dk, rk, case[0] + " dk", x_dk)
     _check_grad(dv, rv, case[0] + " dv")
     if sinks is not None:
         _check_grad(dsink, rs, case[0] + " dsink")
