@@ -1035,12 +1035,13 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
     }
   };
 
-  // ---- D = <dO, O> and LSE of block n (waves 5, 6: 16 rows each, four lanes per row)
-  const int drow = 16 * (wv - 5) + (lane >> 2), dq4 = lane & 3;
-  const float sink_h = (a.sinks && wv >= 5 && wv < 7) ? a.sinks[g * G + drow % G] : 0.0f;
+  // ---- D = <dO, O> and LSE of block n (wave 7: two lanes per row, loaded
+  // two blocks ahead of their use)
+  const int drow = lane >> 1, dhr = lane & 1;
+  const float sink_h = (a.sinks && wv == 7) ? a.sinks[g * G + drow % G] : 0.0f;
   float sterm = 0.0f;
   struct DRows {
-    u32x4 o[4], d[4];
+    u32x4 o[8], d[8];
     float lse;
   };
   auto d_load = [&](DRows& r, int n) {
@@ -1049,9 +1050,9 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
     const long base = ((long)b * a.Sq + t0) * q_tok + (long)g * G * D;
     const uint32_t bytes = (uint32_t)(((ntok - 1) * q_tok + (long)G * D) * 2);
     const rsrc_t ro = make_rsrc(a.o + base, bytes), rd = make_rsrc(a.dout + base, bytes);
-    const uint32_t off = (uint32_t)((((drow / G) * q_tok + (long)(drow % G) * D) + 32 * dq4) * 2);
+    const uint32_t off = (uint32_t)((((drow / G) * q_tok + (long)(drow % G) * D) + 64 * dhr) * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       r.o[i] = buf_load16(ro, off + 16u * i, 0);
       r.d[i] = buf_load16(rd, off + 16u * i, 0);
     }
@@ -1062,15 +1063,22 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
   auto d_finish = [&](const DRows& r, int n) {
     float part = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
       part = dot_bf16x8(__builtin_bit_cast(bf16x8, r.d[i]), __builtin_bit_cast(bf16x8, r.o[i]), part);
     part += __shfl_xor(part, 1);
-    part += __shfl_xor(part, 2);
-    if (dq4 == 0) {
+    if (dhr == 0) {
       lse_lds[n & 1][drow] = r.lse * kLog2e;
       del_lds[n & 1][drow] = part;
       if (a.sinks && n * TQ + drow / G < a.Sq) sterm += __expf(sink_h - r.lse) * part;
     }
+  };
+  // Block boundary: every wave's LDS writes (and the direct-to-LDS loads the
+  // staging waves waited for) are visible after it; global loads and stores
+  // may stay in flight across it.
+  auto block_sync = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
 
   // ---- key waves
@@ -1088,14 +1096,33 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
     const uint32_t qT = lds_addr(q_lds[buf]), oT = lds_addr(o_lds[buf]);
     const uint32_t qa = qT + kop, oa = oT + kop, ka = lds_addr(k_lds[t % NS]) + kop;
     const uint32_t va = lds_addr(v_lds[t % NS]) + vop;
-    // S = Q K^T: lane (col = key), registers = query rows c_row(v, half)
+    // S = Q K^T: lane (col = key), registers = query rows c_row(v, half);
+    // operand reads run two chunks ahead of their MFMAs
     f32x16 s = {};
+    {
+      bf16x8 qr[3], kr[3];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s = mfma32(lds_rd16(qa ^ (32u * c)), lds_rd16(ka ^ (32u * c)), s);
+      for (int c = 0; c < 2; ++c) {
+        qr[c] = lds_rd16(qa ^ (32u * c));
+        kr[c] = lds_rd16(ka ^ (32u * c));
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if (c + 2 < 8) {
+          qr[(c + 2) % 3] = lds_rd16(qa ^ (32u * (c + 2)));
+          kr[(c + 2) % 3] = lds_rd16(ka ^ (32u * (c + 2)));
+        }
+        s = mfma32(qr[c % 3], kr[c % 3], s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // Masking: only the window (and keys past Sk, whose zero K rows would
+    // otherwise get weight exp(-LSE)).  Query rows past Sq need none: their
+    // q, dO rows, LSE and D read as zeros, so P = 1 there multiplies zero dO
+    // rows and dS = P (0 - 0) = 0.
     const int pos0 = a.q_offset + n * TQ;
     const int kb = t * BKT, key = kb + col;
-    const int i_hi = min(pos0 + TQ, a.q_offset + a.Sq) - 1;
-    const bool edge = !(kb + BKT - 1 <= pos0 && kb > i_hi - W) || i_hi < pos0 + TQ - 1 || kb + BKT > a.Sk;
+    const bool edge = !(kb + BKT - 1 <= pos0 && kb > pos0 + TQ - 1 - W) || kb + BKT > a.Sk;
     // the LSE and D of rows c_row(v, half): four runs of four rows, one
     // 16-byte read each
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
@@ -1109,11 +1136,15 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = exp2_fast(fmaf(s[v], c2, -l4[v >> 2][v & 3]));
     if (edge) {
+      // rows c_row(v, half) = 8 (v / 4) + 4 half + v % 4 belong to token
+      // v / 4 (G = 8) or 2 (v / 4) + half (G = 4) of the block
+      const bool kin = key < a.Sk;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = pos0 + c_row(v, half) / G;
-        const bool ok = key <= i && key > i - W && i <= i_hi && key < a.Sk;
-        p[v] = ok ? p[v] : 0.0f;
+      for (int j = 0; j < 4; ++j) {
+        const int i = pos0 + (G == 8 ? j : 2 * j + half);
+        const bool ok = kin && key <= i && key > i - W;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[4 * j + e] = ok ? p[4 * j + e] : 0.0f;
       }
     }
     bf16x8 pb[2];
@@ -1123,12 +1154,14 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
     f32x16 dp = {};
 #pragma unroll
     for (int c = 0; c < 8; ++c) dp = mfma32(lds_rd16(oa ^ (32u * c)), lds_rd16(va + 32u * c), dp);
+    // (tile base + tro) ^ 64 db: the base is 256-byte aligned, so the XOR
+    // only touches the per-lane part; 4096 kc becomes the read's immediate
+    const uint32_t ot0 = oT + tro0, ot1 = oT + tro1;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        dv[db] = mfma32(lds_tr16(oT + ((tro0 ^ (64u * db)) + 4096u * kc), oT + ((tro1 ^ (64u * db)) + 4096u * kc)),
-                        pb[kc], dv[db]);
+        dv[db] = mfma32(lds_tr16((ot0 ^ (64u * db)) + 4096u * kc, (ot1 ^ (64u * db)) + 4096u * kc), pb[kc], dv[db]);
     // dS = P (dP - D), and dS^T into this wave's LDS tile for dQ
     bf16x8 sb[2];
 #pragma unroll
@@ -1141,12 +1174,12 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
       *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(dsT + DsTile::wr(col, half, j)) = x2;
     }
     // dK^T += Q^T dS
+    const uint32_t qt0 = qT + tro0, qt1 = qT + tro1;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        dk[db] = mfma32(lds_tr16(qT + ((tro0 ^ (64u * db)) + 4096u * kc), qT + ((tro1 ^ (64u * db)) + 4096u * kc)),
-                        sb[kc], dk[db]);
+        dk[db] = mfma32(lds_tr16((qt0 ^ (64u * db)) + 4096u * kc, (qt1 ^ (64u * db)) + 4096u * kc), sb[kc], dk[db]);
   };
   // tile t is done: bf16 dK, dV when only this strip sees it, else an fp32
   // partial for bwd_fuse_fixup (side 0: the earlier strip of the boundary)
@@ -1199,27 +1232,51 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
   // ---- dQ waves: dQ^T of block n (D blocks db0, db0 + 1 if two) from the
   // key waves' dS^T and the K tiles, then dq = scale * dQ
   const uint32_t dso0 = DsTile::tro(lane, 0), dso1 = DsTile::tro(lane, 1);
-  auto dq_block = [&](int n) {
+  // wave 5: D blocks 0, 1 (two = true); wave 6: 2; wave 7: 3.  `two` is
+  // passed as a literal where it is known, so wave 7's code holds no second
+  // accumulator next to its D rows.
+  const int db0 = wv == 5 ? 0 : wv - 4;
+  const uint32_t x0 = 64u * db0, x1 = 64u * (db0 + 1);
+  f32x16 acc0 = {}, acc1 = {};
+  // operands of one tile: dS^T (B) and K^T (A) for both 16-key chunks
+  struct DqOps {
+    bf16x8 bop[2], a0[2], a1[2];
+  };
+  auto dq_ops = [&](int t, int buf, bool two) {
+    DqOps o;
+    const uint32_t kT = lds_addr(k_lds[t % NS]);
+    const uint32_t dT = lds_addr(ds_lds[buf][t % NKW]);
+    const uint32_t k0 = kT + tro0, k1 = kT + tro1, d0 = dT + dso0, d1 = dT + dso1;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      o.bop[kc] = lds_tr16((d0 ^ (32u * kc)) + 1024u * kc, (d1 ^ (32u * kc)) + 1024u * kc);
+      o.a0[kc] = lds_tr16((k0 ^ x0) + 4096u * kc, (k1 ^ x0) + 4096u * kc);
+      if (two) o.a1[kc] = lds_tr16((k0 ^ x1) + 4096u * kc, (k1 ^ x1) + 4096u * kc);
+    }
+    return o;
+  };
+  // dQ^T of block n into acc0 (acc1).  (Reading the next tile's operands
+  // during the current tile's MFMAs measured slower: the register rotation
+  // in the runtime loop waits for them anyway.)
+  auto dq_compute = [&](int n, bool two) {
     const int buf = n & 1;
     const int tlo = fuse_lo(a, n, TQ), thi = fuse_hi(a, n, TQ);
-    const int db0 = wv == 7 ? 2 : wv - 5;
-    const bool two = wv == 7;
-    const uint32_t x0 = 64u * db0, x1 = 64u * (db0 + 1);
-    f32x16 acc0 = {}, acc1 = {};
+    acc0 = f32x16{};
+    acc1 = f32x16{};
     for (int t = tlo; t <= thi; ++t) {
-      const uint32_t kT = lds_addr(k_lds[t % NS]);
-      const uint32_t dT = lds_addr(ds_lds[buf][t % NKW]);
+      const DqOps cur = dq_ops(t, buf, two);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        const bf16x8 bop = lds_tr16(dT + ((dso0 ^ (32u * kc)) + 1024u * kc), dT + ((dso1 ^ (32u * kc)) + 1024u * kc));
-        acc0 = mfma32(lds_tr16(kT + ((tro0 ^ x0) + 4096u * kc), kT + ((tro1 ^ x0) + 4096u * kc)), bop, acc0);
-        if (two) acc1 = mfma32(lds_tr16(kT + ((tro0 ^ x1) + 4096u * kc), kT + ((tro1 ^ x1) + 4096u * kc)), bop, acc1);
+        acc0 = mfma32(cur.a0[kc], cur.bop[kc], acc0);
+        if (two) acc1 = mfma32(cur.a1[kc], cur.bop[kc], acc1);
       }
     }
-    // dq = scale * dQ^T: lane (query col, half) holds d = 32 db + 8 a4 + 4 half
-    // + 0..3; v_permlane32_swap gives lane half 0 the 8 values of d = 32 db +
-    // 16 pr + 0..7 and lane half 1 those of 16 pr + 8..15, so every lane
-    // stores 16 bytes per pair of a4
+  };
+  // dq = scale * dQ^T of block n: lane (query col, half) holds d = 32 db +
+  // 8 a4 + 4 half + 0..3; v_permlane32_swap gives lane half 0 the 8 values of
+  // d = 32 db + 16 pr + 0..7 and lane half 1 those of 16 pr + 8..15, so every
+  // lane stores 16 bytes per pair of a4
+  auto dq_store = [&](int n, bool two) {
     const int tq = n * TQ + col / G;
     uint16_t* dqp = a.dq + ((long)b * a.Sq + tq) * q_tok + (long)(g * G + col % G) * D + 8 * half;
     auto store_db = [&](const f32x16& acc, int db) {
@@ -1240,19 +1297,21 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
     if (two) store_db(acc1, db0 + 1);
   };
 
-  // ---- prologue: block n0's tiles, rows, D and LSE
+  // ---- prologue: block n0's tiles, rows, D and LSE (and block n0 + 1's
+  // rows for D in flight)
   for (int t = fuse_lo(a, n0, TQ); t <= fuse_hi(a, n0, TQ); ++t) dma_kv(t, wv, kFuseWaves);
   if (wv == 5) dma_rows(a.q, lds_addr(q_lds[n0 & 1]), n0);
   if (wv == 6) dma_rows(a.dout, lds_addr(o_lds[n0 & 1]), n0);
-  if (wv == 5 || wv == 6) {
-    DRows dr;
-    d_load(dr, n0);
-    d_finish(dr, n0);
-  }
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  DRows dr0, dr1;
+  if (wv == 7) {
+    d_load(dr0, n0);
+    d_finish(dr0, n0);
+    if (n0 + 1 < n1) d_load(dr0, n0 + 1);
+  }
+  block_sync();
 
-  // ---- main loops (the same number of barriers in both roles): iteration n
+  // ---- main loops (the same number of barriers in every role): iteration n
   // computes block n's key tiles and block n - 1's dQ while block n + 1 is
   // staged; iteration n1 only finishes dQ
   if (wv < NKW) {
@@ -1265,29 +1324,48 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
           if (n + 1 == n1 || fuse_lo(a, n + 1, TQ) > t) key_flush(t);
         }
       }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      block_sync();
     }
-  } else {
+  } else if (wv < 7) {
+    // staging waves: q (wave 5) and dO (wave 6) rows of block n + 1, wave 6
+    // also the arriving K/V tile, waited for before the barrier.  The dq of
+    // block n - 2 is stored right after those loads are issued, so that the
+    // wait does not also wait for stores issued just before it.
     for (int n = n0; n <= n1; ++n) {
-      const bool more = n + 1 < n1;
-      DRows dr;
-      if (more) {
+      if (n + 1 < n1) {
         if (wv == 5) dma_rows(a.q, lds_addr(q_lds[(n + 1) & 1]), n + 1);
-        if (wv == 6) dma_rows(a.dout, lds_addr(o_lds[(n + 1) & 1]), n + 1);
-        if (wv == 7 && fuse_hi(a, n + 1, TQ) > fuse_hi(a, n, TQ)) dma_kv(fuse_hi(a, n + 1, TQ), 0, 1);
-        if (wv < 7) d_load(dr, n + 1);
+        if (wv == 6) {
+          dma_rows(a.dout, lds_addr(o_lds[(n + 1) & 1]), n + 1);
+          if (fuse_hi(a, n + 1, TQ) > fuse_hi(a, n, TQ)) dma_kv(fuse_hi(a, n + 1, TQ), 0, 1);
+        }
       }
-      if (n > n0) dq_block(n - 1);
-      if (more && wv < 7) d_finish(dr, n + 1);
+      if (n - 2 >= n0) dq_store(n - 2, wv == 5);
+      if (n > n0) dq_compute(n - 1, wv == 5);
       __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      block_sync();
+    }
+    if (n1 - 1 >= n0) dq_store(n1 - 1, wv == 5);
+  } else {
+    // wave 7: D and LSE of block n + 1 from rows loaded an iteration earlier,
+    // block n + 2's rows loaded meanwhile (two register sets, alternating)
+    auto step = [&](int n, DRows& cur, DRows& nxt) {
+      if (n + 2 < n1) d_load(nxt, n + 2);
+      if (n > n0) {
+        dq_compute(n - 1, false);
+        dq_store(n - 1, false);
+      }
+      if (n + 1 < n1) d_finish(cur, n + 1);
+      block_sync();
+    };
+    for (int n = n0; n <= n1; n += 2) {
+      step(n, dr0, dr1);
+      if (n + 1 <= n1) step(n + 1, dr1, dr0);
     }
   }
 
   // this strip's sink-gradient partial per head, fixed order
   if (a.sinks) {
-    if ((wv == 5 || wv == 6) && dq4 == 0) sink_red[drow] = sterm;
+    if (wv == 7 && dhr == 0) sink_red[drow] = sterm;
     __syncthreads();
     if (tid < G) {
       float sum = 0.0f;
