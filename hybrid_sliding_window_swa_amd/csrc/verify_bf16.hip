@@ -130,10 +130,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
   constexpr int LD_IT = 32 * CPR / 64;         // 16-byte loads per lane per tile (K or V)
   constexpr int ACC_N = NB * ND * 16;          // accumulator floats per lane
-  constexpr int MERGE_SLOTS = NW / 2 > 0 ? NW / 2 : 1;
+  constexpr int NQ_W = (NB * ND + NW - 1) / NW;  // output blocks each wave finishes
+  static_assert((NW & (NW - 1)) == 0, "the merge tree pairs waves");
 
   struct MergeLds {
-    float acc[MERGE_SLOTS][ACC_N][64];
+    float acc[NW][ACC_N][64];
   };
   struct TileLds {
     uint16_t k[NW][KTile<D>::ELEMS];
@@ -239,8 +240,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
     }
   };
 
+  // The tile of new rows (split 0's last) holds only T distinct rows: when
+  // it is not this wave's first tile, its T rows are loaded in the prologue
+  // with the first tile (one memory latency instead of two in a row) and
+  // written into the wave's LDS tile when its turn comes.  Its other rows
+  // keep the previous tile's (finite) values there and are masked out.
+  constexpr int LDN = 2;                       // 16-byte loads per lane for T rows
+  const bool pre_new = s == 0 && ntc % NW == wv && ntc != wv && p.T * CPR <= 64 * LDN;
+  u32x4 nk[LDN], nv[LDN];
+  auto load_new = [&]() {
+#pragma unroll
+    for (int i = 0; i < LDN; ++i) {
+      const int c = lane + 64 * i;
+      const long o = bg_new + (long)min(c / CPR, p.T - 1) * kv_tok + (c % CPR) * 8;
+      nk[i] = __builtin_nontemporal_load((const u32x4*)(p.k_new + o));
+      nv[i] = __builtin_nontemporal_load((const u32x4*)(p.v_new + o));
+    }
+  };
+  auto store_new = [&]() {
+#pragma unroll
+    for (int i = 0; i < LDN; ++i) {
+      const int c = lane + 64 * i;
+      if (c < p.T * CPR) {
+        *(u32x4*)&k_t[KTile<D>::off(c / CPR, (c % CPR) * 8)] = nk[i];
+        *(u32x4*)&v_t[VTile<D>::off(c / CPR, (c % CPR) * 8)] = nv[i];
+      }
+    }
+  };
+
   if (wv < ntiles) {
     load_tile(wv);
+    if (pre_new) load_new();
     store_tile();
   }
   // Drain the prologue loads (queries, first tile) so that inside the loop
@@ -249,7 +279,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
   __builtin_amdgcn_s_waitcnt(0);
   for (int j = wv; j < ntiles; j += NW) {
     const bool more = j + NW < ntiles;
-    if (more) load_tile(j + NW);
+    const bool next_new = more && pre_new && j + NW == ntc;
+    if (more && !next_new) load_tile(j + NW);
     wave_lds_sync();
 
     f32x16 sc[NB];
@@ -311,7 +342,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
       }
     }
     wave_lds_sync();
-    if (more) store_tile();
+    if (next_new) {
+      store_new();
+    } else if (more) {
+      store_tile();
+    }
   }
 
   // ---- merge the waves: common max, then a fixed-order pairwise sum in LDS
@@ -342,67 +377,61 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
 #pragma unroll
     for (int db = 0; db < ND; ++db) acc[nb][db] *= f;
   }
+  // Every wave leaves its rescaled accumulators in LDS; then wave w sums
+  // output blocks q = w, w + NW, ... (q = nb * ND + db) over the waves, in
+  // a fixed pairwise order ((w0 + w2) + (w1 + w3) for four waves: bitwise
+  // deterministic), and writes them: one barrier, and every wave writes.
   MergeLds* ml = (MergeLds*)lds_main;
 #pragma unroll
-  for (int r = NW / 2; r >= 1; r /= 2) {
-    if (wv >= r && wv < 2 * r) {
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
-        for (int db = 0; db < ND; ++db)
+      for (int v = 0; v < 16; ++v) ml->acc[wv][(nb * ND + db) * 16 + v][lane] = acc[nb][db][v];
+  __syncthreads();
 #pragma unroll
-          for (int v = 0; v < 16; ++v) ml->acc[wv - r][(nb * ND + db) * 16 + v][lane] = acc[nb][db][v];
+  for (int qi = 0; qi < NQ_W; ++qi) {
+    const int q = wv + qi * NW;
+    if (q >= NB * ND) break;
+    const int nb = q / ND, db = q % ND;
+    f32x16 y;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float x[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) x[w] = ml->acc[w][q * 16 + v][lane];
+#pragma unroll
+      for (int r = NW / 2; r >= 1; r /= 2)
+#pragma unroll
+        for (int w = 0; w < r; ++w) x[w] += x[w + r];
+      y[v] = x[0];
     }
-    __syncthreads();
-    if (wv < r) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[nb][db][v] += ml->acc[wv][(nb * ND + db) * 16 + v][lane];
-    }
-    __syncthreads();
-  }
-  if (wv != 0) return;
-
-  // ---- wave 0 writes the result of this split
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
+    const float mA = nb == 0 ? m_all[0] : m_all[NB - 1];
+    const float lA = nb == 0 ? l_all[0] : l_all[NB - 1];
     const int m = nb * 32 + col;
     if (DIRECT) {
       if (m >= R) continue;
       const int t = m / G, h = g * G + m % G;
       const float sink2 = p.sinks ? p.sinks[h] * kLog2e : kNegInf;
-      const float M = fmaxf(m_all[nb], sink2);
-      const float f = m_all[nb] == kNegInf ? 0.0f : exp2_fast(m_all[nb] - M);
-      const float denom = l_all[nb] * f + (sink2 == kNegInf ? 0.0f : exp2_fast(sink2 - M));
+      const float M = fmaxf(mA, sink2);
+      const float f = mA == kNegInf ? 0.0f : exp2_fast(mA - M);
+      const float denom = lA * f + (sink2 == kNegInf ? 0.0f : exp2_fast(sink2 - M));
       const float scale = f / denom;
-      uint16_t* op = p.o + (((long)b * p.T + t) * p.Hq + h) * D;
+      uint16_t* op = p.o + (((long)b * p.T + t) * p.Hq + h) * D + db * 32 + 4 * half;
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 y = {acc[nb][db][4 * a4] * scale, acc[nb][db][4 * a4 + 1] * scale,
-                           acc[nb][db][4 * a4 + 2] * scale, acc[nb][db][4 * a4 + 3] * scale};
-          *(bf16x4*)(op + db * 32 + 8 * a4 + 4 * half) = __builtin_convertvector(y, bf16x4);
-        }
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 z = {y[4 * a4] * scale, y[4 * a4 + 1] * scale, y[4 * a4 + 2] * scale, y[4 * a4 + 3] * scale};
+        *(bf16x4*)(op + 8 * a4) = __builtin_convertvector(z, bf16x4);
       }
     } else {
       const long prow = (((long)b * p.Hkv + g) * p.nsplit + s) * p.r_pad + m;
-      float* op = p.ws_o + prow * D;
+      float* op = p.ws_o + prow * D + db * 32 + 4 * half;
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 y = {acc[nb][db][4 * a4], acc[nb][db][4 * a4 + 1], acc[nb][db][4 * a4 + 2],
-                           acc[nb][db][4 * a4 + 3]};
-          *(f32x4*)(op + db * 32 + 8 * a4 + 4 * half) = y;
-        }
-      }
-      if (half == 0) {
-        p.ws_ml[prow * 2] = m_all[nb];
-        p.ws_ml[prow * 2 + 1] = l_all[nb];
+      for (int a4 = 0; a4 < 4; ++a4)
+        *(f32x4*)(op + 8 * a4) = f32x4{y[4 * a4], y[4 * a4 + 1], y[4 * a4 + 2], y[4 * a4 + 3]};
+      if (db == 0 && half == 0) {
+        p.ws_ml[prow * 2] = mA;
+        p.ws_ml[prow * 2 + 1] = lA;
       }
     }
   }
