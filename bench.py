@@ -173,6 +173,9 @@ def read_peaks():
                     out["hbm_copy_by"] = d["measure"]
             elif d["measure"].startswith("mfma_bf16"):
                 out["mfma_bf16_TFLOPs"] = d["TFLOP/s"]
+            elif d["measure"] == "hbm_read_cold_small":
+                out["hbm_read_cold_small_us"] = d["us_median"]
+                out["hbm_read_cold_small_bytes"] = d["bytes"]
     out["source"] = "profiles/mi355x_peaks.txt (swa_peaks)"
     return out
 
@@ -310,6 +313,12 @@ def run_verify(args, swa, torch, dev, stream, names=("verify_ga_b64", "verify_sw
             "GB/s": round(vbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(vbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
+        # small working sets: the floor is one cold read of the same bytes in
+        # one launch (swa_peaks' hbm_read_cold_small), not the streaming rate
+        pk = read_peaks() or {}
+        if pk.get("hbm_read_cold_small_bytes") == vbytes:
+            vres[name]["cold_read_floor_ms"] = round(pk["hbm_read_cold_small_us"] * 1e-3, 5)
+            vres[name]["frac_of_cold_read_floor"] = round(pk["hbm_read_cold_small_us"] * 1e-3 / ms, 4)
         del inp, ws, ov
         torch.cuda.empty_cache()
     ga = vres[names[0]]
