@@ -1255,22 +1255,31 @@ __global__ __launch_bounds__(kFuseWaves * 64) void bwd_fused_swa_kernel(BwdArgs 
     }
     return o;
   };
-  // dQ^T of block n into acc0 (acc1).  (Reading the next tile's operands
-  // during the current tile's MFMAs measured slower: the register rotation
-  // in the runtime loop waits for them anyway.)
+  // dQ^T of block n into acc0 (acc1).  Straight-line over the at most five
+  // live tiles, so every operand read can be issued ahead of the MFMAs: a
+  // step past the block's last live tile reads that tile again with a zero
+  // dS^T operand (its K and dS^T are finite, so it adds exact zeros).
   auto dq_compute = [&](int n, bool two) {
     const int buf = n & 1;
     const int tlo = fuse_lo(a, n, TQ), thi = fuse_hi(a, n, TQ);
     acc0 = f32x16{};
     acc1 = f32x16{};
-    for (int t = tlo; t <= thi; ++t) {
-      const DqOps cur = dq_ops(t, buf, two);
+    DqOps ops[NKW];
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        acc0 = mfma32(cur.a0[kc], cur.bop[kc], acc0);
-        if (two) acc1 = mfma32(cur.a1[kc], cur.bop[kc], acc1);
+    for (int i = 0; i < NKW; ++i) {
+      ops[i] = dq_ops(min(tlo + i, thi), buf, two);
+      if (tlo + i > thi) {
+        ops[i].bop[0] = bf16x8{};
+        ops[i].bop[1] = bf16x8{};
       }
     }
+#pragma unroll
+    for (int i = 0; i < NKW; ++i)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        acc0 = mfma32(ops[i].a0[kc], ops[i].bop[kc], acc0);
+        if (two) acc1 = mfma32(ops[i].a1[kc], ops[i].bop[kc], acc1);
+      }
   };
   // dq = scale * dQ^T of block n: lane (query col, half) holds d = 32 db +
   // 8 a4 + 4 half + 0..3; v_permlane32_swap gives lane half 0 the 8 values of
