@@ -58,6 +58,10 @@ CASES = [
     ("strips_chunk_g8", 1, 1202, 1402, 16, 2, 128, 128, True),
     ("strips_b2_nosink", 2, 1100, 1100, 8, 1, 128, 128, False),
     ("strips_w1_g8", 1, 1030, 1030, 8, 1, 128, 1, True),
+    # the fused kernel on a single (ragged) query block, with and without an
+    # offset: one strip of one block, fewer than five live key tiles
+    ("tiny_g8", 1, 3, 3, 16, 2, 128, 128, True),
+    ("tiny_g4_offset", 1, 5, 21, 8, 2, 128, 64, True),
 ]
 
 
