@@ -93,6 +93,24 @@ __device__ __forceinline__ void lds_dma16(const void* first_row, uint32_t num_re
                    : "m0");
 }
 
+// The descriptor lds_dma16 builds, for callers that keep one across several
+// loads: base, stride 0, num_records, the flags word of make_rsrc.
+__device__ __forceinline__ u32x4 buffer_desc(const void* base_ptr, uint32_t num_records) {
+  const uint64_t base = (uint64_t)(uintptr_t)base_ptr;
+  return u32x4{(uint32_t)base, (uint32_t)(base >> 32) & 0xffffu, num_records, 0x00020000u};
+}
+
+// lds_dma16 with a prebuilt descriptor and a scalar byte offset soffset
+// added to every lane's address (the range check is made on voffset alone,
+// so a lane past num_records still writes zeros and reads nothing); desc,
+// soffset and lds_byte must be wave-uniform.
+__device__ __forceinline__ void lds_dma16_soff(u32x4 desc, uint32_t soffset, uint32_t lds_byte, uint32_t voffset) {
+  __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(lds_byte), "v"(voffset), "s"(desc), "s"(soffset)
+                   : "m0");
+}
+
 // Plain global accesses with a cache policy (see kCacheNT).
 template <bool NT, typename T>
 __device__ __forceinline__ T load_pol(const T* p) {

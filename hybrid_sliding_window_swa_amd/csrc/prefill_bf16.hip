@@ -164,7 +164,8 @@ struct DmaTile {
   static constexpr int KP = CPR + 1, VP = CPR + 4;   // pitches in 16-byte slots
   static constexpr int NK = (32 * KP + 63) / 64, NV = (32 * VP + 63) / 64;
   static constexpr int NPT = NK + NV;                // windows per K + V tile pair
-  static constexpr uint32_t kOut = 0xFFFFFFF0u;      // an offset past any range
+  // an offset past any range, also with a few tiles' bytes added to it
+  static constexpr uint32_t kOut = 0x80000000u;
   // byte offset in global memory of lane `lane`'s 16 bytes of window j of a
   // K (is_k) or V tile whose rows are row_bytes apart
   static __device__ __forceinline__ uint32_t voff(bool is_k, int j, int lane, uint32_t row_bytes) {
@@ -531,6 +532,125 @@ struct QState {
     return sn;
   }
 
+  // Two weights rounded to bf16 and packed (the B operand of P V), and
+  // their fp32 values added to the row sum t.  The sum is formed with
+  // plain fp32 adds: gfx950's v_dot2_f32_bf16, which would sum the rounded
+  // weights, issues to the matrix-core pipeline and waits for every MFMA in
+  // flight (measured: 13 cycles of exclusive matrix-core time each), while
+  // a VALU add runs beside the MFMAs.  The row sum then holds the weights
+  // before their rounding (within 2^-9 of each rounded weight).
+  static __device__ __forceinline__ uint32_t pack_sum(float e0, float e1, float& t) {
+    const bf16x2 w2 = {(__bf16)e0, (__bf16)e1};
+    uint32_t w = __builtin_bit_cast(uint32_t, w2);
+    __asm__ volatile("" : "+v"(w));
+    t += e0 + e1;
+    return w;
+  }
+
+  // One step of the skewed pipeline of the no-window loop.  On entry pw
+  // holds the packed bf16 weights P(t) of tile t (already summed into l) and
+  // s the raw scores S(t+1) of tile t + 1.  The step issues O^T += V(t)^T
+  // P(t)^T (V tile v_t) and the score MFMAs of tile t + 2 (K tile k_next2,
+  // first key kb_next2) alternately, one of each per group, and between
+  // them the exponentials of S(t+1) against the shift in use, their bf16
+  // packing and their sum; then the rescale is decided from that sum as in
+  // fold_sum.  On exit pw holds P(t+1) (summed into l) and the masked S(t+2)
+  // is returned.  No MFMA of a step depends on the step's vector work, and
+  // the score chain is interleaved with independent P V products, so the
+  // matrix core has work while the exponentials issue.  Without PV (the
+  // first step) only the scores and the weights are formed.  `extra(c)` as
+  // in fold.
+  template <bool PV, typename X = NoExtra>
+  __device__ __forceinline__ f32x16 skew_step(const f32x16& s, uint32_t (&pw)[8], float c2, const uint16_t* v_t,
+                                              const uint16_t* k_next2, int kb_next2, int mask_next2, int window,
+                                              int half, int lane, const X& extra = X()) {
+    constexpr int EPM = 16 / Gm::NC;  // exponentials per group
+    constexpr int NPAIR = 8;          // packed weight pairs per tile
+    static_assert(Gm::NC == 2 * Gm::ND, "one P V MFMA per score MFMA");
+    const lds_u16* kbase = lane_base(lds_addr(k_next2), KTile<D>::k_lane_off(lane));
+    bf16x8 ka[Gm::NC];
+    bf16x8 va[2][Gm::ND];
+    bf16x8 pb[2];
+    if constexpr (PV) {
+      const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
+      // operands in the order the groups consume them
+#pragma unroll
+      for (int c = 0; c < Gm::NC; ++c) {
+        ka[c] = KTile<D>::k_operand(kbase, c);
+        va[c / Gm::ND][c % Gm::ND] = VTile<D>::vt_operand(vbase, c % Gm::ND, c / Gm::ND);
+      }
+      pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      pb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+    } else {
+#pragma unroll
+      for (int c = 0; c < Gm::NC; ++c) ka[c] = KTile<D>::k_operand(kbase, c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sn = {};
+    uint32_t pn[NPAIR];
+    float tsum = 0.0f;
+    float ex[EPM];
+    // group c: score MFMA c, P V MFMA c; pack the previous group's weights
+    // and add them to the sum; this group's exponentials
+#pragma unroll
+    for (int c = 0; c < Gm::NC; ++c) {
+      sn = mfma32(ka[c], q[c], sn);
+      if constexpr (PV) acc[c % Gm::ND] = mfma32(va[c / Gm::ND][c % Gm::ND], pb[c / Gm::ND], acc[c % Gm::ND]);
+      if (c > 0) {
+#pragma unroll
+        for (int e = 0; e < EPM; e += 2) pn[((c - 1) * EPM + e) >> 1] = pack_sum(ex[e], ex[e + 1], tsum);
+      }
+#pragma unroll
+      for (int e = 0; e < EPM; ++e) {
+        ex[e] = exp2_fast(fmaf(s[c * EPM + e], c2, -mu));
+        __asm__ volatile("" : "+v"(ex[e]));
+      }
+      extra(c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int e = 0; e < EPM; e += 2) pn[((Gm::NC - 1) * EPM + e) >> 1] = pack_sum(ex[e], ex[e + 1], tsum);
+    if (wave_any(!(tsum <= exp2_fast(kRescaleTau)))) {
+      // as fold_sum: shift by the tile's row max, rescale what has been
+      // accumulated (P V of tiles up to t, issued above), recompute
+      float mx = kNegInf;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = __builtin_elementwise_maximum(mx, s[v]);
+      const float m_new = __builtin_elementwise_maximum(mu, halves_max(mx) * c2);
+      const float alpha = exp2_fast(mu - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db) acc[db] *= alpha;
+      mu = m_new;
+      tsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NPAIR; ++j)
+        pn[j] = pack_sum(exp2_fast(fmaf(s[2 * j], c2, -mu)), exp2_fast(fmaf(s[2 * j + 1], c2, -mu)), tsum);
+    }
+    l_run += tsum;
+#pragma unroll
+    for (int j = 0; j < NPAIR; ++j) pw[j] = pn[j];
+    apply_mask(sn, kb_next2, mask_next2, window, half);
+    return sn;
+  }
+
+  // O^T += V^T P^T for the packed weights pw of the V tile v_t (the last
+  // tile of the skewed pipeline).
+  __device__ __forceinline__ void pv_only(const uint32_t (&pw)[8], const uint16_t* v_t, int lane) {
+    const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
+    bf16x8 va[2][Gm::ND];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db) va[kc][db] = VTile<D>::vt_operand(vbase, db, kc);
+    const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]}),
+                          __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]})};
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < Gm::ND; ++db) acc[db] = mfma32(va[kc][db], pb[kc], acc[db]);
+  }
+
   // Natural-log softmax denominator of each row, sink included, for the
   // backward: lse = (mu + log2 l) * ln 2, mu being the shift the accumulator
   // and l are kept at (the running max, or 0 while that is -inf), so the sum
@@ -577,8 +697,21 @@ __device__ __forceinline__ bool tile_needed(int kb, int wpos_lo, int wpos_hi, in
 
 // ----------------------------------------------------------------------------
 // One workgroup per block of TB tokens (global attention and general shapes).
-// K tiles are staged one tile ahead of V tiles, so while a wave
-// exponentiates tile kt it already computes the scores of tile kt + 1.
+// XCD-aware work order, longest (latest) blocks first.
+//
+// Without a window (NOWIN) the K/V tiles stream through a ring of eight
+// "pair slots" in LDS, each holding one K tile and one V tile in the padded
+// layouts of KTile / VTile, filled by direct-to-LDS loads in whole 1 KiB
+// windows.  The waves run the skewed pipeline of QState::skew_step: step t
+// multiplies P(t) into V(t), computes the scores of tile t + 2 and the
+// weights of tile t + 1, so the pair slot that step t reads holds V(t) and
+// K(t + 2), and step t fetches K(t + 6) and V(t + 4) into the slot step
+// t + 4 reads (last read four steps earlier).  Slots are numbered from the
+// first step of the four-step trips (single steps, a barrier each, come
+// first), so a trip reads slots rb .. rb + 3 and fills (rb ^ 4) .. (rb ^ 4) +
+// 3, rb alternating between 0 and 4: no slot index wraps inside a trip.
+// With a window: a 4-slot K/V ring staged through registers, two tiles per
+// barrier, each wave folding only the tiles of its own range (QState::fold).
 template <int D, int G, int NW, bool NOWIN>
 __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   using Gm = TileGeom<D>;
@@ -586,17 +719,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   constexpr int TW = 32 / G;        // tokens per wave
   constexpr int TB = TW * NW;       // tokens per workgroup
   static_assert(32 % G == 0, "a 32-row block must hold whole tokens");
-
-  // K/V ring: 8 slots without a window (four tiles per barrier), else 4.
-  // Without a window the main loop fills the slots with direct-to-LDS loads
-  // in whole 1 KiB windows (one wave-wide 16-byte load each), so each slot
-  // is rounded up to whole windows; the tile layout inside is the same.
-  constexpr int NS = NOWIN ? 8 : 4;
   using Dma = DmaTile<D>;
-  constexpr int KSLOT = NOWIN ? Dma::NK * 512 : Gm::K_ELEMS;
-  constexpr int VSLOT = NOWIN ? Dma::NV * 512 : Gm::V_ELEMS;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[NS][KSLOT];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[NS][VSLOT];
 
   // XCD-aware work item: workgroups on one XCD (blockIdx % 8) take consecutive
   // token blocks of one (b, g), latest (longest) first.
@@ -634,95 +757,43 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   const int wpos_hi = p.q_offset + min(tw0 + TW, p.Sq) - 1;
   const int wk0 = max(kt_begin, (W > 0 ? max(0, wpos_lo - W + 1) : 0) / KT);
   const int wk1 = tw0 < p.Sq ? wpos_hi / KT : -1;
-
-  // Tile t lives in K slot and V slot (t - kt_begin) % 4.  A step over two
-  // tiles kt, kt + 1 reads K(kt + 1), K(kt + 2), V(kt), V(kt + 1) and stages
-  // K(kt + 3), K(kt + 4), V(kt + 2), V(kt + 3); one barrier per two tiles.
-  Stager<D, NT> s0, s1;
-  s0.init(kv_tok, tid);
-  s1.init(kv_tok, tid);
-  float sink;
-  {
-    // the first PK K tiles and PV V tiles the loop expects resident: every
-    // load is issued before the first LDS store, so the block start waits
-    // for one memory round trip
-    constexpr int PK = NOWIN ? 5 : 3, PV = PK - 1;
-    Stager<D, NT> pro[PK];
-#pragma unroll
-    for (int i = 0; i < PK; ++i) {
-      pro[i].init(kv_tok, tid);
-      if (kt_begin + i <= kt_end) {
-        pro[i].load_k(kg, kv_tok, (kt_begin + i) * KT, key_end, tid);
-        if (i < PV) pro[i].load_v(vg, kv_tok, (kt_begin + i) * KT, key_end, tid);
-      }
-    }
-    sink = p.sinks ? p.sinks[g * G + col % G] : 0.0f;
-    if (!NOWIN) pro[0].zero_below(key_lo - kt_begin * KT, tid);
-#pragma unroll
-    for (int i = 0; i < PK; ++i)
-      if (kt_begin + i <= kt_end) {
-        pro[i].store_k(k_lds[i], tid);
-        if (i < PV) pro[i].store_v(v_lds[i], tid);
-      }
-  }
-  st.reset(p.sinks ? sink * kLog2e : kNegInf, half);
-  // Drain the prologue loads (queries, first tiles): inside the loop the only
-  // loads in flight are then the prefetches, and no wait for the queries can
-  // stall on them.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // Each fold of tile kt also computes the scores of tile kt + 1 (discarded
-  // after the last tile); the last tile of the workgroup is folded after the
-  // loop.  With a window, a wave folds only the tiles of its own range, and
-  // in the step before its first tile it folds a fully masked tile, which
-  // adds nothing, to get those scores.
-  auto tile_mask = [&](int kt) {  // kMaskAll before this wave's first tile
+  const float sink = p.sinks ? p.sinks[g * G + col % G] : 0.0f;
+  // (the mask of tile kt for this wave; kMaskAll before its first tile)
+  auto tile_mask = [&](int kt) {
     int mask;
     tile_needed(kt * KT, wpos_lo, wpos_hi, W, mask);
     return !NOWIN && kt < wk0 ? kMaskAll : mask;
   };
-  f32x16 s = {};
-  int kt = kt_begin;
+
   if constexpr (NOWIN) {
-    // No window: every wave's range starts at the workgroup's first tile, and
-    // a tile past a wave's last query is masked whole by the causal bound, so
-    // every wave folds every tile with no per-wave condition.  Tile t sits in
-    // slot (t - kt_begin) % 8; a step over tiles kt .. kt + 3 reads K(kt + 1
-    // .. kt + 4) and V(kt .. kt + 3) and stages K(kt + 5 .. kt + 8) and V(kt
-    // + 4 .. kt + 7) into the other slots: one barrier per four tiles, and
-    // the scores alternate between two register sets (no copy closes the
-    // loop).
-    s = st.scores(k_lds[0], lane);
-    st.prep(s, kt_begin * KT, tile_mask(kt_begin), W, c2, half);
-    // single steps first, so that a multiple of four tiles remains
-    for (const int kt_single = kt_begin + ((kt_end - kt_begin) & 3); kt < kt_single; ++kt) {
-      const int r = kt - kt_begin;
-      if (kt + 5 <= kt_end) s0.load_k(kg, kv_tok, (kt + 5) * KT, key_end, tid);
-      if (kt + 4 <= kt_end) s0.load_v(vg, kv_tok, (kt + 4) * KT, key_end, tid);
-      s = st.template fold_sum<true>(s, c2, v_lds[r & 7], k_lds[(r + 1) & 7], (kt + 1) * KT, tile_mask(kt + 1), W,
-                                     half, lane);
-      if (kt + 5 <= kt_end) s0.store_k(k_lds[(r + 5) & 7], tid);
-      if (kt + 4 <= kt_end) s0.store_v(v_lds[(r + 4) & 7], tid);
-      __syncthreads();
-    }
-    if (wv >= NW / 2) __builtin_amdgcn_s_setprio(1);
-    // first rows of K tile kt + 5 and V tile kt + 4, advanced by four tiles a
-    // step (an add instead of a 64-bit multiply per tile)
+    constexpr int PAIR = (Dma::NK + Dma::NV) * 512;  // bf16 elements per pair slot: K tile, then V tile
+    constexpr int VREG = Dma::NK * 512;              // the V tile's offset in a slot
+    constexpr uint32_t PAIR_B = 2u * PAIR;
+    // The NPT 1 KiB windows of a step's K + V tile pair, padded to WPW per
+    // wave: wave wv fills windows wv, wv + NW, ..., WPW of them every step
+    // (so its per-lane offsets are fixed); a window past NPT is a dummy whose
+    // lanes all read out of range and write zeros into dma_sink (no memory
+    // access), so every wave issues the same loads with no branch.
+    constexpr int WPW = (Dma::NPT + NW - 1) / NW;
+    static_assert(WPW + 1 <= Gm::NC, "one load per group of a step");
+    __shared__ __attribute__((aligned(16))) uint16_t ring[8][PAIR];
+    __shared__ __attribute__((aligned(16))) uint16_t dma_sink[512];
+
     const long tstride = (long)KT * kv_tok;
     const uint32_t row_b = (uint32_t)(2 * kv_tok), pad_b = (uint32_t)(2 * (kv_tok - D));
-    const uint16_t* kp = kg + (kt + 5) * tstride;
-    const uint16_t* vp = vg + (kt + 4) * tstride;
-    using Stg = Stager<D, NT>;
-    // The step's K/V tiles for the next step, K(kt + 5 .. kt + 8) and V(kt +
-    // 4 .. kt + 7), go straight from memory into their LDS slots (last read
-    // in the previous step).  A K + V tile pair is NPT 1 KiB windows; wave
-    // wv fills windows wv, wv + NW, ... of every pair (the same windows each
-    // step, so its per-lane offsets are fixed), tile i's loads issued during
-    // fold i, one per score MFMA.  Nothing stages through registers and the
-    // only wait is at the step's end, a whole step after the loads issue.
-    constexpr int WPW = (Dma::NPT + NW - 1) / NW;   // windows per wave and tile pair (at most)
-    static_assert(WPW + 1 <= Gm::NC, "one load per score MFMA of a fold");
+    const uint32_t tile_b = (uint32_t)KT * row_b;
+    const uint32_t full_rec = tile_b - pad_b;
+    // records of tile t: rows at or past key_end read as zeros
+    auto tile_rec = [&](int t) {
+      return t * KT + KT <= key_end ? full_rec : (uint32_t)(key_end - t * KT) * row_b - pad_b;
+    };
+    const int singles = (kt_end - kt_begin) & 3;
+    const int kt0 = kt_begin + singles;  // first step of the four-step trips
+    // pair slot read by step t (V(t), K(t + 2))
+    auto pslot = [&](int t) { return (t - kt0) & 7; };
+    const uint32_t ring0 = lds_addr(ring[0]);
+
+    // this wave's windows: global byte offset per lane, LDS offset in a slot
     uint32_t dma_off[WPW], dma_lds[WPW];
     bool dma_k[WPW], dma_on[WPW];
 #pragma unroll
@@ -731,50 +802,158 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
       dma_on[k] = rr < Dma::NPT;
       dma_k[k] = rr < Dma::NK;
       const int win = dma_k[k] ? rr : rr - Dma::NK;
-      dma_off[k] = dma_on[k] ? Dma::voff(dma_k[k], win, lane, row_b) : 0u;
-      dma_lds[k] = 1024u * (uint32_t)win;
+      dma_off[k] = dma_on[k] ? Dma::voff(dma_k[k], win, lane, row_b) : Dma::kOut;
+      dma_lds[k] = dma_k[k] ? 1024u * (uint32_t)win : 2u * VREG + 1024u * (uint32_t)win;
     }
-    const uint32_t k_ring0 = lds_addr(k_lds[0]), v_ring0 = lds_addr(v_lds[0]);
-    const uint32_t full_rec = (uint32_t)KT * row_b - pad_b;
-    for (; kt < kt_end; kt += 4, kp += 4 * tstride, vp += 4 * tstride) {
-      const int r = kt - kt_begin;
-      // window k of tile pair i: K(kt + 5 + i) or V(kt + 4 + i)
-      auto dma = [&](int i, int k) {
-        if (!dma_on[k]) return;
-        const int t = kt + (dma_k[k] ? 5 : 4) + i;
-        if (t > kt_end) return;
-        const uint16_t* first = (dma_k[k] ? kp : vp) + i * tstride;
-        const uint32_t nrec = t * KT + KT <= key_end ? full_rec : (uint32_t)(key_end - t * KT) * row_b - pad_b;
-        const uint32_t slot = (uint32_t)((t - kt_begin) & 7);
-        const uint32_t lds = (dma_k[k] ? k_ring0 + slot * (uint32_t)(2 * KSLOT) : v_ring0 + slot * (uint32_t)(2 * VSLOT)) +
-                             dma_lds[k];
-        Dma::load(first, nrec, lds, dma_off[k]);
-      };
-      auto issue = [&](int f, int c) {
-        if (c >= 1 && c <= WPW) dma(f, c - 1);
-      };
-      // within the step each fold reads the first K operands of the next
-      // fold's tile ahead (all four tiles are resident since the barrier)
-      bf16x8 kpre[QState<D>::KPRE];
-      const f32x16 sa = st.template fold_sum<true, false, true>(
-          s, c2, v_lds[r & 7], k_lds[(r + 1) & 7], (kt + 1) * KT, tile_mask(kt + 1), W, half, lane,
-          [&](int c) { issue(0, c); }, kpre, k_lds[(r + 2) & 7]);
-      const f32x16 sb = st.template fold_sum<true, true, true>(
-          sa, c2, v_lds[(r + 1) & 7], k_lds[(r + 2) & 7], (kt + 2) * KT, tile_mask(kt + 2), W, half, lane,
-          [&](int c) { issue(1, c); }, kpre, k_lds[(r + 3) & 7]);
-      const f32x16 sc = st.template fold_sum<true, true, true>(
-          sb, c2, v_lds[(r + 2) & 7], k_lds[(r + 3) & 7], (kt + 3) * KT, tile_mask(kt + 3), W, half, lane,
-          [&](int c) { issue(2, c); }, kpre, k_lds[(r + 4) & 7]);
-      s = st.template fold_sum<true, true, false>(sc, c2, v_lds[(r + 3) & 7], k_lds[(r + 4) & 7], (kt + 4) * KT,
-                                              tile_mask(kt + 4), W, half, lane, [&](int c) { issue(3, c); },
-                                              kpre);
+    const uint32_t sink_lds = lds_addr(dma_sink);
+
+    // Prologue: K(kt_begin .. + 5) and V(kt_begin .. + 3), window i of them
+    // by wave i mod NW; K(t) goes to the slot of step t - 2.
+    {
+      constexpr int PK = 6, PV = 4;
+      for (int i = wv; i < PK * Dma::NK + PV * Dma::NV; i += NW) {
+        const bool is_k = i < PK * Dma::NK;
+        const int j = is_k ? i : i - PK * Dma::NK;
+        const int nw = is_k ? Dma::NK : Dma::NV;
+        const int t = kt_begin + j / nw, win = j % nw;
+        if (t > kt_end) continue;
+        const uint32_t lds = ring0 + (uint32_t)pslot(is_k ? t - 2 : t) * PAIR_B + (is_k ? 0u : 2u * VREG) +
+                             1024u * (uint32_t)win;
+        Dma::load((is_k ? kg : vg) + t * tstride, tile_rec(t), lds, Dma::voff(is_k, win, lane, row_b));
+      }
+    }
+    st.reset(p.sinks ? sink * kLog2e : kNegInf, half);
+    // drain the prologue loads (queries, first tiles): inside the loop the
+    // only loads in flight are then the prefetches
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // every wave's range starts at the workgroup's first tile, and a tile
+    // past a wave's last query is masked whole by the causal bound, so every
+    // wave folds every tile with no per-wave condition
+    f32x16 s = st.scores(&ring[pslot(kt_begin - 2)][0], lane);
+    st.prep(s, kt_begin * KT, tile_mask(kt_begin), W, c2, half);
+    uint32_t pw[8];
+    s = st.template skew_step<false>(s, pw, c2, nullptr, &ring[pslot(kt_begin - 1)][0], (kt_begin + 1) * KT,
+                                     tile_mask(kt_begin + 1), W, half, lane);
+    // the slots of K(kt_begin) and K(kt_begin + 1) are refilled two and three
+    // steps on: every wave has read them before that
+    __syncthreads();
+
+    // General step t (single steps and the last trips): bounds-checked loads
+    // of the tiles that exist, the mask of tile t + 2.
+    auto general_step = [&](int t) {
+      const int r = pslot(t);
+      s = st.template skew_step<true>(s, pw, c2, &ring[r][VREG], &ring[r][0], (t + 2) * KT, tile_mask(t + 2), W,
+                                      half, lane, [&](int c) {
+                                        if (c >= 1 && c <= WPW) {
+                                          const int k = c - 1;
+                                          const int tt = t + (dma_k[k] ? 6 : 4);
+                                          if (dma_on[k] && tt <= kt_end)
+                                            Dma::load((dma_k[k] ? kg : vg) + tt * tstride, tile_rec(tt),
+                                                      ring0 + (uint32_t)pslot(t + 4) * PAIR_B + dma_lds[k],
+                                                      dma_off[k]);
+                                        }
+                                      });
+    };
+    int kt = kt_begin;
+    for (; kt < kt0; ++kt) {
+      general_step(kt);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (wv >= NW / 2) __builtin_amdgcn_s_setprio(1);
+    // Four-step trips.  Window k's loads of a trip share one buffer
+    // descriptor based at the first row of the tile it fetches in the
+    // trip's first step (K(kt + 6) or V(kt + 4)), with its range cut at
+    // key_end: step i adds i tiles to the lane offsets, rows at or past
+    // key_end (and tiles past kt_end) read as zeros without a memory access,
+    // and lanes pointed at kOut (row padding, dummy windows) stay out of
+    // range.  The score tiles of a trip need no mask unless its last one
+    // (kt + 5) reaches a query position.
+    const uint16_t* bp[WPW];
+#pragma unroll
+    for (int k = 0; k < WPW; ++k) bp[k] = dma_k[k] ? kg + (kt + 6) * tstride : vg + (kt + 4) * tstride;
+    const uint32_t trip_rec = 3u * tile_b + full_rec;
+    uint32_t m0_step[WPW];  // LDS stride of window k from one step to the next (0: the sink)
+#pragma unroll
+    for (int k = 0; k < WPW; ++k) m0_step[k] = dma_on[k] ? PAIR_B : 0u;
+    for (uint32_t rb = 0; kt < kt_end; kt += 4, rb ^= 4u) {
+      const bool masked = (kt + 5) * KT + KT - 1 > pos_lo;
+      u32x4 desc[WPW];
+      uint32_t m0k[WPW];
+#pragma unroll
+      for (int k = 0; k < WPW; ++k) {
+        // keys of window k's tiles this trip: from (kt + 6) or (kt + 4) tiles on
+        const int key0 = (kt + (dma_k[k] ? 6 : 4)) * KT;
+        const int rows = min(key_end - key0, 4 * KT);
+        desc[k] = buffer_desc(bp[k], rows <= 0 ? 0u : min(trip_rec, (uint32_t)rows * row_b - pad_b));
+        bp[k] += 4 * tstride;
+        m0k[k] = dma_on[k] ? ring0 + (rb ^ 4u) * PAIR_B + dma_lds[k] : sink_lds;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t* slot = &ring[rb + i][0];
+        s = st.template skew_step<true>(s, pw, c2, slot + VREG, slot, (kt + i + 2) * KT,
+                                        masked ? tile_mask(kt + i + 2) : 0, W, half, lane, [&](int c) {
+                                          if (c >= 1 && c <= WPW) {
+                                            const int k = c - 1;
+                                            lds_dma16_soff(desc[k], 0u, m0k[k] + (uint32_t)i * m0_step[k],
+                                                           dma_off[k] + (uint32_t)i * tile_b);
+                                          }
+                                        });
+      }
       // every direct-to-LDS load of this wave has landed before the barrier
       // that hands the slots to the other waves
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    st.template fold_sum<false>(s, c2, v_lds[(kt_end - kt_begin) & 7], nullptr, 0, 0, W, half, lane);
+    st.pv_only(pw, &ring[pslot(kt_end)][VREG], lane);
   } else {
+    // K/V ring of four slots, staged through registers; tile t in slot
+    // (t - kt_begin) % 4.  A step over two tiles kt, kt + 1 reads K(kt + 1),
+    // K(kt + 2), V(kt), V(kt + 1) and stages K(kt + 3), K(kt + 4), V(kt + 2),
+    // V(kt + 3); one barrier per two tiles.
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[4][Gm::K_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[4][Gm::V_ELEMS];
+    Stager<D, NT> s0, s1;
+    s0.init(kv_tok, tid);
+    s1.init(kv_tok, tid);
+    {
+      // the first PK K tiles and PV V tiles the loop expects resident: every
+      // load is issued before the first LDS store, so the block start waits
+      // for one memory round trip
+      constexpr int PK = 3, PV = PK - 1;
+      Stager<D, NT> pro[PK];
+#pragma unroll
+      for (int i = 0; i < PK; ++i) {
+        pro[i].init(kv_tok, tid);
+        if (kt_begin + i <= kt_end) {
+          pro[i].load_k(kg, kv_tok, (kt_begin + i) * KT, key_end, tid);
+          if (i < PV) pro[i].load_v(vg, kv_tok, (kt_begin + i) * KT, key_end, tid);
+        }
+      }
+      pro[0].zero_below(key_lo - kt_begin * KT, tid);
+#pragma unroll
+      for (int i = 0; i < PK; ++i)
+        if (kt_begin + i <= kt_end) {
+          pro[i].store_k(k_lds[i], tid);
+          if (i < PV) pro[i].store_v(v_lds[i], tid);
+        }
+    }
+    st.reset(p.sinks ? sink * kLog2e : kNegInf, half);
+    // drain the prologue loads (queries, first tiles): inside the loop the
+    // only loads in flight are then the prefetches
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // Each fold of tile kt also computes the scores of tile kt + 1 (discarded
+    // after the last tile); the last tile of the workgroup is folded after
+    // the loop.  A wave folds only the tiles of its own range, and in the
+    // step before its first tile it folds a fully masked tile, which adds
+    // nothing, to get those scores.
+    f32x16 s = {};
+    int kt = kt_begin;
     if (wk0 == kt_begin && wk1 >= 0) {
       s = st.scores(k_lds[0], lane);
       st.prep(s, kt_begin * KT, tile_mask(kt_begin), W, c2, half);
