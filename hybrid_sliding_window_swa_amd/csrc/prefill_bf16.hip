@@ -39,6 +39,8 @@
 //   per token block, K/V tiles staged two at a time in a four-slot ring (K one
 //   tile ahead of V, one barrier per two tiles), XCD-aware order with
 //   the longest (latest) blocks first.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -560,46 +562,81 @@ struct QState {
   // matrix core has work while the exponentials issue.  Without PV (the
   // first step) only the scores and the weights are formed.  `extra(c)` as
   // in fold.
-  template <bool PV, typename X = NoExtra>
+  // K and V^T operands of a step's first groups, read during the previous
+  // step (skew_step's PRE_IN / PRE_OUT).
+  static constexpr int SKEW_PRE = 2;
+  struct SkewOps {
+    bf16x8 k[SKEW_PRE];
+    bf16x8 v[SKEW_PRE];
+  };
+
+  // The operands of group c are read SKEW_PRE groups ahead, during group c -
+  // SKEW_PRE, so the reads of the eight waves spread over the step instead
+  // of queueing at its start.  With PRE_IN the operands of groups 0 ..
+  // SKEW_PRE - 1 come from ops (read by the previous step), else they are
+  // read at the start; with PRE_OUT the last groups read those of the next
+  // step (V tile v_after, K tile k_after) into ops.
+  template <bool PV, int PRE_IN = 0, int PRE_OUT = 0, typename X = NoExtra>
   __device__ __forceinline__ f32x16 skew_step(const f32x16& s, uint32_t (&pw)[8], float c2, const uint16_t* v_t,
                                               const uint16_t* k_next2, int kb_next2, int mask_next2, int window,
-                                              int half, int lane, const X& extra = X()) {
+                                              int half, int lane, const X& extra = X(), SkewOps* ops = nullptr,
+                                              const uint16_t* v_after = nullptr, const uint16_t* k_after = nullptr) {
     constexpr int EPM = 16 / Gm::NC;  // exponentials per group
     constexpr int NPAIR = 8;          // packed weight pairs per tile
+    constexpr int RA = SKEW_PRE;      // read-ahead distance in groups
     static_assert(Gm::NC == 2 * Gm::ND, "one P V MFMA per score MFMA");
+    static_assert((PRE_IN == 0 || PRE_IN == RA) && (PRE_OUT == 0 || PRE_OUT == RA) && RA < Gm::NC,
+                  "read-ahead depth");
     const lds_u16* kbase = lane_base(lds_addr(k_next2), KTile<D>::k_lane_off(lane));
+    const lds_u16* vbase = PV ? lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane)) : nullptr;
     bf16x8 ka[Gm::NC];
     bf16x8 va[2][Gm::ND];
     bf16x8 pb[2];
-    if constexpr (PV) {
-      const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
-      // operands in the order the groups consume them
+    auto read_group = [&](int c) {
+      ka[c] = KTile<D>::k_operand(kbase, c);
+      if constexpr (PV) va[c / Gm::ND][c % Gm::ND] = VTile<D>::vt_operand(vbase, c % Gm::ND, c / Gm::ND);
+    };
 #pragma unroll
-      for (int c = 0; c < Gm::NC; ++c) {
-        ka[c] = KTile<D>::k_operand(kbase, c);
-        va[c / Gm::ND][c % Gm::ND] = VTile<D>::vt_operand(vbase, c % Gm::ND, c / Gm::ND);
+    for (int c = 0; c < RA; ++c) {
+      if (PRE_IN > 0) {
+        ka[c] = ops->k[c];
+        va[c / Gm::ND][c % Gm::ND] = ops->v[c];
+      } else {
+        read_group(c);
       }
+    }
+    if constexpr (PV) {
       pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
       pb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
-    } else {
-#pragma unroll
-      for (int c = 0; c < Gm::NC; ++c) ka[c] = KTile<D>::k_operand(kbase, c);
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x16 sn = {};
     uint32_t pn[NPAIR];
     float tsum = 0.0f;
     float ex[EPM];
-    // group c: score MFMA c, P V MFMA c; pack the previous group's weights
-    // and add them to the sum; this group's exponentials
+    // group c: score MFMA c; the operands of group c + RA; pack the previous
+    // group's weights and add them to the sum; P V MFMA c; this group's
+    // exponentials
 #pragma unroll
     for (int c = 0; c < Gm::NC; ++c) {
       sn = mfma32(ka[c], q[c], sn);
-      if constexpr (PV) acc[c % Gm::ND] = mfma32(va[c / Gm::ND][c % Gm::ND], pb[c / Gm::ND], acc[c % Gm::ND]);
+      if (c + RA < Gm::NC) {
+        read_group(c + RA);
+      } else if constexpr (PRE_OUT > 0) {
+        const int j = c + RA - Gm::NC;
+        const lds_u16* kb2 = lane_base(lds_addr(k_after), KTile<D>::k_lane_off(lane));
+        const lds_u16* vb2 = lane_base(lds_addr(v_after), VTile<D>::vt_lane_off(lane));
+        ops->k[j] = KTile<D>::k_operand(kb2, j);
+        ops->v[j] = VTile<D>::vt_operand(vb2, j % Gm::ND, j / Gm::ND);
+      }
       if (c > 0) {
 #pragma unroll
         for (int e = 0; e < EPM; e += 2) pn[((c - 1) * EPM + e) >> 1] = pack_sum(ex[e], ex[e + 1], tsum);
       }
+      // the P V MFMA issues once the score MFMA is well under way, so the
+      // wave does not stall on it with its vector work queued behind
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (PV) acc[c % Gm::ND] = mfma32(va[c / Gm::ND][c % Gm::ND], pb[c / Gm::ND], acc[c % Gm::ND]);
 #pragma unroll
       for (int e = 0; e < EPM; ++e) {
         ex[e] = exp2_fast(fmaf(s[c * EPM + e], c2, -mu));
@@ -891,18 +928,29 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
         bp[k] += 4 * tstride;
         m0k[k] = dma_on[k] ? ring0 + (rb ^ 4u) * PAIR_B + dma_lds[k] : sink_lds;
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      // steps 1 .. 3 of the trip get their first operands read by the step
+      // before (the slots of a trip are all resident since its barrier)
+      typename QState<D>::SkewOps ops;
+      auto trip_step = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
         uint16_t* slot = &ring[rb + i][0];
-        s = st.template skew_step<true>(s, pw, c2, slot + VREG, slot, (kt + i + 2) * KT,
-                                        masked ? tile_mask(kt + i + 2) : 0, W, half, lane, [&](int c) {
-                                          if (c >= 1 && c <= WPW) {
-                                            const int k = c - 1;
-                                            lds_dma16_soff(desc[k], 0u, m0k[k] + (uint32_t)i * m0_step[k],
-                                                           dma_off[k] + (uint32_t)i * tile_b);
-                                          }
-                                        });
-      }
+        uint16_t* after = &ring[rb + (i < 3 ? i + 1 : i)][0];
+        constexpr int PRE = QState<D>::SKEW_PRE;
+        constexpr int PIN = i > 0 ? PRE : 0, POUT = i < 3 ? PRE : 0;
+        s = st.template skew_step<true, PIN, POUT>(
+            s, pw, c2, slot + VREG, slot, (kt + i + 2) * KT, masked ? tile_mask(kt + i + 2) : 0, W, half, lane,
+            [&](int c) {
+              if (c >= 1 && c <= WPW) {
+                const int k = c - 1;
+                lds_dma16_soff(desc[k], 0u, m0k[k] + (uint32_t)i * m0_step[k], dma_off[k] + (uint32_t)i * tile_b);
+              }
+            },
+            &ops, after + VREG, after);
+      };
+      trip_step(std::integral_constant<int, 0>());
+      trip_step(std::integral_constant<int, 1>());
+      trip_step(std::integral_constant<int, 2>());
+      trip_step(std::integral_constant<int, 3>());
       // every direct-to-LDS load of this wave has landed before the barrier
       // that hands the slots to the other waves
       __builtin_amdgcn_s_waitcnt(0);
