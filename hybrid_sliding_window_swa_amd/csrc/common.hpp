@@ -213,15 +213,26 @@ using VTile = PadTile<D, D + 32>;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Sum of the 16 bf16 weights of two bf16x8 vectors into acc (fp32), two per
-// v_dot2_f32_bf16: the row sum uses exactly the rounded weights that enter P V.
-__device__ __forceinline__ float sum_bf16x16(const bf16x8& a, const bf16x8& b, float acc) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#define SWA_DOT2(v, i) acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, i, i + 1), one, acc, false)
-  SWA_DOT2(a, 0); SWA_DOT2(a, 2); SWA_DOT2(a, 4); SWA_DOT2(a, 6);
-  SWA_DOT2(b, 0); SWA_DOT2(b, 2); SWA_DOT2(b, 4); SWA_DOT2(b, 6);
-#undef SWA_DOT2
-  return acc;
+// Two weights rounded to bf16 and packed (a pair of the B operand of P V),
+// and their sum added to the row sum t: with ROUNDED the rounded weights
+// that enter P V (one v_dot2_f32_bf16), else the fp32 weights before the
+// rounding (within 2^-9 of each rounded weight; two VALU adds).  gfx950's
+// v_dot2_f32_bf16 issues to the matrix-core pipeline and waits for every
+// MFMA in flight (measured: 13 cycles of exclusive matrix-core time each),
+// while an add runs beside the MFMAs: kernels that keep the matrix core
+// busy take the adds, the others the rounded sum.
+template <bool ROUNDED = false>
+__device__ __forceinline__ uint32_t pack_sum(float e0, float e1, float& t) {
+  const bf16x2 w2 = {(__bf16)e0, (__bf16)e1};
+  uint32_t w = __builtin_bit_cast(uint32_t, w2);
+  __asm__ volatile("" : "+v"(w));
+  if constexpr (ROUNDED) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, t, false);
+  } else {
+    t += e0 + e1;
+  }
+  return w;
 }
 
 // Wave-local LDS ordering: make this wave's LDS writes visible to its other

@@ -189,8 +189,9 @@ struct NoExtra {
 };
 
 // Per-lane state of one 32-query block; row m of the block is (token m / G,
-// head m % G), and lane l holds query column l % 32.
-template <int D>
+// head m % G), and lane l holds query column l % 32.  RSUM: the row sums add
+// the rounded weights (pack_sum<true>), else the weights before rounding.
+template <int D, bool RSUM = false>
 struct QState {
   using Gm = TileGeom<D>;
   bf16x8 q[Gm::NC];
@@ -288,12 +289,13 @@ struct QState {
     update_max(mx, c2);
   }
 
-  // P = exp2(s*c2 - mu) rounded to bf16, l += sum P, O^T += V^T P^T for the V
-  // tile v_t.  With NEXT the scores of the K tile k_next (first key kb_next)
-  // are computed in the same instruction stream, masked, reduced to their
+  // P = exp2(s*c2 - mu) rounded to bf16, l += the sum of the weights
+  // (pack_sum), O^T += V^T P^T for the V tile v_t.  With NEXT the scores of
+  // the K tile k_next (first key kb_next) are computed in the same
+  // instruction stream, masked, reduced to their
   // row max and folded into the running max (so mu is ready for them) and
-  // returned.  Each score MFMA is followed by a share of the exponentials,
-  // each P V MFMA by a share of the row sums and of the next row max
+  // returned.  Each score MFMA is followed by a share of the exponentials
+  // and their sums, each P V MFMA by a share of the next row max
   // (scheduling fences keep that order), so the matrix core and the vector
   // ALU of the SIMD work at the same time.
   // `extra(c)` runs right after score MFMA c (work that then issues while
@@ -332,12 +334,7 @@ struct QState {
         sn = mfma32(ka[c], q[c], sn);
         if (c > 0) {
 #pragma unroll
-          for (int e = 0; e < EPM; e += 2) {
-            const bf16x2 w2 = {(__bf16)ex[e], (__bf16)ex[e + 1]};
-            uint32_t w = __builtin_bit_cast(uint32_t, w2);
-            __asm__ volatile("" : "+v"(w));
-            pw[((c - 1) * EPM + e) >> 1] = w;
-          }
+          for (int e = 0; e < EPM; e += 2) pw[((c - 1) * EPM + e) >> 1] = pack_sum<RSUM>(ex[e], ex[e + 1], l_run);
         }
 #pragma unroll
         for (int e = 0; e < EPM; ++e) {
@@ -348,16 +345,13 @@ struct QState {
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int e = 0; e < EPM; e += 2) {
-        const bf16x2 w2 = {(__bf16)ex[e], (__bf16)ex[e + 1]};
-        pw[((Gm::NC - 1) * EPM + e) >> 1] = __builtin_bit_cast(uint32_t, w2);
-      }
+      for (int e = 0; e < EPM; e += 2) pw[((Gm::NC - 1) * EPM + e) >> 1] = pack_sum<RSUM>(ex[e], ex[e + 1], l_run);
       pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
       pb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
       apply_mask(sn, kb_next, mask_next, window, half);
-      // O^T += V^T P^T (keys 16kc .. 16kc+15 per MFMA) with the row sums of
-      // P and the row max of the next scores in between; the second key half
-      // of V is read while the first is multiplied
+      // O^T += V^T P^T (keys 16kc .. 16kc+15 per MFMA) with the row max of
+      // the next scores in between; the second key half of V is read while
+      // the first is multiplied
 #pragma unroll
       for (int db = 0; db < Gm::ND; ++db) va[1][db] = VTile<D>::vt_operand(vbase, db, 1);
       float mx = kNegInf;
@@ -374,14 +368,8 @@ struct QState {
           }
         }
 #pragma unroll
-        for (int j = i * 8 / NPV; j < (i + 1) * 8 / NPV; ++j) {
-          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-          const bf16x8& pv = pb[j >> 2];
-          const int e = 2 * (j & 3);
-          const bf16x2 pair = {pv[e], pv[e + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, one, l_run, false);
+        for (int j = i * 8 / NPV; j < (i + 1) * 8 / NPV; ++j)
           mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(sn[2 * j], sn[2 * j + 1]));
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
       update_max(mx, c2);
@@ -390,20 +378,23 @@ struct QState {
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int db = 0; db < Gm::ND; ++db) va[kc][db] = VTile<D>::vt_operand(vbase, db, kc);
+      uint32_t pw[8];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) pb[v >> 3][v & 7] = (__bf16)exp2_fast(fmaf(s[v], c2, -mu));
+      for (int j = 0; j < 8; ++j)
+        pw[j] = pack_sum<RSUM>(exp2_fast(fmaf(s[2 * j], c2, -mu)), exp2_fast(fmaf(s[2 * j + 1], c2, -mu)), l_run);
+      pb[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      pb[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int db = 0; db < Gm::ND; ++db) acc[db] = mfma32(va[kc][db], pb[kc], acc[db]);
-      l_run = sum_bf16x16(pb[0], pb[1], l_run);
     }
     return sn;
   }
 
   // Fold of one tile whose rescale need is decided by its weights' sum (the
   // no-window loop): P = exp2(s*c2 - mu) with the current shift, rounded to
-  // bf16, then this lane's sum of its 16 rounded weights.  A weight above
+  // bf16, then this lane's sum of its 16 weights (pack_sum).  A weight above
   // 2^kRescaleTau forces that sum above it, so when no lane's sum exceeds it
   // every weight is bounded as under the max-based rule, and no row max is
   // needed: the check is one compare per lane before P V.  Otherwise (rare:
@@ -420,7 +411,6 @@ struct QState {
     constexpr int EPM = 16 / Gm::NC;  // exponentials per score MFMA
     constexpr int NPAIR = 8;          // packed weight pairs per tile
     const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     f32x16 sn = {};
     uint32_t pw[NPAIR];
     float tsum = 0.0f;
@@ -433,28 +423,15 @@ struct QState {
 #pragma unroll
       for (int db = 0; db < Gm::ND; ++db) va[0][db] = VTile<D>::vt_operand(vbase, db, 0);
       __builtin_amdgcn_sched_barrier(0);
-      // group c: score MFMA c; pack the previous group's weights; add the
-      // pair packed one group earlier to the sum; this group's exponentials
+      // group c: score MFMA c; pack the previous group's weights and add
+      // them to the sum; this group's exponentials
       float ex[EPM];
 #pragma unroll
       for (int c = 0; c < Gm::NC; ++c) {
         sn = mfma32(ka[c], q[c], sn);
         if (c > 0) {
 #pragma unroll
-          for (int e = 0; e < EPM; e += 2) {
-            const bf16x2 w2 = {(__bf16)ex[e], (__bf16)ex[e + 1]};
-            uint32_t w = __builtin_bit_cast(uint32_t, w2);
-            __asm__ volatile("" : "+v"(w));
-            pw[((c - 1) * EPM + e) >> 1] = w;
-          }
-          if (c > 1) {
-#pragma unroll
-            for (int e = 0; e < EPM; e += 2) {
-              tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[((c - 2) * EPM + e) >> 1]), one,
-                                                     tsum, false);
-              __asm__ volatile("" : "+v"(tsum));
-            }
-          }
+          for (int e = 0; e < EPM; e += 2) pw[((c - 1) * EPM + e) >> 1] = pack_sum<RSUM>(ex[e], ex[e + 1], tsum);
         }
 #pragma unroll
         for (int e = 0; e < EPM; ++e) {
@@ -465,26 +442,15 @@ struct QState {
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int e = 0; e < EPM; e += 2) {
-        const bf16x2 w2 = {(__bf16)ex[e], (__bf16)ex[e + 1]};
-        pw[((Gm::NC - 1) * EPM + e) >> 1] = __builtin_bit_cast(uint32_t, w2);
-      }
-#pragma unroll
-      for (int c = Gm::NC - 2; c < Gm::NC; ++c)
-#pragma unroll
-        for (int e = 0; e < EPM; e += 2)
-          tsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[(c * EPM + e) >> 1]), one, tsum, false);
+      for (int e = 0; e < EPM; e += 2) pw[((Gm::NC - 1) * EPM + e) >> 1] = pack_sum<RSUM>(ex[e], ex[e + 1], tsum);
     } else {
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int db = 0; db < Gm::ND; ++db) va[kc][db] = VTile<D>::vt_operand(vbase, db, kc);
 #pragma unroll
-      for (int j = 0; j < NPAIR; ++j) {
-        const bf16x2 w2 = {(__bf16)exp2_fast(fmaf(s[2 * j], c2, -mu)), (__bf16)exp2_fast(fmaf(s[2 * j + 1], c2, -mu))};
-        pw[j] = __builtin_bit_cast(uint32_t, w2);
-        tsum = __builtin_amdgcn_fdot2_f32_bf16(w2, one, tsum, false);
-      }
+      for (int j = 0; j < NPAIR; ++j)
+        pw[j] = pack_sum<RSUM>(exp2_fast(fmaf(s[2 * j], c2, -mu)), exp2_fast(fmaf(s[2 * j + 1], c2, -mu)), tsum);
     }
     if (wave_any(!(tsum <= exp2_fast(kRescaleTau)))) {
       // a weight may exceed 2^tau (or be non-finite): shift by the tile's row max
@@ -502,11 +468,8 @@ struct QState {
       mu = m_new;
       tsum = 0.0f;
 #pragma unroll
-      for (int j = 0; j < NPAIR; ++j) {
-        const bf16x2 w2 = {(__bf16)exp2_fast(fmaf(s[2 * j], c2, -mu)), (__bf16)exp2_fast(fmaf(s[2 * j + 1], c2, -mu))};
-        pw[j] = __builtin_bit_cast(uint32_t, w2);
-        tsum = __builtin_amdgcn_fdot2_f32_bf16(w2, one, tsum, false);
-      }
+      for (int j = 0; j < NPAIR; ++j)
+        pw[j] = pack_sum<RSUM>(exp2_fast(fmaf(s[2 * j], c2, -mu)), exp2_fast(fmaf(s[2 * j + 1], c2, -mu)), tsum);
     }
     l_run += tsum;
     bf16x8 pb[2];
@@ -532,21 +495,6 @@ struct QState {
       __builtin_amdgcn_sched_barrier(0);
     }
     return sn;
-  }
-
-  // Two weights rounded to bf16 and packed (the B operand of P V), and
-  // their fp32 values added to the row sum t.  The sum is formed with
-  // plain fp32 adds: gfx950's v_dot2_f32_bf16, which would sum the rounded
-  // weights, issues to the matrix-core pipeline and waits for every MFMA in
-  // flight (measured: 13 cycles of exclusive matrix-core time each), while
-  // a VALU add runs beside the MFMAs.  The row sum then holds the weights
-  // before their rounding (within 2^-9 of each rounded weight).
-  static __device__ __forceinline__ uint32_t pack_sum(float e0, float e1, float& t) {
-    const bf16x2 w2 = {(__bf16)e0, (__bf16)e1};
-    uint32_t w = __builtin_bit_cast(uint32_t, w2);
-    __asm__ volatile("" : "+v"(w));
-    t += e0 + e1;
-    return w;
   }
 
   // One step of the skewed pipeline of the no-window loop.  On entry pw
@@ -631,7 +579,7 @@ struct QState {
       }
       if (c > 0) {
 #pragma unroll
-        for (int e = 0; e < EPM; e += 2) pn[((c - 1) * EPM + e) >> 1] = pack_sum(ex[e], ex[e + 1], tsum);
+        for (int e = 0; e < EPM; e += 2) pn[((c - 1) * EPM + e) >> 1] = pack_sum<RSUM>(ex[e], ex[e + 1], tsum);
       }
       // the P V MFMA issues once the score MFMA is well under way, so the
       // wave does not stall on it with its vector work queued behind
@@ -646,7 +594,7 @@ struct QState {
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int e = 0; e < EPM; e += 2) pn[((Gm::NC - 1) * EPM + e) >> 1] = pack_sum(ex[e], ex[e + 1], tsum);
+    for (int e = 0; e < EPM; e += 2) pn[((Gm::NC - 1) * EPM + e) >> 1] = pack_sum<RSUM>(ex[e], ex[e + 1], tsum);
     if (wave_any(!(tsum <= exp2_fast(kRescaleTau)))) {
       // as fold_sum: shift by the tile's row max, rescale what has been
       // accumulated (P V of tiles up to t, issued above), recompute
@@ -662,7 +610,7 @@ struct QState {
       tsum = 0.0f;
 #pragma unroll
       for (int j = 0; j < NPAIR; ++j)
-        pn[j] = pack_sum(exp2_fast(fmaf(s[2 * j], c2, -mu)), exp2_fast(fmaf(s[2 * j + 1], c2, -mu)), tsum);
+        pn[j] = pack_sum<RSUM>(exp2_fast(fmaf(s[2 * j], c2, -mu)), exp2_fast(fmaf(s[2 * j + 1], c2, -mu)), tsum);
     }
     l_run += tsum;
 #pragma unroll
@@ -749,8 +697,14 @@ __device__ __forceinline__ bool tile_needed(int kb, int wpos_lo, int wpos_hi, in
 // 3, rb alternating between 0 and 4: no slot index wraps inside a trip.
 // With a window: a 4-slot K/V ring staged through registers, two tiles per
 // barrier, each wave folding only the tiles of its own range (QState::fold).
-template <int D, int G, int NW, bool NOWIN>
+// LSE: also save each row's log-sum-exp (p.lse).  The row sums add the
+// rounded weights (QState's RSUM), so that a saved log-sum-exp matches the
+// output, except in the plain no-window kernel, whose matrix core is the
+// bottleneck: there they add the weights before rounding, off the
+// matrix-core pipeline (pack_sum).
+template <int D, int G, int NW, bool NOWIN, bool LSE>
 __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
+  using QS = QState<D, LSE || !NOWIN>;
   using Gm = TileGeom<D>;
   constexpr int NT = NW * 64;
   constexpr int TW = 32 / G;        // tokens per wave
@@ -780,7 +734,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   const int W = NOWIN ? 0 : p.window;  // NOWIN is launched only for window 0
   const float c2 = p.scale_log2;
 
-  QState<D> st;
+  QS st;
   st.load_q(p.q + qoff, q_tok, tw0, G, g, p.Sq, p.q_offset, col, half);
 
   const int tlast = min(t0 + TB, p.Sq) - 1;
@@ -930,12 +884,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
       }
       // steps 1 .. 3 of the trip get their first operands read by the step
       // before (the slots of a trip are all resident since its barrier)
-      typename QState<D>::SkewOps ops;
+      typename QS::SkewOps ops;
       auto trip_step = [&](auto ic) {
         constexpr int i = decltype(ic)::value;
         uint16_t* slot = &ring[rb + i][0];
         uint16_t* after = &ring[rb + (i < 3 ? i + 1 : i)][0];
-        constexpr int PRE = QState<D>::SKEW_PRE;
+        constexpr int PRE = QS::SKEW_PRE;
         constexpr int PIN = i > 0 ? PRE : 0, POUT = i < 3 ? PRE : 0;
         s = st.template skew_step<true, PIN, POUT>(
             s, pw, c2, slot + VREG, slot, (kt + i + 2) * KT, masked ? tile_mask(kt + i + 2) : 0, W, half, lane,
@@ -1046,7 +1000,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
   }
   if (wk1 >= 0) {
     st.store_o(p.o + qoff, q_tok, tw0, G, g, p.Sq, col, half);
-    if (p.lse) st.store_lse(p.lse + (long)b * p.Sq * p.Hq, p.Hq, tw0, G, g, p.Sq, col, half);
+    if constexpr (LSE) st.store_lse(p.lse + (long)b * p.Sq * p.Hq, p.Hq, tw0, G, g, p.Sq, col, half);
   }
 }
 
@@ -1154,7 +1108,11 @@ __global__ __launch_bounds__(G * 64) void prefill_swa_strip_kernel(PrefillArgs p
 #pragma unroll
       for (int it = 0; it < SIT; ++it) qpre[hh][it] = buf_load16<kStripQPolicy>(r, rows_voff(it, hh), 0);
   };
-  QState<D> st;
+  // (row sums of the rounded weights in every mode: the saved log-sum-exp
+  // matches the output, and the plain and training forwards agree bit for
+  // bit; the sum's matrix-pipeline instruction costs nothing here, where the
+  // matrix core has slack)
+  QState<D, true> st;
   // Partial rotary embedding of the staged first half-head (every rotated
   // dimension lies there: 2 * rope_hr <= D / 2) of rows at tokens tw0 ...
   // The wave's TW x rope_hr (cos, sin) live in LDS from block to block: the
@@ -1390,10 +1348,14 @@ static hipError_t launch_generic(const PrefillArgs& a0, hipStream_t stream) {
   a.total = a.B * a.Hkv * a.n_tb;
   a.per_xcd = (a.total + 7) / 8;
   dim3 grid(8 * a.per_xcd), block(NW * 64);
-  if (a.window == 0)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW, true>), grid, block, 0, stream, a);
+  if (a.window == 0 && a.lse)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW, true, true>), grid, block, 0, stream, a);
+  else if (a.window == 0)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW, true, false>), grid, block, 0, stream, a);
+  else if (a.lse)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW, false, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, G, NW, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

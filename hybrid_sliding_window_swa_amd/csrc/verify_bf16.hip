@@ -329,10 +329,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
         for (int db = 0; db < ND; ++db) acc[nb][db] *= alpha;
       }
       const float mu = m_run[nb] == kNegInf ? 0.0f : m_run[nb];
-      bf16x8 pb[2];
+      uint32_t pw[8];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) pb[v >> 3][v & 7] = (__bf16)exp2_fast(sc[nb][v] - mu);
-      l_run[nb] = sum_bf16x16(pb[0], pb[1], l_run[nb]);
+      for (int j = 0; j < 8; ++j)
+        pw[j] = pack_sum<true>(exp2_fast(sc[nb][2 * j] - mu), exp2_fast(sc[nb][2 * j + 1] - mu), l_run[nb]);
+      const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]}),
+                            __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]})};
       const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {

@@ -43,7 +43,9 @@
  *     entry point); violating them is undefined behaviour.
  *   - dtype SWA_BF16: q, k, v, o and caches are bfloat16; scores, softmax and
  *     accumulation are fp32, the attention weights are rounded to bf16 before
- *     the value product, and O is rounded to bf16 (round to nearest even).
+ *     the value product (the row sum that divides O adds the rounded
+ *     weights, or, in the global-attention prefill, the weights before that
+ *     rounding), and O is rounded to bf16 (round to nearest even).
  *     dtype SWA_F32: everything is fp32 and nothing is rounded to bf16.
  *   - sinks, when given, are fp32 [Hq] device values: finite or -inf.
  *   - Supported: D in {64, 128}; Hq % Hkv == 0.  The bf16 paths also need
@@ -137,7 +139,12 @@ SWA_API swa_status_t swa_attn_prefill_rope(const void *q, const void *k, const v
  * natural-log softmax denominator with the sink,
  *   lse[b, r, h] = log(exp(sink_h) + sum_{j in J(i)} exp(s_j)),
  * which swa_attn_backward needs.  lse [B, Sq, Hq] fp32 DEVICE.  SWA_BF16 only;
- * other arguments and rules as swa_attn_prefill.
+ * other arguments and rules as swa_attn_prefill.  The row sums (o's divisor
+ * and lse) add the attention weights after their rounding to bf16, the
+ * weights that enter P V, so that lse matches o for the backward; where
+ * swa_attn_prefill adds them before the rounding (global attention; at
+ * most 2^-9 apart relatively) the two outputs can differ at bf16 rounding
+ * level, elsewhere they are equal.
  */
 SWA_API swa_status_t swa_attn_prefill_lse(const void *q, const void *k, const void *v,
                                   const float *sinks, void *o, float *lse,

@@ -130,7 +130,15 @@ def test_forward_lse_matches_oracle(case):
     o, lse = m.swa_attn_prefill_lse(q.to(dev), k.to(dev), v.to(dev), sd, cfg.window, cfg.q_offset, cfg.scale)
     o_plain = m.swa_attn_prefill(q.to(dev), k.to(dev), v.to(dev), sd, cfg.window, cfg.q_offset, cfg.scale)
     torch.cuda.synchronize()
-    assert torch.equal(o.view(torch.int16), o_plain.view(torch.int16))
+    if cfg.window > 0:
+        assert torch.equal(o.view(torch.int16), o_plain.view(torch.int16))
+    else:
+        # without a window the plain prefill sums the weights before their
+        # rounding (at most 2^-9 apart relatively); a sum near the
+        # lazy-rescale threshold can also move a rescale, and with it the
+        # rounding of later weights, so the two agree to the bf16 tolerance
+        assert_close(o, o_plain.float().cpu().numpy().astype(np.float64), BF16_TOL,
+                     case[0] + " (training vs plain)")
     ref = oracle.prefill(q, k, v, sinks, cfg.window, cfg.q_offset, cfg.scale, want_lse=True)
     assert_close(o, ref["o"], BF16_TOL, case[0])
     err = np.abs(lse.cpu().numpy() - ref["lse"]).max()
