@@ -44,6 +44,8 @@ CASES = [
     ("g1_w1", 1, 70, 70, 4, 4, 64, 1, True),
     ("model_heads", 1, 256, 256, 64, 8, 128, 128, True),
     ("global_chunk_g2", 2, 77, 120, 8, 4, 128, 0, True),
+    # the LSE-saving global kernel at D 64
+    ("global_d64_g4", 1, 150, 150, 8, 2, 64, 0, True),
     # the other instantiations of the strip dQ kernel (G 4 with D 128, G 8
     # with D 64) and a window that is not a multiple of the tile
     ("swa_g4_d128", 1, 200, 200, 16, 4, 128, 128, True),
