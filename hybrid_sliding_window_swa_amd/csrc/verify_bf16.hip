@@ -21,13 +21,17 @@
 //     16-byte loads of whole rows); K is read back as the MFMA A operand of
 //     S^T = K Q^T, V with ds_read_b64_tr_b16 as the A operand of
 //     O^T += V^T P^T.  The next tile's loads are issued before the current
-//     tile is computed.
+//     tile is computed; on a wave's first tile the scores are computed from
+//     its K half while its V half is still arriving, and the wave that owns
+//     the tile of new rows computes that tile first.
 //   * Rows past the end of the valid cache range are clamped to the last
 //     valid row and masked out, so unused cache slots are never read and may
 //     hold anything, NaN included.
 //   * With one split per (request, KV head) the workgroup folds the sink and
 //     writes O directly; otherwise it writes (max, sum, unnormalised O) to the
 //     workspace and verify_combine merges the splits, folding the sink once.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -140,7 +144,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
     uint16_t k[NW][KTile<D>::ELEMS];
     uint16_t v[NW][VTile<D>::ELEMS];
   };
-  constexpr size_t LDS_MAIN = sizeof(MergeLds) > sizeof(TileLds) ? sizeof(MergeLds) : sizeof(TileLds);
+  // 4 KiB accumulator blocks that fit in a wave's own K and V tiles
+  constexpr int KBLK = (int)(sizeof(uint16_t) * KTile<D>::ELEMS / 4096);
+  constexpr int VBLK = (int)(sizeof(uint16_t) * VTile<D>::ELEMS / 4096);
+  constexpr bool OWN_MERGE = NB * ND <= KBLK + VBLK;
+  constexpr size_t LDS_MAIN =
+      OWN_MERGE || sizeof(TileLds) > sizeof(MergeLds) ? sizeof(TileLds) : sizeof(MergeLds);
   __shared__ __attribute__((aligned(16))) unsigned char lds_main[LDS_MAIN];
   __shared__ float lds_m[NW][NB * 32];
   __shared__ float lds_l[NW][NB * 32];
@@ -168,7 +177,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
 
   const int G = p.Hq / p.Hkv;
   const int R = G * p.T;
-  const int tid = threadIdx.x, wv = wave_index();
+  const int wv = wave_index();
   const int half = lane >> 5, col = lane & 31;
   const long kv_tok = (long)p.Hkv * D;
   // ring: slot of the oldest committed position held, to map slot -> position
@@ -220,33 +229,49 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
     const bool nw = (s == 0 && j == ntc);
     const uint16_t* kb = nw ? p.k_new : p.k_cache;
     const uint16_t* vb = nw ? p.v_new : p.v_cache;
+    // every cache row is read once: non-temporal, so the stream does not
+    // displace reused data in the L2 and the Infinity Cache (measured:
+    // 5.6 -> 6.1 TB/s on the 64-request global cache).  All K loads are
+    // issued before the V loads, so that the K half can be stored (and its
+    // scores computed) while V is still arriving.
 #pragma unroll
     for (int i = 0; i < LD_IT; ++i) {
       const int c = lane + 64 * i;
-      const long o = row_off(j, c / CPR) + (c % CPR) * 8;
-      // every cache row is read once: non-temporal, so the stream does not
-      // displace reused data in the L2 and the Infinity Cache (measured:
-      // 5.6 -> 6.1 TB/s on the 64-request global cache)
-      kpre[i] = __builtin_nontemporal_load((const u32x4*)(kb + o));
-      vpre[i] = __builtin_nontemporal_load((const u32x4*)(vb + o));
+      kpre[i] = __builtin_nontemporal_load((const u32x4*)(kb + row_off(j, c / CPR) + (c % CPR) * 8));
+    }
+#pragma unroll
+    for (int i = 0; i < LD_IT; ++i) {
+      const int c = lane + 64 * i;
+      vpre[i] = __builtin_nontemporal_load((const u32x4*)(vb + row_off(j, c / CPR) + (c % CPR) * 8));
     }
   };
-  auto store_tile = [&]() {
+  auto store_k = [&]() {
 #pragma unroll
     for (int i = 0; i < LD_IT; ++i) {
       const int c = lane + 64 * i;
       *(u32x4*)&k_t[KTile<D>::off(c / CPR, (c % CPR) * 8)] = kpre[i];
+    }
+  };
+  auto store_v = [&]() {
+#pragma unroll
+    for (int i = 0; i < LD_IT; ++i) {
+      const int c = lane + 64 * i;
       *(u32x4*)&v_t[VTile<D>::off(c / CPR, (c % CPR) * 8)] = vpre[i];
     }
   };
 
-  // The tile of new rows (split 0's last) holds only T distinct rows: when
-  // it is not this wave's first tile, its T rows are loaded in the prologue
-  // with the first tile (one memory latency instead of two in a row) and
-  // written into the wave's LDS tile when its turn comes.  Its other rows
-  // keep the previous tile's (finite) values there and are masked out.
+  // The tile of new rows (split 0's last) holds only T distinct rows.  The
+  // wave that owns it computes it first: its T rows (LDN loads per lane) are
+  // issued in the prologue ahead of the wave's first cache tile, and the
+  // wave waits only for them, so the new tile is computed while the cache
+  // tile is still arriving instead of after it.  Rows T..31 of that LDS tile
+  // are zeros (masked; zero V rows keep P V finite).  With more than
+  // 64 * LDN / CPR new rows the tile is an ordinary last tile instead.
   constexpr int LDN = 2;                       // 16-byte loads per lane for T rows
-  const bool pre_new = s == 0 && ntc % NW == wv && ntc != wv && p.T * CPR <= 64 * LDN;
+  const bool new_first = s == 0 && ntc % NW == wv && p.T * CPR <= 64 * LDN;
+  // this wave's tiles: wv, wv + NW, ... (the new tile, when it has it, first)
+  const int nt_w = wv < ntiles ? (ntiles - 1 - wv) / NW + 1 : 0;
+  auto tile_of = [&](int i) { return new_first ? (i == 0 ? ntc : wv + (i - 1) * NW) : wv + i * NW; };
   u32x4 nk[LDN], nv[LDN];
   auto load_new = [&]() {
 #pragma unroll
@@ -257,30 +282,44 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
       nv[i] = __builtin_nontemporal_load((const u32x4*)(p.v_new + o));
     }
   };
-  auto store_new = [&]() {
+  auto store_new = [&](bool is_v) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < LDN; ++i) {
+    for (int i = 0; i < LD_IT; ++i) {
       const int c = lane + 64 * i;
-      if (c < p.T * CPR) {
-        *(u32x4*)&k_t[KTile<D>::off(c / CPR, (c % CPR) * 8)] = nk[i];
-        *(u32x4*)&v_t[VTile<D>::off(c / CPR, (c % CPR) * 8)] = nv[i];
-      }
+      const bool have = i < LDN && c < p.T * CPR;
+      if (is_v)
+        *(u32x4*)&v_t[VTile<D>::off(c / CPR, (c % CPR) * 8)] = have ? nv[i < LDN ? i : 0] : zero;
+      else
+        *(u32x4*)&k_t[KTile<D>::off(c / CPR, (c % CPR) * 8)] = have ? nk[i < LDN ? i : 0] : zero;
     }
   };
 
-  if (wv < ntiles) {
-    load_tile(wv);
-    if (pre_new) load_new();
-    store_tile();
+  // Prologue: the first tile's K into LDS, its V stored after its scores
+  // (the V half of its loads has the scores' time to arrive) and only then
+  // the next tile's loads issued, since they reuse the registers; with the
+  // new tile first, its K and V, the next (cache) tile's loads staying in
+  // flight behind it.  From the second tile on, the next tile's loads are
+  // issued at the top of each step and its K and V stored at the end.
+  if (new_first) {
+    load_new();
+    // The next tile's loads, or, when the wave has no cache tile, the new
+    // tile's own rows again (never used): one path, so the compiler's waits
+    // for the T new rows leave these loads in flight.
+    load_tile(nt_w > 1 ? tile_of(1) : ntc);
+    store_new(false);
+    store_new(true);
+  } else if (nt_w > 0) {
+    load_tile(tile_of(0));
+    store_k();
   }
-  // Drain the prologue loads (queries, first tile) so that inside the loop
-  // the only loads in flight are the prefetch of the next tile and nothing
-  // waits on it before the current tile is computed.
-  __builtin_amdgcn_s_waitcnt(0);
-  for (int j = wv; j < ntiles; j += NW) {
-    const bool more = j + NW < ntiles;
-    const bool next_new = more && pre_new && j + NW == ntc;
-    if (more && !next_new) load_tile(j + NW);
+  // One step per tile; the first is a copy of its own (FIRST), so that the
+  // two schedules do not share one loop body's registers.
+  auto step = [&](auto first_c, int i) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    const int j = tile_of(i);
+    const bool more = i + 1 < nt_w;
+    if (!FIRST && more) load_tile(tile_of(i + 1));
     wave_lds_sync();
 
     f32x16 sc[NB];
@@ -293,27 +332,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma32(a, qreg[nb][c], sc[nb]);
     }
+    if (FIRST && !new_first) {
+      store_v();
+      if (more) load_tile(tile_of(1));
+    }
+    // Which rows of the tile a query sees, as two range tests per element
+    // with per-tile and per-lane bounds (no per-element branches): row r is
+    // visible iff a = a0 + r < a_hi and b = b0 + r (taken into [0, slots) by
+    // adding slots when negative) > b_lo.
+    //   new tile:  r < min(T, t + 1) (token r at position L + r, tokens 0..t
+    //              visible) and r > t - window;
+    //   cache:     slot ci = c0 + 32 j + r < c1, and its position above
+    //              L + t - window: position ci in a linear cache, L - ring_n
+    //              + e with e = (ci - ring_base_slot) mod slots in a ring.
     const bool is_new_tile = (s == 0 && j == ntc);
+    const int cb = c0 + j * 32;
+    const int a0 = is_new_tile ? 0 : cb;
+    const int b0 = is_new_tile ? 0 : (p.ring ? cb - ring_base_slot : cb);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int t = qt[nb];
+      int a_hi = is_new_tile ? min(p.T, t + 1) : c1;
+      a_hi = t < 0 ? INT32_MIN : a_hi;  // padding rows see nothing
+      const int b_lo = p.window <= 0 ? -1 : (is_new_tile ? 0 : (p.ring ? ring_n : L)) + t - p.window;
       float mx = kNegInf;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = c_row(v, half);
-        bool ok;
-        if (is_new_tile) {
-          // new token u at position L + u, visible to query t iff u <= t and in window
-          ok = t >= 0 && r < p.T && r <= t && (p.window <= 0 || r > t - p.window);
-        } else {
-          const int ci = c0 + j * 32 + r;
-          int pos = ci;
-          if (p.ring) {
-            const int d = ci - ring_base_slot;
-            pos = L - ring_n + (d >= 0 ? d : d + p.slots);
-          }
-          ok = t >= 0 && ci < c1 && (p.window <= 0 || pos > L + t - p.window);
-        }
+        int b = b0 + r;
+        b += b < 0 ? p.slots : 0;
+        const bool ok = (a0 + r < a_hi) & (b > b_lo);
         const float x = ok ? sc[nb][v] * p.scale_log2 : kNegInf;
         sc[nb][v] = x;
         mx = fmaxf(mx, x);
@@ -321,13 +369,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
       mx = halves_max(mx);
       const float m_new = fmaxf(m_run[nb], mx);
       const bool need = m_new > m_run[nb] + kRescaleTau;
-      if (wave_any(need)) {
+      // A wave's first tile finds its accumulators and sum still zero: only
+      // the max moves.  Later, the rescale is a real branch (the empty asm
+      // keeps the compiler from turning it into unconditional multiplies),
+      // taken only when some row's max has grown past the threshold.
+      if (!FIRST && wave_any(need)) {
+        __asm__ volatile("");
         const float alpha = need ? exp2_fast(m_run[nb] - m_new) : 1.0f;
-        m_run[nb] = need ? m_new : m_run[nb];
         l_run[nb] *= alpha;
 #pragma unroll
         for (int db = 0; db < ND; ++db) acc[nb][db] *= alpha;
       }
+      m_run[nb] = need ? m_new : m_run[nb];
       const float mu = m_run[nb] == kNegInf ? 0.0f : m_run[nb];
       uint32_t pw[8];
 #pragma unroll
@@ -335,6 +388,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
         pw[j] = pack_sum<true>(exp2_fast(sc[nb][2 * j] - mu), exp2_fast(sc[nb][2 * j + 1] - mu), l_run[nb]);
       const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]}),
                             __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]})};
+      if (FIRST) wave_lds_sync();  // this step stored the V half
       const lds_u16* vbase = lane_base(lds_addr(v_t), VTile<D>::vt_lane_off(lane));
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
@@ -344,14 +398,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
       }
     }
     wave_lds_sync();
-    if (next_new) {
-      store_new();
-    } else if (more) {
-      store_tile();
+    if (more) {
+      store_k();
+      store_v();
     }
-  }
+  };
+  if (nt_w > 0) step(std::true_type{}, 0);
+  for (int i = 1; i < nt_w; ++i) step(std::false_type{}, i);
 
-  // ---- merge the waves: common max, then a fixed-order pairwise sum in LDS
+  // ---- merge the waves.  Each wave leaves its running max and sum per query
+  // row in lds_m / lds_l and its unscaled accumulators in LDS; after one
+  // barrier, wave w finishes output blocks q = w, w + NW, ... (q = nb * ND +
+  // db): the common max M of the row over the waves, l = sum_w l_w 2^(m_w -
+  // M), and the sum over the waves of acc_w 2^(m_w - M) in a fixed pairwise
+  // order ((w0 + w2) + (w1 + w3) for four waves: bitwise deterministic).
+  // When a wave's accumulators fit in its own K/V tile (NB = 1) they go
+  // there as soon as the wave is done with its tiles; otherwise into a merge
+  // area over all the tiles, behind a barrier.  A block is 16 floats per
+  // lane, stored as 4 x 64 lane-contiguous 16-byte entries.
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float lt = halves_sum(l_run[nb]);
@@ -360,56 +424,58 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
       lds_l[wv][nb * 32 + col] = lt;
     }
   }
-  __syncthreads();
-  float m_all[NB], l_all[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    float mm = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, lds_m[w][nb * 32 + col]);
-    float ll = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = lds_m[w][nb * 32 + col];
-      ll += mw == kNegInf ? 0.0f : lds_l[w][nb * 32 + col] * exp2_fast(mw - mm);
-    }
-    m_all[nb] = mm;
-    l_all[nb] = ll;
-    const float f = m_run[nb] == kNegInf ? 0.0f : exp2_fast(m_run[nb] - mm);
-#pragma unroll
-    for (int db = 0; db < ND; ++db) acc[nb][db] *= f;
-  }
-  // Every wave leaves its rescaled accumulators in LDS; then wave w sums
-  // output blocks q = w, w + NW, ... (q = nb * ND + db) over the waves, in
-  // a fixed pairwise order ((w0 + w2) + (w1 + w3) for four waves: bitwise
-  // deterministic), and writes them: one barrier, and every wave writes.
+  TileLds* tl = (TileLds*)lds_main;
   MergeLds* ml = (MergeLds*)lds_main;
+  auto blk_ptr = [&](int w, int q) -> f32x4* {
+    if constexpr (OWN_MERGE) {
+      return q < KBLK ? (f32x4*)tl->k[w] + q * 256 : (f32x4*)tl->v[w] + (q - KBLK) * 256;
+    } else {
+      return (f32x4*)&ml->acc[w][q * 16][0];
+    }
+  };
+  if constexpr (!OWN_MERGE) __syncthreads();  // every wave is done with its tiles
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+    for (int db = 0; db < ND; ++db) {
+      f32x4* bp = blk_ptr(wv, nb * ND + db);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) ml->acc[wv][(nb * ND + db) * 16 + v][lane] = acc[nb][db][v];
+      for (int v4 = 0; v4 < 4; ++v4)
+        bp[v4 * 64 + lane] = f32x4{acc[nb][db][4 * v4], acc[nb][db][4 * v4 + 1], acc[nb][db][4 * v4 + 2],
+                                   acc[nb][db][4 * v4 + 3]};
+    }
   __syncthreads();
 #pragma unroll
   for (int qi = 0; qi < NQ_W; ++qi) {
     const int q = wv + qi * NW;
     if (q >= NB * ND) break;
     const int nb = q / ND, db = q % ND;
+    float mw[NW], fw[NW];
+    float mA = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = lds_m[w][nb * 32 + col];
+      mA = fmaxf(mA, mw[w]);
+    }
+    float lA = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      fw[w] = mw[w] == kNegInf ? 0.0f : exp2_fast(mw[w] - mA);
+      lA += mw[w] == kNegInf ? 0.0f : lds_l[w][nb * 32 + col] * fw[w];
+    }
     f32x16 y;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float x[NW];
+    for (int v4 = 0; v4 < 4; ++v4) {
+      f32x4 x[NW];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) x[w] = ml->acc[w][q * 16 + v][lane];
+      for (int w = 0; w < NW; ++w) x[w] = blk_ptr(w, q)[v4 * 64 + lane] * fw[w];
 #pragma unroll
       for (int r = NW / 2; r >= 1; r /= 2)
 #pragma unroll
         for (int w = 0; w < r; ++w) x[w] += x[w + r];
-      y[v] = x[0];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[4 * v4 + e] = x[0][e];
     }
-    const float mA = nb == 0 ? m_all[0] : m_all[NB - 1];
-    const float lA = nb == 0 ? l_all[0] : l_all[NB - 1];
     const int m = nb * 32 + col;
     if (DIRECT) {
       if (m >= R) continue;
