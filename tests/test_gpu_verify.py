@@ -43,6 +43,11 @@ CASES = [
     (_vcfg("ring_w2", 10, 4, 64, 8, 128, 2, True, 2, 0, 0), EDGE_LENS),
     (_vcfg("ring_d64", 10, 4, 16, 2, 64, 128, True, 128, 0, 0), EDGE_LENS),
     (_vcfg("ring_t8_g8", 10, 8, 64, 8, 128, 128, True, 128, 0, 0), EDGE_LENS),
+    # q_len 16: at D = 128 the tile of new rows is then an ordinary last tile
+    # (more new rows than the wave that computes it first can hold), at
+    # D = 64 it is still computed first
+    (_vcfg("ring_t16_g4", 10, 16, 16, 4, 128, 128, True, 128, 0, 0), EDGE_LENS),
+    (_vcfg("ring_t16_g4_d64", 10, 16, 16, 4, 64, 128, True, 128, 0, 0), EDGE_LENS),
     # the wider window the pages compare W = 128 against, on a 512-slot ring
     (_vcfg("ring_w512", 10, 4, 64, 8, 128, 512, True, 512, 0, 0),
      [0, 1, 127, 128, 129, 511, 512, 513, 1000, 5000]),
@@ -51,6 +56,7 @@ CASES = [
     (_vcfg("linear_global_t1", 10, 1, 16, 2, 128, 0, False, 1100, 0, 0), EDGE_LENS),
     (_vcfg("linear_global_t8", 10, 8, 64, 8, 128, 0, False, 1100, 0, 0), EDGE_LENS),
     (_vcfg("linear_global_d64", 10, 4, 16, 2, 64, 0, False, 1100, 0, 0), EDGE_LENS),
+    (_vcfg("linear_global_t16_g2", 10, 16, 8, 4, 128, 0, False, 1100, 0, 0), EDGE_LENS),
     # a sliding window over a linear cache
     (_vcfg("linear_w128", 10, 4, 64, 8, 128, 128, False, 1100, 0, 0), EDGE_LENS),
     (_vcfg("linear_long", 3, 4, 64, 8, 128, 0, False, 20000, 0, 0), [19999, 7777, 12345]),
