@@ -873,15 +873,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
       const bool masked = (kt + 5) * KT + KT - 1 > pos_lo;
       u32x4 desc[WPW];
       uint32_t m0k[WPW];
-#pragma unroll
-      for (int k = 0; k < WPW; ++k) {
+      // window k's descriptor for this trip, built in the first step right
+      // before its first load (scalar work between that step's MFMAs rather
+      // than at the trip start, where both waves of a SIMD sit after the barrier)
+      auto make_desc = [&](int k) {
         // keys of window k's tiles this trip: from (kt + 6) or (kt + 4) tiles on
         const int key0 = (kt + (dma_k[k] ? 6 : 4)) * KT;
         const int rows = min(key_end - key0, 4 * KT);
         desc[k] = buffer_desc(bp[k], rows <= 0 ? 0u : min(trip_rec, (uint32_t)rows * row_b - pad_b));
         bp[k] += 4 * tstride;
         m0k[k] = dma_on[k] ? ring0 + (rb ^ 4u) * PAIR_B + dma_lds[k] : sink_lds;
-      }
+      };
       // steps 1 .. 3 of the trip get their first operands read by the step
       // before (the slots of a trip are all resident since its barrier)
       typename QS::SkewOps ops;
@@ -896,6 +898,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_bf16_kernel(PrefillArgs p) {
             [&](int c) {
               if (c >= 1 && c <= WPW) {
                 const int k = c - 1;
+                if constexpr (i == 0) make_desc(k);
                 lds_dma16_soff(desc[k], 0u, m0k[k] + (uint32_t)i * m0_step[k], dma_off[k] + (uint32_t)i * tile_b);
               }
             },
