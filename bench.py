@@ -171,6 +171,10 @@ def read_peaks():
                 if d["GB/s"] > out.get("hbm_copy_GBs", 0.0):
                     out["hbm_copy_GBs"] = d["GB/s"]
                     out["hbm_copy_by"] = d["measure"]
+            elif d["measure"] == "mfma_bf16_32x32x16_random_operands":
+                # operands switching every instruction, as attention's do:
+                # the rate at the clock the chip's power limit then allows
+                out["mfma_bf16_random_operands_TFLOPs"] = d["TFLOP/s"]
             elif d["measure"].startswith("mfma_bf16"):
                 out["mfma_bf16_TFLOPs"] = d["TFLOP/s"]
             elif d["measure"] == "hbm_read_cold_small":
@@ -727,6 +731,9 @@ def main():
         if "ga_prefill" in result:
             gp = result["ga_prefill"]
             gp["frac_of_measured_mfma"] = round(gp["TFLOP/s"] / peaks["mfma_bf16_TFLOPs"], 4)
+            if "mfma_bf16_random_operands_TFLOPs" in peaks:
+                gp["frac_of_measured_mfma_random_operands"] = round(
+                    gp["TFLOP/s"] / peaks["mfma_bf16_random_operands_TFLOPs"], 4)
     if args.only is None and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, *tensors, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -12,6 +12,9 @@
 //     policy is the ceiling.
 //   * bf16 MFMA: v_mfma_f32_32x32x16_bf16 on four independent accumulators,
 //     two waves per SIMD, operands in registers (no memory traffic).
+//   * The same with operands that change every instruction (pseudo-random
+//     bf16 values): the rate at the clock the chip holds when the matrix
+//     cores switch like they do on attention's data.
 //   * Cold small read: the streaming read of 42,729,472 bytes (the bytes one
 //     SWA-ring verify of 64 requests moves) right after 512 MiB of other
 //     memory was written (so none of it sits in the L2 or the 256 MB
@@ -105,6 +108,44 @@ __global__ __launch_bounds__(512) void mfma_kernel(float* out, float seed) {
   }
   float r = 0.0f;
   for (int j = 0; j < 4; ++j)
+    for (int v = 0; v < 16; ++v) r += acc[j][v];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
+// The same MFMA stream on operands that change from one instruction to the
+// next: eight (A, B) pairs per lane of pseudo-random bf16 values in
+// [-2, 2) (an integer hash of the thread and pair index), each MFMA of an
+// iteration on its own pair.  Attention's operands toggle like this; the
+// constant operands above hardly switch the multipliers, and the chip's
+// power-limited clock differs between the two.
+__device__ __forceinline__ uint32_t hash32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ __launch_bounds__(512) void mfma_rand_kernel(float* out, uint32_t seed) {
+  bf16x8 a[8], b[8];
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[j][i] = (__bf16)((float)(hash32(seed ^ (t * 131u + j * 17u + i)) >> 8) * 0x1p-22f - 2.0f);
+      b[j][i] = (__bf16)((float)(hash32(~seed ^ (t * 137u + j * 19u + i)) >> 8) * 0x1p-22f - 2.0f);
+    }
+  f32x16 acc[4] = {};
+  for (int it = 0; it < kMfmaIter / 2; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[j], acc[j & 3], 0, 0, 0);
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
     for (int v = 0; v < 16; ++v) r += acc[j][v];
   out[blockIdx.x * blockDim.x + threadIdx.x] = r;
 }
@@ -217,6 +258,10 @@ int main() {
   const double flop = (double)mfma_blocks * 8 * kMfmaIter * 4 * 32768.0;
   printf("{\"measure\": \"mfma_bf16_32x32x16\", \"flop\": %.4e, \"ms\": %.4f, \"TFLOP/s\": %.1f}\n", flop, mm,
          flop / (mm * 1e-3) / 1e12);
+  const float mr = time_ms(
+      [&] { hipLaunchKernelGGL(mfma_rand_kernel, dim3(mfma_blocks), dim3(512), 0, 0, sink, 12345u); }, 500.0f, 10);
+  printf("{\"measure\": \"mfma_bf16_32x32x16_random_operands\", \"flop\": %.4e, \"ms\": %.4f, \"TFLOP/s\": %.1f}\n",
+         flop, mr, flop / (mr * 1e-3) / 1e12);
   {
     const long cold = 42729472L, c16 = cold / 16;
     const int grid = 16 * cus;
