@@ -167,7 +167,12 @@ def read_peaks():
             if d["measure"] == "hbm_read":
                 out["hbm_read_GBs"] = d["GB/s"]
             elif d["measure"].startswith("hbm_copy"):
-                # the faster of the library's copy kernel and torch's copy_
+                if d["measure"] == "hbm_copy_head_groups":
+                    # the sliding-window prefill's own access pattern as a
+                    # copy: 2 KiB head-group segments of 16 KiB token rows
+                    out["hbm_copy_head_groups_GBs"] = d["GB/s"]
+                # the fastest copy: the library's copy kernels (contiguous or
+                # grid-stride ranges, head-group segments) and torch's copy_
                 if d["GB/s"] > out.get("hbm_copy_GBs", 0.0):
                     out["hbm_copy_GBs"] = d["GB/s"]
                     out["hbm_copy_by"] = d["measure"]
@@ -177,6 +182,10 @@ def read_peaks():
                 out["mfma_bf16_random_operands_TFLOPs"] = d["TFLOP/s"]
             elif d["measure"].startswith("mfma_bf16"):
                 out["mfma_bf16_TFLOPs"] = d["TFLOP/s"]
+            elif d["measure"] == "hbm_read_head_rows":
+                # the global-cache verify's own access pattern: one KV head's
+                # 256-byte rows per workgroup
+                out["hbm_read_head_rows_GBs"] = d["GB/s"]
             elif d["measure"] == "hbm_read_cold_small":
                 out["hbm_read_cold_small_us"] = d["us_median"]
                 out["hbm_read_cold_small_bytes"] = d["bytes"]
@@ -725,9 +734,14 @@ def main():
         result["measured_ceilings"] = peaks
         result["roofline"]["frac_of_measured_copy"] = round(
             result["roofline"]["achieved"] / peaks["hbm_copy_GBs"], 4)
+        if "hbm_copy_head_groups_GBs" in peaks:
+            result["roofline"]["frac_of_measured_head_group_copy"] = round(
+                result["roofline"]["achieved"] / peaks["hbm_copy_head_groups_GBs"], 4)
         if "verify" in result:
             v = result["verify"]["roofline"]
             v["frac_of_measured_read"] = round(v["achieved"] / peaks["hbm_read_GBs"], 4)
+            if "hbm_read_head_rows_GBs" in peaks:
+                v["frac_of_measured_head_rows_read"] = round(v["achieved"] / peaks["hbm_read_head_rows_GBs"], 4)
         if "ga_prefill" in result:
             gp = result["ga_prefill"]
             gp["frac_of_measured_mfma"] = round(gp["TFLOP/s"] / peaks["mfma_bf16_TFLOPs"], 4)

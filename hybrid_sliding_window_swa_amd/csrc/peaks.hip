@@ -2,8 +2,16 @@
 // on the GPU itself (the datasheet figures are 8 TB/s HBM and 2.5 PFLOP/s
 // dense bf16 MFMA at the peak engine clock).
 //
-//   * HBM streaming read: a grid-stride read of 8 GiB, four independent
-//     16-byte loads in flight per thread, XOR-reduced so nothing is dead code.
+//   * HBM streaming read: a read of 8 GiB, grid-stride or one contiguous
+//     range per workgroup, four independent 16-byte loads in flight per
+//     thread, XOR-reduced so nothing is dead code.
+//   * The same 8 GiB read in the global-cache verify's pattern: one KV
+//     head's 256-byte rows of a [rows, 8, 128] bf16 cache per workgroup
+//     (the other heads' rows in between), the eight heads' workgroups of a
+//     row range side by side.
+//   * The 8 GiB copy in the sliding-window prefill's pattern: 2 KiB head-group
+//     segments of 16 KiB token rows, one head group and token range per
+//     workgroup, the eight groups' workgroups of a range side by side.
 //   * HBM copy: reading one 8 GiB buffer and writing another (bytes read +
 //     bytes written per second), best of 1, 2, 4 or 8 independent loads in
 //     flight per thread before their stores, grid-stride or one contiguous
@@ -44,17 +52,46 @@ __device__ __forceinline__ u32x4 ld(const u32x4* p) {
   return *p;
 }
 
-template <bool NT>
+// Four independent 16-byte loads in flight per thread.  BLOCKED: workgroup
+// b reads one contiguous range; otherwise grid-stride.
+template <bool NT, bool BLOCKED = false>
 __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ p, long n16, uint32_t* out) {
   u32x4 acc = {0, 0, 0, 0};
-  long i = blockIdx.x * 256L + threadIdx.x;
-  const long stride = (long)gridDim.x * 256;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
+  long i, end, stride;
+  if constexpr (BLOCKED) {
+    const long per = ((n16 + gridDim.x - 1) / gridDim.x + 1023) / 1024 * 1024;
+    i = blockIdx.x * per + threadIdx.x;
+    end = blockIdx.x * per + per < n16 ? blockIdx.x * per + per : n16;
+    stride = 256;
+  } else {
+    i = blockIdx.x * 256L + threadIdx.x;
+    end = n16;
+    stride = (long)gridDim.x * 256;
+  }
+  for (; i + 3 * stride < end; i += 4 * stride) {
     const u32x4 a = ld<NT>(p + i), b = ld<NT>(p + i + stride), c = ld<NT>(p + i + 2 * stride),
                 d = ld<NT>(p + i + 3 * stride);
     acc ^= a ^ b ^ c ^ d;
   }
-  for (; i < n16; i += stride) acc ^= ld<NT>(p + i);
+  for (; i < end; i += stride) acc ^= ld<NT>(p + i);
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) out[0] = 1;
+}
+
+// The global-cache verify's access pattern: the buffer as a [rows, 8, 128]
+// bf16 cache, workgroup w = 8 s + h reading the 256-byte rows of KV head h
+// in row range s (so the eight heads' workgroups of a range run side by
+// side), non-temporal, four 16-byte loads in flight per thread.  rows_per:
+// rows per workgroup, a multiple of 64.
+__global__ __launch_bounds__(256) void read_head_rows_kernel(const u32x4* __restrict__ p, long rows_per,
+                                                             uint32_t* out) {
+  u32x4 acc = {0, 0, 0, 0};
+  const int t = threadIdx.x, h = blockIdx.x & 7;
+  const long r0 = (long)(blockIdx.x >> 3) * rows_per;
+  for (long r = r0 + t / 16; r + 48 < r0 + rows_per; r += 64) {
+    const u32x4 a = ld<true>(p + (r * 8 + h) * 16 + (t & 15)), b = ld<true>(p + ((r + 16) * 8 + h) * 16 + (t & 15)),
+                c = ld<true>(p + ((r + 32) * 8 + h) * 16 + (t & 15)), d = ld<true>(p + ((r + 48) * 8 + h) * 16 + (t & 15));
+    acc ^= a ^ b ^ c ^ d;
+  }
   if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) out[0] = 1;
 }
 
@@ -64,6 +101,26 @@ __device__ __forceinline__ void st(u32x4 v, u32x4* p) {
     __builtin_nontemporal_store(v, p);
   } else {
     *p = v;
+  }
+}
+
+// The sliding-window prefill's access pattern as a copy: both buffers as
+// [tokens, 64, 128] bf16 (16 KiB token rows), workgroup w = 8 s + g
+// copying the 2 KiB segment of head group g (heads 8g .. 8g + 7) of the
+// token rows in range s, non-temporal, four 16-byte loads in flight per
+// thread before their stores.  tok_per: tokens per workgroup, a multiple
+// of 2.
+__global__ __launch_bounds__(256) void copy_head_groups_kernel(const u32x4* __restrict__ p, u32x4* __restrict__ q,
+                                                               long tok_per) {
+  const int t = threadIdx.x, g = blockIdx.x & 7;
+  const long t0 = (long)(blockIdx.x >> 3) * tok_per;
+  // thread t: token (t / 128) + 2 k, chunk t % 128 of the 2 KiB segment
+  for (long k = t0 + t / 128; k + 6 < t0 + tok_per; k += 8) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = ld<true>(p + ((k + 2 * j) * 8 + g) * 128 + (t & 127));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st<true>(v[j], q + ((k + 2 * j) * 8 + g) * 128 + (t & 127));
   }
 }
 
@@ -208,20 +265,26 @@ int main() {
   // flight per thread, grid-stride or one contiguous range per workgroup
   float rd = 1e30f, cp = 1e30f;
   int rd_grid = 0, cp_grid = 0, cp_depth = 0;
-  bool rd_nt = false, cp_nt = false, cp_blocked = false;
+  bool rd_nt = false, rd_blocked = false, cp_nt = false, cp_blocked = false;
   for (int nt = 0; nt < 2; ++nt) {
     for (int mult : {4, 8, 16, 32, 64}) {
       const int grid = mult * cus;
       const float settle = (mult == 4 && nt == 0) ? 500.0f : 0.0f;
-      const float r = time_ms(
-          [&] {
-            if (nt)
-              hipLaunchKernelGGL(read_kernel<true>, dim3(grid), dim3(256), 0, 0, a, n16, flag);
-            else
-              hipLaunchKernelGGL(read_kernel<false>, dim3(grid), dim3(256), 0, 0, a, n16, flag);
-          },
-          settle, 10);
-      if (r < rd) { rd = r; rd_grid = grid; rd_nt = nt; }
+      for (int blocked = 0; blocked < 2; ++blocked) {
+        const float r = time_ms(
+            [&] {
+              if (nt && blocked)
+                hipLaunchKernelGGL((read_kernel<true, true>), dim3(grid), dim3(256), 0, 0, a, n16, flag);
+              else if (nt)
+                hipLaunchKernelGGL((read_kernel<true, false>), dim3(grid), dim3(256), 0, 0, a, n16, flag);
+              else if (blocked)
+                hipLaunchKernelGGL((read_kernel<false, true>), dim3(grid), dim3(256), 0, 0, a, n16, flag);
+              else
+                hipLaunchKernelGGL((read_kernel<false, false>), dim3(grid), dim3(256), 0, 0, a, n16, flag);
+            },
+            blocked ? 0.0f : settle, 10);
+        if (r < rd) { rd = r; rd_grid = grid; rd_nt = nt; rd_blocked = blocked; }
+      }
       for (int blocked = 0; blocked < 2; ++blocked) {
         for (int depth : {1, 2, 4, 8}) {
           const float c = time_ms(
@@ -247,12 +310,46 @@ int main() {
       }
     }
   }
-  printf("{\"measure\": \"hbm_read\", \"bytes\": %ld, \"grid\": %d, \"nontemporal\": %s, \"ms\": %.4f, \"GB/s\": %.1f}\n",
-         bytes, rd_grid, rd_nt ? "true" : "false", rd, bytes / (rd * 1e-3) / 1e9);
+  printf("{\"measure\": \"hbm_read\", \"bytes\": %ld, \"grid\": %d, \"nontemporal\": %s, "
+         "\"contiguous_per_workgroup\": %s, \"ms\": %.4f, \"GB/s\": %.1f}\n",
+         bytes, rd_grid, rd_nt ? "true" : "false", rd_blocked ? "true" : "false", rd, bytes / (rd * 1e-3) / 1e9);
   printf("{\"measure\": \"hbm_copy\", \"bytes_read_plus_written\": %ld, \"grid\": %d, \"nontemporal\": %s, "
          "\"loads_in_flight\": %d, \"contiguous_per_workgroup\": %s, \"ms\": %.4f, \"GB/s\": %.1f}\n",
          2 * bytes, cp_grid, cp_nt ? "true" : "false", cp_depth, cp_blocked ? "true" : "false", cp,
          2.0 * bytes / (cp * 1e-3) / 1e9);
+  {
+    // rows of 2 KiB (eight heads x 256 bytes); grids that divide them evenly
+    const long rows = bytes / 2048;
+    float hr = 1e30f;
+    int hr_grid = 0;
+    for (int mult : {8, 16, 32, 64}) {
+      const int grid = mult * cus;
+      const long rows_per = rows / (grid / 8);
+      if (rows_per % 64 != 0 || rows_per * (grid / 8) != rows) continue;
+      const float r = time_ms(
+          [&] { hipLaunchKernelGGL(read_head_rows_kernel, dim3(grid), dim3(256), 0, 0, a, rows_per, flag); }, 0.0f,
+          10);
+      if (r < hr) { hr = r; hr_grid = grid; }
+    }
+    printf("{\"measure\": \"hbm_read_head_rows\", \"bytes\": %ld, \"grid\": %d, \"ms\": %.4f, \"GB/s\": %.1f}\n",
+           bytes, hr_grid, hr, bytes / (hr * 1e-3) / 1e9);
+  }
+  {
+    const long toks = bytes / 16384;
+    float hc = 1e30f;
+    int hc_grid = 0;
+    for (int mult : {1, 2, 4, 8}) {
+      const int grid = mult * cus;
+      const long tok_per = toks / (grid / 8);
+      if (tok_per % 8 != 0 || tok_per * (grid / 8) != toks) continue;
+      const float r = time_ms(
+          [&] { hipLaunchKernelGGL(copy_head_groups_kernel, dim3(grid), dim3(256), 0, 0, a, b, tok_per); }, 0.0f, 10);
+      if (r < hc) { hc = r; hc_grid = grid; }
+    }
+    printf("{\"measure\": \"hbm_copy_head_groups\", \"bytes_read_plus_written\": %ld, \"grid\": %d, \"ms\": %.4f, "
+           "\"GB/s\": %.1f}\n",
+           2 * bytes, hc_grid, hc, 2.0 * bytes / (hc * 1e-3) / 1e9);
+  }
   const float mm = time_ms([&] { hipLaunchKernelGGL(mfma_kernel, dim3(mfma_blocks), dim3(512), 0, 0, sink, 0.001f); },
                            500.0f, 10);
   const double flop = (double)mfma_blocks * 8 * kMfmaIter * 4 * 32768.0;
@@ -272,7 +369,7 @@ int main() {
     for (int r = 0; r < 21; ++r) {
       (void)hipMemsetAsync(b, r & 0xff, 512L << 20);  // evict: 512 MiB written elsewhere
       (void)hipEventRecord(s0);
-      hipLaunchKernelGGL(read_kernel<true>, dim3(grid), dim3(256), 0, 0, a, c16, flag);
+      hipLaunchKernelGGL((read_kernel<true, false>), dim3(grid), dim3(256), 0, 0, a, c16, flag);
       (void)hipEventRecord(s1);
       (void)hipEventSynchronize(s1);
       (void)hipEventElapsedTime(&t[r], s0, s1);
