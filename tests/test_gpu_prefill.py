@@ -123,6 +123,43 @@ def test_prefill_bf16_large_scores(W, G, with_sink):
     assert np.abs(lse.cpu().numpy() - ref["lse"]).max() <= 2 * 2.0 ** -9
 
 
+# The strip kernel's continuous skewed pipeline (query lengths a multiple of
+# the 32-token block, no rotary mode): strips of several blocks (B * Hkv
+# workgroups share the CUs, so each strip gets n_tb * B * Hkv / CUs blocks),
+# unaligned offsets, D 64, G 4, W = 1 (one tile per block), a prefix.
+SKEW_CASES = [
+    # name, B, S, Hq, Hkv, D, W, Sk, q_offset
+    ("skew_w128_g8", 8, 1024, 64, 8, 128, 128, None, 0),
+    ("skew_w96_g4_unaligned", 4, 512, 32, 8, 128, 96, 682, 170),
+    ("skew_w64_d64_g8", 8, 512, 64, 8, 64, 64, None, 0),
+    ("skew_w1_g8", 8, 512, 64, 8, 128, 1, None, 0),
+    ("skew_w32_d64_g4_offset", 4, 1024, 32, 8, 64, 32, 1088, 64),
+    ("skew_w128_prefix", 2, 640, 64, 8, 128, 128, 1000, 352),
+    ("skew_one_block_strips", 1, 96, 16, 2, 128, 128, None, 0),
+]
+
+
+@pytest.mark.parametrize("case", SKEW_CASES, ids=[c[0] for c in SKEW_CASES])
+def test_prefill_skewed_strips(case):
+    """Every row and head against the oracle; the log-sum-exp variant gives
+    the same output bit for bit and its LSE within the bound of the
+    training-forward tests."""
+    name, B, S, Hq, Hkv, D, W, Sk, off = case
+    dev = device()
+    m = swa()
+    cfg = _cfg(name, B, S, Hq, Hkv, D, W, "bf16", Sk=Sk)
+    q, k, v, sinks = prefill_inputs(cfg)
+    ref = oracle.prefill(q, k, v, sinks, W, off, cfg.scale, want_lse=True)
+    qd, kd, vd, sd = q.to(dev), k.to(dev), v.to(dev), sinks.to(dev)
+    o = m.swa_attn_prefill(qd, kd, vd, sd, W, off, cfg.scale)
+    o2, lse = m.swa_attn_prefill_lse(qd, kd, vd, sd, W, off, cfg.scale)
+    torch.cuda.synchronize()
+    assert_close(o, ref["o"], BF16_TOL, name)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), f"{name}: LSE variant output differs"
+    err = np.abs(lse.cpu().numpy() - ref["lse"]).max()
+    assert err <= 2 * 2.0 ** -9, f"{name}: LSE error {err:.3e}"
+
+
 def test_prefill_chunked_equals_oracle():
     """Chunked prefill (queries [c0, c0 + C) over the full K/V with q_offset = c0)."""
     dev = device()
@@ -189,6 +226,7 @@ POISON_CASES = [
     # name, B, Sq, q_offset, Sk, Hq, Hkv, D, window, dtype
     ("strip_w128", 2, 100, 512, 700, 64, 8, 128, 128, "bf16"),       # keys used 385..611
     ("strip_w96_unaligned", 1, 200, 250, 520, 64, 8, 128, 96, "bf16"),
+    ("skew_strip_w96_unaligned", 1, 192, 250, 520, 64, 8, 128, 96, "bf16"),
     ("strip_w64_g4_d64", 1, 90, 310, 460, 16, 4, 64, 64, "bf16"),
     ("generic_w128_unaligned", 1, 100, 600, 760, 16, 2, 128, 128, "bf16"),
     ("generic_w512", 1, 200, 700, 1000, 8, 1, 128, 512, "bf16"),
