@@ -63,10 +63,11 @@ __device__ __forceinline__ SplitRange split_range(const VerifyArgs& p, int L) {
 // KV head innermost.  Workgroups start in linear-id order, so the short work
 // runs last and the tail stays short.  Every wave derives the order from
 // cache_len (requests b = lane + 64c); returns false when linear id i has no
-// work.  Used for up to kLptMaxB requests.
+// work.  Used for up to kLptMaxB requests.  nh: the KV-head items per
+// (request, split), g the item's index among them.
 constexpr int kLptMaxB = 256;
 
-__device__ bool lpt_item(const VerifyArgs& p, int i, int lane, int& b, int& g, int& s) {
+__device__ bool lpt_item(const VerifyArgs& p, int nh, int i, int lane, int& b, int& g, int& s) {
   constexpr int CH = kLptMaxB / 64;
   int nfull[CH], rem[CH];
 #pragma unroll
@@ -87,11 +88,11 @@ __device__ bool lpt_item(const VerifyArgs& p, int i, int lane, int& b, int& g, i
   for (int c = 0; c < CH; ++c) {
     if (c * 64 >= p.B) break;
     for (int l = 0; l < 64 && c * 64 + l < p.B; ++l) {
-      const int n = __builtin_amdgcn_readlane(nfull[c], l) * p.Hkv;
+      const int n = __builtin_amdgcn_readlane(nfull[c], l) * nh;
       if (i < acc + n) {
         b = c * 64 + l;
-        s = (i - acc) / p.Hkv;
-        g = (i - acc) % p.Hkv;
+        s = (i - acc) / nh;
+        g = (i - acc) % nh;
         return true;
       }
       acc += n;
@@ -99,8 +100,8 @@ __device__ bool lpt_item(const VerifyArgs& p, int i, int lane, int& b, int& g, i
   }
   // partial splits: this lane's requests ranked by (size desc, index asc)
   const int j = i - acc;
-  const int target = j / p.Hkv;
-  g = j % p.Hkv;
+  const int target = j / nh;
+  g = j % nh;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     if (c * 64 >= p.B) break;
@@ -127,8 +128,14 @@ __device__ bool lpt_item(const VerifyArgs& p, int i, int lane, int& b, int& g, i
 
 }  // namespace
 
-template <int D, int NB, int NW, bool DIRECT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1, NB == 1 ? 2 : 1))) void verify_bf16_kernel(VerifyArgs p) {
+// HP KV heads per workgroup (1 or 2), NW waves per head: the waves of the
+// heads of a pair read adjacent 256-byte rows of the same cache positions at
+// the same time, which HBM serves at the contiguous-read rate (measured:
+// 7.04-7.17 TB/s for two heads' waves in one workgroup against 6.67-6.70 for
+// one head per workgroup, on the same 8 GiB).  Each head's waves fold and
+// merge exactly as with one head per workgroup.
+template <int D, int NB, int NW, bool DIRECT, int HP = 1>
+__global__ __launch_bounds__(NW * HP * 64) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1, NB == 1 ? 2 : 1))) void verify_bf16_kernel(VerifyArgs p) {
   constexpr int NC = D / 16;
   constexpr int ND = D / 32;
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
@@ -137,12 +144,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
   constexpr int NQ_W = (NB * ND + NW - 1) / NW;  // output blocks each wave finishes
   static_assert((NW & (NW - 1)) == 0, "the merge tree pairs waves");
 
+  static_assert(HP == 1 || NB == 1, "head pairs with one 32-row block per head");
   struct MergeLds {
-    float acc[NW][ACC_N][64];
+    float acc[NW * HP][ACC_N][64];
   };
   struct TileLds {
-    uint16_t k[NW][KTile<D>::ELEMS];
-    uint16_t v[NW][VTile<D>::ELEMS];
+    uint16_t k[NW * HP][KTile<D>::ELEMS];
+    uint16_t v[NW * HP][VTile<D>::ELEMS];
   };
   // 4 KiB accumulator blocks that fit in a wave's own K and V tiles
   constexpr int KBLK = (int)(sizeof(uint16_t) * KTile<D>::ELEMS / 4096);
@@ -151,22 +159,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
   constexpr size_t LDS_MAIN =
       OWN_MERGE || sizeof(TileLds) > sizeof(MergeLds) ? sizeof(TileLds) : sizeof(MergeLds);
   __shared__ __attribute__((aligned(16))) unsigned char lds_main[LDS_MAIN];
-  __shared__ float lds_m[NW][NB * 32];
-  __shared__ float lds_l[NW][NB * 32];
+  __shared__ float lds_m[NW * HP][NB * 32];
+  __shared__ float lds_l[NW * HP][NB * 32];
 
   // grid (B * Hkv, nsplit): workgroups are dealt to the 8 XCDs round-robin by
   // linear id, so with (request, KV head) as the fastest dimension every XCD
   // gets the same mix of long and short requests (with 8 KV heads, XCD = KV
   // head); splits past a request's length exit at once.
   const int lane = threadIdx.x & 63;
+  const int wv_all = wave_index();
+  const int hs = wv_all / NW;  // this wave's head within the workgroup's pair
+  const int nh = p.Hkv / HP;   // head items per (request, split)
   int g, b, s;
   if (DIRECT || p.B > kLptMaxB) {
-    g = blockIdx.x % p.Hkv;
-    b = blockIdx.x / p.Hkv;
+    g = blockIdx.x % nh;
+    b = blockIdx.x / nh;
     s = blockIdx.y;
-  } else if (!lpt_item(p, blockIdx.x + blockIdx.y * gridDim.x, lane, b, g, s)) {
+  } else if (!lpt_item(p, nh, blockIdx.x + blockIdx.y * gridDim.x, lane, b, g, s)) {
     return;
   }
+  g = g * HP + hs;
   const int L = p.cache_len[b];
   const SplitRange sr = split_range(p, L);
   if (s >= sr.ns) return;
@@ -177,7 +189,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
 
   const int G = p.Hq / p.Hkv;
   const int R = G * p.T;
-  const int wv = wave_index();
+  const int wv = wv_all - hs * NW;  // wave index among this head's NW
   const int half = lane >> 5, col = lane & 31;
   const long kv_tok = (long)p.Hkv * D;
   // ring: slot of the oldest committed position held, to map slot -> position
@@ -208,8 +220,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
     for (int db = 0; db < ND; ++db) acc[nb][db] = f32x16{};
   }
 
-  uint16_t* k_t = ((TileLds*)lds_main)->k[wv];
-  uint16_t* v_t = ((TileLds*)lds_main)->v[wv];
+  uint16_t* k_t = ((TileLds*)lds_main)->k[wv_all];
+  uint16_t* v_t = ((TileLds*)lds_main)->v[wv_all];
   const long bg_off = ((long)b * p.slots * p.Hkv + g) * D;
   const long bg_new = ((long)b * p.T * p.Hkv + g) * D;
 
@@ -420,17 +432,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
   for (int nb = 0; nb < NB; ++nb) {
     const float lt = halves_sum(l_run[nb]);
     if (half == 0) {
-      lds_m[wv][nb * 32 + col] = m_run[nb];
-      lds_l[wv][nb * 32 + col] = lt;
+      lds_m[wv_all][nb * 32 + col] = m_run[nb];
+      lds_l[wv_all][nb * 32 + col] = lt;
     }
   }
   TileLds* tl = (TileLds*)lds_main;
   MergeLds* ml = (MergeLds*)lds_main;
+  // (w: a wave of this head)
   auto blk_ptr = [&](int w, int q) -> f32x4* {
+    const int wa = hs * NW + w;
     if constexpr (OWN_MERGE) {
-      return q < KBLK ? (f32x4*)tl->k[w] + q * 256 : (f32x4*)tl->v[w] + (q - KBLK) * 256;
+      return q < KBLK ? (f32x4*)tl->k[wa] + q * 256 : (f32x4*)tl->v[wa] + (q - KBLK) * 256;
     } else {
-      return (f32x4*)&ml->acc[w][q * 16][0];
+      return (f32x4*)&ml->acc[wa][q * 16][0];
     }
   };
   if constexpr (!OWN_MERGE) __syncthreads();  // every wave is done with its tiles
@@ -454,14 +468,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NB == 1
     float mA = kNegInf;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      mw[w] = lds_m[w][nb * 32 + col];
+      mw[w] = lds_m[hs * NW + w][nb * 32 + col];
       mA = fmaxf(mA, mw[w]);
     }
     float lA = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       fw[w] = mw[w] == kNegInf ? 0.0f : exp2_fast(mw[w] - mA);
-      lA += mw[w] == kNegInf ? 0.0f : lds_l[w][nb * 32 + col] * fw[w];
+      lA += mw[w] == kNegInf ? 0.0f : lds_l[hs * NW + w][nb * 32 + col] * fw[w];
     }
     f32x16 y;
 #pragma unroll
@@ -600,14 +614,14 @@ VerifyPlan plan_verify_bf16(int B, int T, int Hq, int Hkv, int D, int slots, int
   return pl;
 }
 
-template <int D, int NB, int NW>
+template <int D, int NB, int NW, int HP>
 static hipError_t launch_verify_t(VerifyArgs a, const VerifyPlan& pl, hipStream_t s) {
-  dim3 grid(a.B * a.Hkv, pl.nsplit), block(NW * 64);
+  dim3 grid(a.B * a.Hkv / HP, pl.nsplit), block(NW * HP * 64);
   if (pl.nsplit == 1) {
-    hipLaunchKernelGGL((verify_bf16_kernel<D, NB, NW, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((verify_bf16_kernel<D, NB, NW, true, HP>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((verify_bf16_kernel<D, NB, NW, false>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((verify_bf16_kernel<D, NB, NW, false, HP>), grid, block, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPP = 256 / (D / 4);
@@ -621,10 +635,14 @@ hipError_t launch_verify_bf16(const VerifyArgs& a0, const VerifyPlan& pl, hipStr
   a.split_len = pl.split_len;
   a.nsplit = pl.nsplit;
   a.r_pad = 32 * pl.nb;
+  // head pairs whenever one 32-row block serves a head and the heads pair up
+  const bool pairs = pl.nb == 1 && a.Hkv % 2 == 0;
   if (a.D == 128) {
-    return pl.nb == 1 ? launch_verify_t<128, 1, 4>(a, pl, s) : launch_verify_t<128, 2, 2>(a, pl, s);
+    if (pl.nb == 1) return pairs ? launch_verify_t<128, 1, 4, 2>(a, pl, s) : launch_verify_t<128, 1, 4, 1>(a, pl, s);
+    return launch_verify_t<128, 2, 2, 1>(a, pl, s);
   }
-  return pl.nb == 1 ? launch_verify_t<64, 1, 4>(a, pl, s) : launch_verify_t<64, 2, 2>(a, pl, s);
+  if (pl.nb == 1) return pairs ? launch_verify_t<64, 1, 4, 2>(a, pl, s) : launch_verify_t<64, 1, 4, 1>(a, pl, s);
+  return launch_verify_t<64, 2, 2, 1>(a, pl, s);
 }
 
 }  // namespace swa
