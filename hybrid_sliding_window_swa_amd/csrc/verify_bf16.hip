@@ -589,6 +589,8 @@ VerifyPlan plan_verify_bf16(int B, int T, int Hq, int Hkv, int D, int slots, int
   const int R = G * T;
   pl.nb = R <= 32 ? 1 : 2;
   pl.waves = pl.nb == 1 ? 4 : 2;
+  // split launches pair the KV heads (two per workgroup) when they can
+  const int head_items = pl.nb == 1 && Hkv % 2 == 0 ? Hkv / 2 : Hkv;
   const int unit = 32 * pl.waves;
   // most cache rows one request can need
   long max_rows = slots;
@@ -600,7 +602,7 @@ VerifyPlan plan_verify_bf16(int B, int T, int Hq, int Hkv, int D, int slots, int
   // partials, the short partial splits close the tail); one request at
   // 262144 rows takes 0.18 ms with 8192-row splits (264 workgroups) against
   // 0.21 ms with 2048 (1032) and 0.24 ms with 1024.
-  long want = max_rows * (long)B * Hkv / 256;
+  long want = max_rows * (long)B * head_items / 256;
   long sl = unit;
   while (sl < want && sl < 16384) sl *= 2;
   if (sl < unit) sl = unit;
@@ -635,8 +637,12 @@ hipError_t launch_verify_bf16(const VerifyArgs& a0, const VerifyPlan& pl, hipStr
   a.split_len = pl.split_len;
   a.nsplit = pl.nsplit;
   a.r_pad = 32 * pl.nb;
-  // head pairs whenever one 32-row block serves a head and the heads pair up
-  const bool pairs = pl.nb == 1 && a.Hkv % 2 == 0;
+  // head pairs for the split (long-cache) launches, which stream from HBM,
+  // when one 32-row block serves a head and the heads pair up; a one-split
+  // launch (the SWA ring, short contexts) is bound by its latency, and after
+  // an Infinity-Cache flush the 64-request ring verify measured 16.5 us with
+  // one head per workgroup against 19.7 us with pairs
+  const bool pairs = pl.nb == 1 && a.Hkv % 2 == 0 && pl.nsplit > 1;
   if (a.D == 128) {
     if (pl.nb == 1) return pairs ? launch_verify_t<128, 1, 4, 2>(a, pl, s) : launch_verify_t<128, 1, 4, 1>(a, pl, s);
     return launch_verify_t<128, 2, 2, 1>(a, pl, s);

@@ -139,8 +139,11 @@ def test_workspace_sizes(lib):
     # global cache of 65536 rows: splits of <= 16384 rows, (D + 2) floats per row and split
     b = ws(64, 4, 64, 8, 128, 65536, 0, 0, BF16)
     assert b == 64 * 8 * 4 * 32 * 130 * 4
-    # one request of 262148 rows: splits of 8192 rows
-    assert ws(1, 4, 64, 8, 128, 262148, 0, 0, BF16) == 1 * 8 * 33 * 32 * 130 * 4
+    # one request of 262148 rows: the 8 KV heads paired (4 items per split), so
+    # splits of 4096 rows for about 256 workgroups: 65 splits
+    assert ws(1, 4, 64, 8, 128, 262148, 0, 0, BF16) == 1 * 8 * 65 * 32 * 130 * 4
+    # with an odd number of KV heads there are no pairs: 7 items, splits of 8192 rows
+    assert ws(1, 4, 56, 7, 128, 262148, 0, 0, BF16) == 1 * 7 * 33 * 32 * 130 * 4
 
 
 def _append(lib, ptr=1, B=2, T=4, Hkv=8, D=128, slots=128, ring=1, dt=BF16):
