@@ -241,7 +241,7 @@ SWA_API swa_status_t swa_attn_verify(const void *q, const void *k_new, const voi
  *   Maximum: swa_attn_verify_workspace_bytes(...) of the same arguments must
  *   not exceed SWA_VERIFY_NOALLOC_SCRATCH_BYTES (64 MiB, e.g. 64 requests x 8
  *   KV heads over 65536-slot global caches need 34 MB, one request over
- *   262144 slots 4.3 MB); larger sizes return SWA_ERR_WORKSPACE with nothing
+ *   262144 slots 8.5 MB); larger sizes return SWA_ERR_WORKSPACE with nothing
  *   enqueued.
  *   All calls on one GPU share that GPU's array, so calls that overlap on
  *   one GPU (other streams, other host threads) race and must be ordered by
