@@ -10,11 +10,14 @@
 // one 32-column MFMA block), so the cache is streamed exactly once.
 //
 // Work decomposition
-//   * Workgroup = (split of the cache rows, KV head g, request b).  Split 0
-//     also takes the tile of q_len new rows.  Within a workgroup, wave w takes
-//     tiles w, w + NW, ... (32 rows each) and keeps its own online-softmax
-//     state for the 32*NB query rows; the waves are merged through LDS at
-//     the end, in a fixed order (bitwise deterministic).
+//   * Workgroup = (split of the cache rows, KV head g, request b), or, for
+//     the split launches of long caches, (split, pair of KV heads, request):
+//     NW waves per head, the two heads' waves reading the two heads' rows
+//     of each cache position side by side.  Split 0 also takes the tile of
+//     q_len new rows.  Within a head, wave w takes tiles w, w + NW, ... (32
+//     rows each) and keeps its own online-softmax state for the 32*NB query
+//     rows; a head's waves are merged through LDS at the end, in a fixed
+//     order (bitwise deterministic).
 //   * Split workgroups run longest first: all full splits, then each
 //     request's partial split by decreasing length, so the tail is short.
 //   * K and V tiles are staged row-major in a per-wave LDS tile (coalesced
@@ -162,10 +165,10 @@ __global__ __launch_bounds__(NW * HP * 64) __attribute__((amdgpu_waves_per_eu(NB
   __shared__ float lds_m[NW * HP][NB * 32];
   __shared__ float lds_l[NW * HP][NB * 32];
 
-  // grid (B * Hkv, nsplit): workgroups are dealt to the 8 XCDs round-robin by
-  // linear id, so with (request, KV head) as the fastest dimension every XCD
-  // gets the same mix of long and short requests (with 8 KV heads, XCD = KV
-  // head); splits past a request's length exit at once.
+  // grid (B * Hkv / HP, nsplit): workgroups are dealt to the 8 XCDs
+  // round-robin by linear id, so with (request, KV head or head pair) as the
+  // fastest dimension every XCD gets the same mix of long and short
+  // requests; splits past a request's length exit at once.
   const int lane = threadIdx.x & 63;
   const int wv_all = wave_index();
   const int hs = wv_all / NW;  // this wave's head within the workgroup's pair
